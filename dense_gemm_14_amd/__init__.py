@@ -1,0 +1,160 @@
+"""Python binding of libgemm355 (gfx950 HIP kernels behind a C ABI).
+
+Argument marshalling only: every step of the product runs in the HIP kernels
+of ``libgemm355.so``. There is no CPU path and no fallback -- if the library
+cannot be loaded, every call raises.
+
+The functions mirror the C entry points declared in ``include/gemm355.h``:
+
+    gemm_bf16_nt(M, N, K, A, B, C, stream=None)
+    gemm_nvfp4_nt(M, N, K, Aq, SFA, Bq, SFB, C, stream=None)
+
+Operands may be torch tensors on a ROCm device (their storage is checked
+against the sizes before the call, since the C side cannot see it) or raw
+device addresses as ints (unchecked). ``stream`` is a ``torch.cuda.Stream``,
+a raw hipStream_t as int, or None for torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "libgemm355.so")
+HEADER = os.path.join(ROOT, "include", "gemm355.h")
+
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_UNSUPPORTED = 2
+ERR_NO_DEVICE = 3
+ERR_LAUNCH = 4
+
+_lib = None
+
+
+class Gemm355Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what, status_string(status), status))
+
+
+def load() -> ctypes.CDLL:
+    """Load libgemm355.so, building it first if (and only if) none is built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    try:
+        lib = ctypes.CDLL(LIB_PATH)
+    except OSError as e:  # no silent fallback: the HIP library is the product
+        raise RuntimeError("libgemm355.so could not be loaded from %s: %s" % (LIB_PATH, e)) from e
+    p, i = ctypes.c_void_p, ctypes.c_int
+    lib.gemm_bf16_nt.argtypes = [i, i, i, p, p, p, p]
+    lib.gemm_bf16_nt.restype = i
+    lib.gemm_nvfp4_nt.argtypes = [i, i, i, p, p, p, p, p, p]
+    lib.gemm_nvfp4_nt.restype = i
+    lib.gemm355_status_string.argtypes = [i]
+    lib.gemm355_status_string.restype = ctypes.c_char_p
+    lib.gemm355_tile_order.argtypes = [i, i, i, p, p]
+    lib.gemm355_tile_order.restype = i
+    lib.gemm355_schedule.argtypes = [i, i, p, i]
+    lib.gemm355_schedule.restype = i
+    _lib = lib
+    return lib
+
+
+def declared_functions() -> list:
+    """Names of the functions declared in include/gemm355.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    return load().gemm355_status_string(int(status)).decode()
+
+
+# ---- marshalling -----------------------------------------------------------
+
+def _addr(x, need_bytes: int, what: str):
+    """Device address of a tensor (checked) or a raw int address (unchecked)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s: expected a torch tensor or an int address, got %r" % (what, type(x)))
+    if x.device.type != "cuda":
+        raise ValueError("%s must be on the GPU, got device %s" % (what, x.device))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    have = x.numel() * x.element_size()
+    if have < need_bytes:
+        raise ValueError("%s holds %d bytes, the sizes need %d" % (what, have, need_bytes))
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise Gemm355Error(status, what)
+
+
+# ---- entry points ------------------------------------------------------------
+
+def gemm_bf16_nt(M: int, N: int, K: int, A, B, C, stream=None) -> None:
+    """C (M x N, BF16) = A (M x K, BF16) @ B (N x K, BF16)^T, FP32 sums."""
+    lib = load()
+    M, N, K = int(M), int(N), int(K)
+    nz = M > 0 and N > 0
+    a = _addr(A, M * K * 2 if nz else 0, "A")
+    b = _addr(B, N * K * 2 if nz else 0, "B")
+    c = _addr(C, M * N * 2 if nz else 0, "C")
+    _check(lib.gemm_bf16_nt(M, N, K, a, b, c, _stream(stream)), "gemm_bf16_nt")
+
+
+def gemm_nvfp4_nt(M: int, N: int, K: int, Aq, SFA, Bq, SFB, C, stream=None) -> None:
+    """C (M x N, BF16) = dec(Aq, SFA) @ dec(Bq, SFB)^T for E2M1 codes + E4M3 scales."""
+    lib = load()
+    M, N, K = int(M), int(N), int(K)
+    nz = M > 0 and N > 0
+    aq = _addr(Aq, M * K // 2 if nz else 0, "Aq")
+    sfa = _addr(SFA, M * K // 16 if nz else 0, "SFA")
+    bq = _addr(Bq, N * K // 2 if nz else 0, "Bq")
+    sfb = _addr(SFB, N * K // 16 if nz else 0, "SFB")
+    c = _addr(C, M * N * 2 if nz else 0, "C")
+    _check(lib.gemm_nvfp4_nt(M, N, K, aq, sfa, bq, sfb, c, _stream(stream)), "gemm_nvfp4_nt")
+
+
+def tile_order(tiles_m: int, tiles_n: int, supergroup: int):
+    """Visiting order of output tiles as two lists (tm, tn); host only."""
+    lib = load()
+    n = tiles_m * tiles_n
+    tm = (ctypes.c_int * max(n, 1))()
+    tn = (ctypes.c_int * max(n, 1))()
+    _check(lib.gemm355_tile_order(tiles_m, tiles_n, supergroup, tm, tn), "gemm355_tile_order")
+    return list(tm[:n]), list(tn[:n])
+
+
+def schedule(tiles: int, grid: int):
+    """slot[w][r] = visiting-order position of workgroup w in round r (-1: none)."""
+    lib = load()
+    rounds = -(-tiles // grid) if tiles > 0 and grid > 0 else 1
+    buf = (ctypes.c_int * max(rounds * max(grid, 1), 1))()
+    r = lib.gemm355_schedule(tiles, grid, buf, len(buf))
+    if r < 0:
+        raise Gemm355Error(-r, "gemm355_schedule")
+    return [list(buf[w * r:(w + 1) * r]) for w in range(grid)]

@@ -1,0 +1,121 @@
+/*
+ * gemm355.h -- C ABI of libgemm355: dense NT matrix products on AMD Instinct
+ * MI355X (gfx950).
+ *
+ *   C = A * B^T    A is M x K, B is N x K, both row-major; C is M x N row-major.
+ *
+ * The operation is the one defined in "Achieve cuBLAS Performance on NVIDIA
+ * GB300 for HGEMM" (opening paragraph): BF16 inputs and output, FP32
+ * accumulation. The block-scaled variant takes its operand format from
+ * "NVFP4 GEMM on Blackwell", section "NVFP4 Datatype": E2M1 codes with one FP8
+ * scale per 16 consecutive elements.
+ *
+ * Conventions shared by every entry point
+ *  - All array pointers are DEVICE pointers owned by the caller. The library
+ *    allocates nothing, keeps no per-call state and never synchronises: it
+ *    enqueues the work on `stream` and returns. `stream` is a hipStream_t
+ *    passed as void*; NULL means the default (null) stream.
+ *  - Arrays are dense, row-major, with no padding between rows (the leading
+ *    dimension of A and B is K, that of C is N). C must not overlap any input.
+ *  - Only the M x N elements of C are written.
+ *  - Results for inputs holding NaN or infinity are unspecified.
+ *  - Every argument check happens before the first HIP runtime call, so a
+ *    rejected call touches neither the device nor the stream. Faults that
+ *    happen during the asynchronous execution surface at the caller's next
+ *    synchronisation, as usual for HIP.
+ *  - Calls are thread-safe: the library holds no mutable state apart from a
+ *    per-device cache of the compute-unit count, filled once under a lock.
+ */
+#ifndef GEMM355_H
+#define GEMM355_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum gemm355_status {
+    GEMM355_OK = 0,               /* work enqueued (or nothing to do)              */
+    GEMM355_ERR_INVALID_ARG = 1,  /* negative size, NULL pointer, overlapping C    */
+    GEMM355_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels handle:   */
+                                  /* alignment, K or N granularity, extents       */
+    GEMM355_ERR_NO_DEVICE = 3,    /* no usable HIP device / attribute query failed */
+    GEMM355_ERR_LAUNCH = 4        /* the kernel launch itself reported an error    */
+} gemm355_status;
+
+/*
+ * gemm_bf16_nt -- C[m][n] = bf16( sum_k A[m][k] * B[n][k] )
+ *
+ * ("Achieve cuBLAS Performance on NVIDIA GB300 for HGEMM", opening paragraph.)
+ *   M, N, K  sizes, >= 0.
+ *   A        M x K BF16 values (2 bytes each), row-major.
+ *   B        N x K BF16 values, row-major.
+ *   C        M x N BF16 output, row-major.
+ * Products are exact, sums are FP32 (order unspecified), and the FP32 result
+ * is rounded to BF16 to nearest, ties to even ("Optimized B200 Matrix
+ * Multiplication", section 5 "The Epilogue").
+ * Edge cases: M == 0 or N == 0 does nothing and returns GEMM355_OK (A, B and C
+ * may then be NULL); K == 0 writes +0 to all of C (A and B may be NULL).
+ * Requirements, else GEMM355_ERR_UNSUPPORTED: A, B, C 16-byte aligned;
+ * K % 8 == 0 and N % 8 == 0 (whole 16-byte row segments); every operand,
+ * padded up to a multiple of 256 rows, spans less than 2^31 bytes.
+ */
+int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, void *stream);
+
+/*
+ * gemm_nvfp4_nt -- block-scaled FP4 operands, BF16 output.
+ *
+ * ("NVFP4 GEMM on Blackwell", section "NVFP4 Datatype".)
+ *   Aq   M x K/2 bytes: E2M1 codes, two per byte, element k = 2j in the low
+ *        nibble of byte j and k = 2j+1 in the high nibble. An E2M1 code is
+ *        sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; its 16
+ *        values are +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *   SFA  M x K/16 bytes: one E4M3 ("FN": bias 7, no infinities) scale per 16
+ *        consecutive elements of a row, row-major.
+ *   Bq, SFB  the same for the N x K operand B.
+ *   C    M x N BF16 output, row-major.
+ * a(m,k) = e2m1(Aq code) * e4m3(SFA[m][k/16]), likewise b(n,k), and
+ * C[m][n] = bf16( sum_k a(m,k) * b(n,k) ) with FP32 sums. There is no
+ * per-tensor global scale. Every decoded element is exact in BF16 and in FP16
+ * (at most 6 significant bits, magnitude within [2^-10, 2688]).
+ * Edge cases as for gemm_bf16_nt.
+ * Requirements, else GEMM355_ERR_UNSUPPORTED: Aq, Bq, C 16-byte aligned; SFA,
+ * SFB 4-byte aligned; K % 64 == 0; N % 8 == 0; extents as for gemm_bf16_nt.
+ */
+int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
+                  const void *SFB, void *C, void *stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char *gemm355_status_string(int status);
+
+/*
+ * gemm355_tile_order -- host-only view of the output-tile visiting order.
+ *
+ * Writes, for positions p = 0 .. tiles_m*tiles_n - 1 of the visiting order,
+ * the tile coordinates tm[p], tn[p]. The order is the "supergroup" order of
+ * "NVFP4 GEMM on Blackwell", section "Kernel 5", "Redesign": bands of
+ * `supergroup` adjacent N tiles; inside a band every M tile in turn, and for
+ * each M tile the band's N tiles in turn; the last band may be narrower.
+ * Returns GEMM355_ERR_INVALID_ARG for non-positive sizes or NULL outputs.
+ * No HIP call is made.
+ */
+int gemm355_tile_order(int tiles_m, int tiles_n, int supergroup, int *tm, int *tn);
+
+/*
+ * gemm355_schedule -- host-only view of which workgroup computes which tile.
+ *
+ * For a persistent grid of `grid` workgroups, writes slot[w * rounds + r] =
+ * the visiting-order position that workgroup w computes in its round r, or
+ * -1 when it has none, for r < rounds = ceil(tiles / grid). Workgroups are
+ * dispatched to the 8 XCDs round-robin (w % 8); positions are dealt out so
+ * that the grid/8 workgroups of one XCD take consecutive positions in each
+ * round. `slot` must hold grid * rounds ints. Returns the number of rounds,
+ * or a negative status on bad arguments. No HIP call is made.
+ */
+int gemm355_schedule(int tiles, int grid, int *slot, int slot_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM355_H */

@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: the library loads, exports what its header
+declares, rejects bad arguments before any HIP call, and its host-side tile
+schedule is a bijection with the documented order. No compute is launched.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import dense_gemm_14_amd as g
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced
+
+
+def test_library_exports_every_declared_function():
+    lib = g.load()
+    names = g.declared_functions()
+    assert set(names) >= {"gemm_bf16_nt", "gemm_nvfp4_nt", "gemm355_status_string",
+                          "gemm355_tile_order", "gemm355_schedule"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(5):
+        assert g.status_string(s)
+    assert g.status_string(99) == "unknown status"
+
+
+def _bf16(M, N, K, a=FAKE, b=FAKE + 0x100000, c=FAKE + 0x200000):
+    return g.load().gemm_bf16_nt(M, N, K, a, b, c, None)
+
+
+def _fp4(M, N, K, aq=FAKE, sfa=FAKE + 0x100000, bq=FAKE + 0x200000, sfb=FAKE + 0x300000, c=FAKE + 0x400000):
+    return g.load().gemm_nvfp4_nt(M, N, K, aq, sfa, bq, sfb, c, None)
+
+
+@pytest.mark.parametrize("fn", [_bf16, _fp4])
+def test_rejections_happen_before_any_device_call(fn):
+    assert fn(-1, 8, 64) == g.ERR_INVALID_ARG
+    assert fn(8, -8, 64) == g.ERR_INVALID_ARG
+    assert fn(8, 8, -64) == g.ERR_INVALID_ARG
+    # empty output: nothing to do, even with NULL pointers
+    assert fn(0, 8, 64, None, None, None) == g.OK if fn is _bf16 else fn(0, 8, 64, None, None, None, None, None) == g.OK
+    assert fn(8, 8, 64, c=None) == g.ERR_INVALID_ARG
+    assert fn(8, 12, 64) == g.ERR_UNSUPPORTED          # N % 8
+    assert fn(8, 8, 64, c=FAKE + 0x900008) == g.ERR_UNSUPPORTED  # C not 16-byte aligned
+
+
+def test_bf16_specific_rejections():
+    assert _bf16(8, 8, 64, a=None) == g.ERR_INVALID_ARG
+    assert _bf16(8, 8, 12) == g.ERR_UNSUPPORTED                   # K % 8
+    assert _bf16(8, 8, 64, a=FAKE + 2) == g.ERR_UNSUPPORTED
+    assert _bf16(1 << 16, 8, 1 << 15, b=1 << 40, c=1 << 41) == g.ERR_UNSUPPORTED  # A spans 4 GiB
+    # C overlapping A
+    assert _bf16(8, 8, 64, a=FAKE, c=FAKE + 64) == g.ERR_INVALID_ARG
+
+
+def test_fp4_specific_rejections():
+    assert _fp4(8, 8, 64, sfa=None) == g.ERR_INVALID_ARG
+    assert _fp4(8, 8, 32) == g.ERR_UNSUPPORTED                    # K % 64
+    assert _fp4(8, 8, 64, sfb=FAKE + 0x300002) == g.ERR_UNSUPPORTED  # scales need 4-byte alignment
+    assert _fp4(8, 8, 64, aq=FAKE + 8) == g.ERR_UNSUPPORTED
+
+
+def test_binding_checks_tensor_sizes_before_calling():
+    import torch
+    with pytest.raises(ValueError):
+        g.gemm_bf16_nt(4, 8, 8, torch.zeros(4, 8, dtype=torch.bfloat16), FAKE, FAKE)  # CPU tensor
+
+
+def _golden_order():
+    pairs = []
+    for line in open(os.path.join(GOLDEN, "supergroup4_order.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            m, n = line.split()
+            pairs.append((int(m), int(n)))
+    return pairs
+
+
+def test_tile_order_matches_the_pages_supergroup_example():
+    tm, tn = g.tile_order(2, 8, 4)
+    assert list(zip(tm, tn)) == _golden_order()
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n,sg", [(32, 32, 8), (32, 32, 4), (1, 32, 8), (5, 7, 3),
+                                                 (32, 32, 1), (3, 2, 8), (31, 33, 8)])
+def test_tile_order_is_a_bijection(tiles_m, tiles_n, sg):
+    tm, tn = g.tile_order(tiles_m, tiles_n, sg)
+    assert sorted(zip(tm, tn)) == [(m, n) for m in range(tiles_m) for n in range(tiles_n)]
+
+
+@pytest.mark.parametrize("tiles,grid", [(1024, 256), (256, 256), (32, 32), (1, 1), (7, 7), (1000, 248), (12, 8)])
+def test_schedule_covers_every_tile_once(tiles, grid):
+    slots = g.schedule(tiles, grid)
+    got = sorted(p for w in slots for p in w if p >= 0)
+    assert got == list(range(tiles))
+
+
+def test_schedule_keeps_an_xcds_tiles_compact():
+    # 8192^3 with 256 x 256 tiles: 32 x 32 tiles on 256 workgroups. In each
+    # round the 32 workgroups of one XCD (w % 8 equal) must cover a 4 x 8
+    # block of tiles: 4 A row strips and 8 B row strips per L2.
+    slots = g.schedule(1024, 256)
+    tm, tn = g.tile_order(32, 32, 8)
+    for r in range(4):
+        for x in range(8):
+            pos = [slots[w][r] for w in range(256) if w % 8 == x]
+            ms = {tm[p] for p in pos}
+            ns = {tn[p] for p in pos}
+            assert len(ms) == 4 and len(ns) == 8, (r, x, ms, ns)

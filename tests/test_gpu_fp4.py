@@ -1,0 +1,103 @@
+"""Parity of the HIP block-scaled FP4 path (gemm_nvfp4_nt through the C ABI)
+with the oracle.
+
+The tolerance's absolute term is scaled by sigma_A * sigma_B (sqrt(3) times
+the rms of each decoded operand), the stated bound for [-1, 1] data
+transferred to the FP4 workload's second moment. Exactly summable scale
+choices have a unique answer and are checked bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_14_amd as g
+import oracle
+import synthetic as syn
+from tests import tolerance
+from tests.gpu_util import GuardedC, need_gpu, sample_positions, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fp4(Aq, SFA, Bq, SFB, M, N, K):
+    C = GuardedC(M, N)
+    g.gemm_nvfp4_nt(M, N, K, to_dev(Aq), to_dev(SFA), to_dev(Bq), to_dev(SFB), C.view)
+    torch.cuda.synchronize()
+    assert C.guards_intact(), "write outside C"
+    return C.bits()
+
+
+def _sigma(Q, SF, K):
+    return tolerance.sigma_of(oracle.decode_nvfp4(Q, SF, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (1, 8, 64), (65, 72, 128), (257, 264, 192),
+                                   (513, 520, 320), (300, 8, 1024), (128, 1024, 512)])
+def test_ragged_shapes_match_oracle(M, N, K):
+    need_gpu()
+    Aq, SFA = syn.fp4_operand(M, K, seed=M + 5 * N + K)
+    Bq, SFB = syn.fp4_operand(N, K, seed=M + 5 * N + K + 1)
+    C = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+    ref = oracle.gemm_nvfp4_nt(Aq, SFA, Bq, SFB, K)
+    res = tolerance.check(C, ref, K, _sigma(Aq, SFA, K) * _sigma(Bq, SFB, K))
+    assert res, res
+
+
+@pytest.mark.parametrize("M,N,K", [(264, 520, 512), (513, 256, 448)])
+def test_exact_unit_exponent_scales_bitwise(M, N, K):
+    # scales 2^0 * (1 + m/8), all 16 codes, K <= 512: sums exact in FP32
+    need_gpu()
+    Aq = syn.fp4_codes(M, K, seed=61)
+    Bq = syn.fp4_codes(N, K, seed=62)
+    SFA = syn.e4m3_scales(M, K, seed=63, u_lo=0, u_hi=0)
+    SFB = syn.e4m3_scales(N, K, seed=64, u_lo=0, u_hi=0)
+    C = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+    assert np.array_equal(C, oracle.gemm_nvfp4_nt(Aq, SFA, Bq, SFB, K))
+
+
+def test_decoded_identity_reproduces_A():
+    # B = I as FP4 (code 2 = 1.0 on the diagonal, unit scales 0x38): C = dec(A).
+    need_gpu()
+    M, K = 300, 512
+    Aq, SFA = syn.fp4_operand(M, K, seed=65)
+    codes = np.zeros((K, K), np.uint8)
+    codes[np.arange(K), np.arange(K)] = 2
+    Bq = syn.pack_nibbles(codes)
+    SFB = np.full((K, K // 16), 0x38, np.uint8)
+    C = run_fp4(Aq, SFA, Bq, SFB, M, K, K)
+    # compared as values: code 8 decodes to -0, and the sign of a zero sum is
+    # not part of the contract
+    want = syn.to_bf16_bits(oracle.decode_nvfp4(Aq, SFA, K))
+    assert np.array_equal(tolerance.bf16_bits_to_f64(C), tolerance.bf16_bits_to_f64(want))
+
+
+def test_fp4_workload_sampled_against_oracle():
+    need_gpu()
+    M = N = K = 8192
+    Aq, SFA = syn.fp4_operand(M, K, seed=syn.seed_for(5, 0))
+    Bq, SFB = syn.fp4_operand(N, K, seed=syn.seed_for(5, 0) + 1)
+    C = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+    ms, ns = sample_positions(M, N, 3000, seed=5)
+    ref = oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns)
+    sig = _sigma(Aq[:512], SFA[:512], K) * _sigma(Bq[:512], SFB[:512], K)
+    res = tolerance.check(C[ms, ns], ref, K, sig)
+    assert res, res
+    assert np.all(np.isfinite(tolerance.bf16_bits_to_f64(C)))
+
+
+def test_fp4_workload_exactly_summable_every_element():
+    # scales in {2^-1, 2^0}, all 16 codes, K = 8192: sums exact in FP32.
+    need_gpu()
+    M = N = K = 8192
+    Aq = syn.fp4_codes(M, K, seed=71)
+    Bq = syn.fp4_codes(N, K, seed=72)
+    SFA = syn.e4m3_scales(M, K, seed=73, u_lo=-1, u_hi=0, m_lo=0, m_hi=0)
+    SFB = syn.e4m3_scales(N, K, seed=74, u_lo=-1, u_hi=0, m_lo=0, m_hi=0)
+    C = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+    Ad = oracle.decode_nvfp4(Aq, SFA, K)
+    Bd = oracle.decode_nvfp4(Bq, SFB, K)
+    want = oracle.bf16_from_double(Ad @ Bd.T)
+    ms, ns = sample_positions(M, N, 300, seed=8)
+    assert np.array_equal(oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns), want[ms, ns])
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
