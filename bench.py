@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Throughput of libgemm355 on one MI355X: TFLOP/s of C = A * B^T.
+
+Default workload: BF16 M = N = K = 8192 (inputs i.i.d. uniform[-1, 1] rounded
+to BF16, FP32 accumulation, BF16 output), rotating between enough input sets
+that the footprint exceeds twice the 256 MiB last-level cache (the
+measurement method of "NVFP4 GEMM on Blackwell", section "Benchmarking":
+separate warm-up and timed iterations, buffer rotation, uniform data).
+
+A step is one call of the library's entry point on one input set that is
+already resident in device memory. W warm-up steps run first, then exactly K
+timed steps bracketed by device synchronisation; HIP events recorded on the
+launch stream time them. One JSON line goes to stdout:
+  value      TFLOP/s over the K timed steps (2 M N K per step);
+  roofline   the kernel's achieved TFLOP/s (algorithmic FLOPs per launch over
+             the mean launch duration) against the dense peak of its operand
+             type, plus HBM traffic per launch from the committed rocprofv3
+             counter summary when it was taken from the current kernel source;
+  cpu_baseline  the plain CPU oracle timed on a bounded sample of the same
+             workload's output elements on this host's cores.
+
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+LLC_BYTES = 256 << 20                  # MI355X Infinity Cache (last-level cache)
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # published dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (kind, M, N, K)
+    "bf16_8192": ("bf16", 8192, 8192, 8192),
+    "bf16_4096": ("bf16", 4096, 4096, 4096),
+    "bf16_8000": ("bf16", 8000, 8000, 8000),
+    "bf16_skinny": ("bf16", 128, 8192, 8192),
+    "bf16_256": ("bf16", 256, 256, 256),
+    "fp4_8192": ("fp4", 8192, 8192, 8192),
+}
+CONFIG_INDEX = {"bf16_256": 0, "bf16_4096": 1, "bf16_8192": 2, "bf16_8000": 3, "bf16_skinny": 3,
+                "fp4_8192": 4}
+KERNEL_NAME = {"bf16": "gemm_nt_kernel<Bf16Staging>", "fp4": "gemm_nt_kernel<Fp4Staging>"}
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """SHA-256 over the HIP sources; counter figures are used only if it matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_14_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def set_bytes(kind, M, N, K):
+    if kind == "bf16":
+        return 2 * (M * K + N * K + M * N)
+    return M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + 2 * M * N
+
+
+def algorithmic_bytes(kind, M, N, K):
+    """Compulsory traffic of one product: read the operands once, write C once."""
+    return set_bytes(kind, M, N, K)
+
+
+def make_sets(kind, M, N, K, n_sets, cfg):
+    import numpy as np
+    import torch
+    import synthetic as syn
+    sets = []
+    for s in range(n_sets):
+        seed = syn.seed_for(cfg, s)
+        if kind == "bf16":
+            A = torch.from_numpy(syn.bf16_uniform(M, K, seed).view(np.int16)).cuda()
+            B = torch.from_numpy(syn.bf16_uniform(N, K, seed + 500).view(np.int16)).cuda()
+            ops = (A, B)
+        else:
+            Aq, SFA = syn.fp4_operand(M, K, seed)
+            Bq, SFB = syn.fp4_operand(N, K, seed + 500)
+            ops = tuple(torch.from_numpy(x).cuda() for x in (Aq, SFA, Bq, SFB))
+        C = torch.empty(M * N, dtype=torch.int16, device="cuda")
+        sets.append((ops, C))
+    return sets
+
+
+def launcher(kind, M, N, K, stream):
+    import dense_gemm_14_amd as g
+    if kind == "bf16":
+        return lambda ops, C: g.gemm_bf16_nt(M, N, K, ops[0], ops[1], C, stream=stream)
+    return lambda ops, C: g.gemm_nvfp4_nt(M, N, K, *ops, C, stream=stream)
+
+
+def read_traffic(workload: str, launches_flops: float):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    path = os.path.join(PROFILE_DIR, "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
+    """The oracle, as it stands, on a bounded sample of output elements."""
+    import numpy as np
+    import oracle
+    import synthetic as syn
+    from tests import tolerance
+    (ops, C) = sets[0]
+    host = [o.cpu().numpy() for o in ops]
+    if kind == "bf16":
+        A, B = (h.view(np.uint16) for h in host)
+        fn = lambda ms, ns: oracle.gemm_bf16_nt_at(A, B, ms, ns)
+    else:
+        Aq, SFA, Bq, SFB = host
+        fn = lambda ms, ns: oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns)
+    g = np.random.Generator(np.random.PCG64(seed))
+    cores = oracle.max_threads()
+    # calibrate on a small batch, then size the timed sample to the target
+    n0 = max(64, cores * 8)
+    t0 = time.perf_counter()
+    fn(g.integers(0, M, n0).astype(np.int32), g.integers(0, N, n0).astype(np.int32))
+    rate = n0 / max(time.perf_counter() - t0, 1e-6)
+    n = int(min(max(rate * seconds_target, n0), M * N))
+    ms = g.integers(0, M, n).astype(np.int32)
+    ns = g.integers(0, N, n).astype(np.int32)
+    t0 = time.perf_counter()
+    ref = fn(ms, ns)
+    dt = time.perf_counter() - t0
+    # the same sample doubles as a spot check of the GPU output of set 0
+    got = C.cpu().numpy().view(np.uint16).reshape(M, N)[ms, ns]
+    sigma = 1.0
+    if kind == "fp4":
+        sub = slice(0, min(M, 256))
+        sigma = (tolerance.sigma_of(oracle.decode_nvfp4(host[0][sub], host[1][sub], K)) *
+                 tolerance.sigma_of(oracle.decode_nvfp4(host[2][sub], host[3][sub], K)))
+    chk = tolerance.check(got, ref, K, sigma)
+    return {
+        "value": 2.0 * n * K / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d random output elements of the %dx%dx%d product (full K each), "
+                  "binary64 sums, %.1f s" % (n, M, N, K, dt),
+        "seconds": dt,
+        "spot_check": {"elements": n, "within_tolerance": bool(chk), "worst_ratio": chk.worst_ratio},
+    }
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.bitwise_not(src, out=dst)  # one elementwise kernel: reads and writes nbytes
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="bf16_8192", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (used for profiler runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return 0
+
+    import dense_gemm_14_amd as g
+    g.load()  # fails loudly if the HIP library is missing
+
+    kind, M, N, K = WORKLOADS[args.workload]
+    per_set = set_bytes(kind, M, N, K)
+    n_sets = 2 * LLC_BYTES // per_set + 1
+    sets = make_sets(kind, M, N, K, n_sets, CONFIG_INDEX[args.workload])
+    stream = torch.cuda.current_stream()
+    run = launcher(kind, M, N, K, stream)
+
+    for i in range(args.warmup):
+        run(*sets[i % n_sets])
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        run(*sets[i % n_sets])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / max(args.steps, 1)
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms_step * 1e-3) / 1e12
+
+    # output of set 0 for the spot check: make sure it was produced last-ish
+    run(*sets[0])
+    torch.cuda.synchronize()
+
+    dtype = "bf16" if kind == "bf16" else "fp16"  # FP4 operands are decoded to FP16 for the MFMA
+    traffic = read_traffic(args.workload, flops)
+    roofline = {
+        "bound": "mfma",
+        "kernel": KERNEL_NAME[kind],
+        "achieved": round(tflops, 2),
+        "peak": PEAK_TFLOPS[dtype],
+        "unit": "TFLOP/s",
+        "frac": round(tflops / PEAK_TFLOPS[dtype], 4),
+        "traffic": traffic,
+        "algorithmic_bytes": algorithmic_bytes(kind, M, N, K),
+        "mean_launch_ms": round(ms_step, 5),
+    }
+    out = {
+        "metric": "TFLOP/s for BF16 C=A·B^T at M=N=K=8192; % of MI355X dense BF16 peak"
+        if args.workload == "bf16_8192" else "TFLOP/s for %s C=A·B^T at %dx%dx%d" % (kind, M, N, K),
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if kind == "bf16" else "fp4(e2m1+e4m3)->fp16",
+        "data": "synthetic",
+        "config": {"workload": "%s_nt_%dx%dx%d" % (kind, M, N, K), "M": M, "N": N, "K": K,
+                   "rotation_sets": n_sets, "footprint_MiB": round(n_sets * per_set / 2 ** 20, 1),
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "percent_of_peak": round(100.0 * tflops / PEAK_TFLOPS[dtype], 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(kind, M, N, K, sets, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -16,8 +16,13 @@
 //     from memory, so each global load has a whole K step to arrive. One
 //     workgroup barrier per K step separates reuse of a stage.
 //   * LDS rows are 128 bytes (64 elements); the 16-byte chunk c of row r is
-//     stored at chunk position c ^ (r & 7), so the 8 rows read together by a
-//     ds_read_b128 quarter-wave hit 8 different 16-byte bank groups.
+//     stored at chunk position c ^ ((r >> 1) & 7). gfx950's LDS serves a
+//     ds_read_b128 16 lanes (256 bytes, 64 banks of 4 bytes) per cycle; the 16
+//     consecutive rows one such group reads at the same logical chunk then
+//     cover all 16 bank groups (row parity picks the 128-byte half of the bank
+//     space, (r >> 1) & 7 the chunk within it). Measured on the device: 4 LDS
+//     cycles per ds_read_b128 and no bank conflicts, against 8 cycles with the
+//     c ^ (r & 7) swizzle that suits a 32-bank LDS.
 //   * The matrix instruction is v_mfma_f32_32x32x16_{bf16,f16}. It is fed
 //     B rows as its first operand and A rows as its second, so the 32 x 32
 //     result block arrives transposed: each lane holds one row m of C and
@@ -76,16 +81,47 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned bytes
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, RSRC_WORD3);
 }
 
+// Physical 16-byte chunk position of logical chunk `chunk` in LDS tile row `row`.
+__device__ inline int swizzle(int row, int chunk)
+{
+    return chunk ^ ((row >> 1) & 7);
+}
+
 // Byte offset of 16-byte chunk `chunk` of LDS tile row `row`.
 __device__ inline int lds_offset(int row, int chunk)
 {
-    return row * ROW_BYTES + ((chunk ^ (row & 7)) << 4);
+    return row * ROW_BYTES + (swizzle(row, chunk) << 4);
 }
 
 __device__ inline unsigned pack_bf16(float lo, float hi)
 {
     f32x2 v = {lo, hi};
     return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2)); // RNE
+}
+
+// ---- instruction interleaving hints ---------------------------------------
+//
+// Each hint asks the scheduler for `n` instructions of one class at this point
+// of the region's order (classes: matrix, LDS read, LDS write, global read,
+// vector ALU). A K step issues 64 matrix instructions of 32 cycles each per
+// wave; everything else is threaded between them so that the matrix pipe never
+// waits for an issue slot.
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200 };
+#define SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+// Nothing is moved across this point by the scheduler.
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// One sub-step: 16 matrix instructions with the 8 fragment reads of the next
+// sub-step threaded in, one read after each of the first 8.
+__device__ inline void schedule_reads_with_mma()
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        SCHED(SG_MFMA, 1);
+        SCHED(SG_DS_READ, 1);
+    }
+    SCHED(SG_MFMA, 8);
 }
 
 // ---- BF16 operands --------------------------------------------------------
@@ -140,6 +176,33 @@ struct Bf16Staging {
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0, s1, acc, 0, 0, 0);
     }
+
+    // Sub-step 1: 16 matrix instructions, 8 fragment reads, the 16 LDS
+    // writes of the next slice.
+    static __device__ void schedule_commit()
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            SCHED(SG_MFMA, 1);
+            SCHED(SG_DS_READ, 1);
+            SCHED(SG_DS_WRITE, 1);
+            SCHED(SG_MFMA, 1);
+            SCHED(SG_DS_WRITE, 1);
+        }
+    }
+
+    // Sub-step 2: 16 matrix instructions, 8 fragment reads, the 16 global
+    // reads of the slice after next.
+    static __device__ void schedule_load()
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            SCHED(SG_MFMA, 1);
+            SCHED(SG_DS_READ, 1);
+            SCHED(SG_VMEM_READ, 2);
+            SCHED(SG_MFMA, 1);
+        }
+    }
 };
 
 // ---- block-scaled FP4 operands ---------------------------------------------
@@ -160,12 +223,14 @@ struct Fp4Staging {
     __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
     int a_code_off, b_code_off, a_sf_off, b_sf_off;
     int lds_off;
+    int K;
     u32x4 a_code[2], b_code[2];
     unsigned a_sf, b_sf;
 
     __device__ void init(const Problem &p, int tm, int tn, int tid)
     {
         const unsigned kc = (unsigned)p.K / 2, ks = (unsigned)p.K / 16;
+        K = p.K;
         ra = make_rsrc(p.a, (unsigned)p.M * kc);
         rb = make_rsrc(p.b, (unsigned)p.N * kc);
         rsa = make_rsrc(p.sfa, (unsigned)p.M * ks);
@@ -179,13 +244,16 @@ struct Fp4Staging {
 
     __device__ void load(int k0)
     {
-        const int oc = k0 / 2, os = k0 / 16;   // K % 64 == 0: every step is whole
-        a_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_code_off + oc, 0, 0));
-        a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_code_off + oc + 16, 0, 0));
-        b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_code_off + oc, 0, 0));
-        b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_code_off + oc + 16, 0, 0));
-        a_sf = __builtin_amdgcn_raw_buffer_load_b32(rsa, a_sf_off + os, 0, 0);
-        b_sf = __builtin_amdgcn_raw_buffer_load_b32(rsb, b_sf_off + os, 0, 0);
+        // K % 64 == 0: every step is whole; a step at or past K reads zeros
+        const bool valid = k0 < K;
+        const int oc = k0 / 2, os = k0 / 16;
+        const int ac = valid ? a_code_off + oc : OOB, bc = valid ? b_code_off + oc : OOB;
+        a_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, ac, 0, 0));
+        a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, ac + 16, 0, 0));
+        b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, bc, 0, 0));
+        b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, bc + 16, 0, 0));
+        a_sf = __builtin_amdgcn_raw_buffer_load_b32(rsa, valid ? a_sf_off + os : OOB, 0, 0);
+        b_sf = __builtin_amdgcn_raw_buffer_load_b32(rsb, valid ? b_sf_off + os : OOB, 0, 0);
     }
 
     // 8 codes (one dword) scaled by `s` -> 8 FP16 values.
@@ -209,7 +277,7 @@ struct Fp4Staging {
         for (int h = 0; h < 2; ++h) {                    // two dwords = 16 elements
             const int d = BLK * 2 + h;                   // 16-byte chunk d of the row
             const unsigned codes = code[d >> 2][d & 3];
-            *reinterpret_cast<f16x8 *>(row_base + ((d ^ (row & 7)) << 4)) = decode8(codes, s2);
+            *reinterpret_cast<f16x8 *>(row_base + (swizzle(row, d) << 4)) = decode8(codes, s2);
         }
     }
 
@@ -232,9 +300,47 @@ struct Fp4Staging {
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(s0, s1, acc, 0, 0, 0);
     }
+
+    // Sub-step 1: 16 matrix instructions, 8 fragment reads, the decode
+    // (vector ALU) and 16 LDS writes of the next slice.
+    static __device__ void schedule_commit()
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            SCHED(SG_MFMA, 1);
+            SCHED(SG_DS_READ, 1);
+            SCHED(SG_VALU, 9);
+            SCHED(SG_DS_WRITE, 1);
+            SCHED(SG_MFMA, 1);
+            SCHED(SG_VALU, 9);
+            SCHED(SG_DS_WRITE, 1);
+        }
+    }
+
+    // Sub-step 2: 16 matrix instructions, 8 fragment reads, the 6 global
+    // reads of the slice after next.
+    static __device__ void schedule_load()
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            SCHED(SG_MFMA, 1);
+            SCHED(SG_DS_READ, 1);
+            SCHED(SG_VMEM_READ, 1);
+            SCHED(SG_MFMA, 1);
+        }
+    }
 };
 
 // ---- the persistent kernel --------------------------------------------------
+
+// Make this wave's LDS writes visible to the workgroup and wait for all waves.
+// Only LDS is fenced: global loads still in flight stay in flight.
+__device__ inline void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <class Staging>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
@@ -252,16 +358,24 @@ void gemm_nt_kernel(Problem p)
     const int half = lane >> 5;
 
     // Per-lane LDS fragment addresses: row (l32 + 32 i) of the wave's block,
-    // chunk (2 kk + half) for K sub-step kk.
+    // logical chunk (2 kk + half) for K sub-step kk of 16 elements.
     const int a_row = (wm * 128 + l32) * ROW_BYTES;
     const int b_row = TILE_BYTES + (wn * 128 + l32) * ROW_BYTES;
     int kofs[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        kofs[kk] = ((2 * kk + half) ^ (l32 & 7)) << 4;
+        kofs[kk] = swizzle(l32, 2 * kk + half) << 4;   // rows differ from l32 by multiples of 32
 
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
     const int nk = (p.K + BK - 1) / BK;
+
+    auto read_frags = [&](const uint8_t *stage, int kk, frag *fa, frag *fb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            fa[i] = *reinterpret_cast<const frag *>(stage + a_row + i * 32 * ROW_BYTES + kofs[kk]);
+            fb[i] = *reinterpret_cast<const frag *>(stage + b_row + i * 32 * ROW_BYTES + kofs[kk]);
+        }
+    };
 
     for (int round = 0;; ++round) {
         const int pos = schedule_position(blockIdx.x, round, p.grid);
@@ -277,39 +391,60 @@ void gemm_nt_kernel(Problem p)
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = f32x16{};
 
+        auto mma_all = [&](const frag *fa, const frag *fb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = Staging::mma(fb[j], fa[i], acc[i][j]);
+        };
+
         Staging st;
         st.init(p, tm, tn, tid);
-        if (nk > 0) {
-            st.load(0);
-            st.commit(lds);
-            if (nk > 1)
-                st.load(BK);
-        }
-        __syncthreads();
+        frag fa0[4], fb0[4], fa1[4], fb1[4];
+        st.load(0);
+        lds_barrier();            // every wave is done with the previous tile's stages
+        st.commit(lds);
+        st.load(BK);
+        lds_barrier();
+        read_frags(lds, 0, fa0, fb0);
 
+        // Software pipeline over K steps. Step kt computes on LDS stage kt & 1
+        // in four sub-steps of 16; each sub-step's fragments were read from LDS
+        // during the previous sub-step's matrix instructions. Along the way the
+        // step writes the registers holding slice kt + 1 into the other stage,
+        // requests slice kt + 2 from memory, and -- after the step's single
+        // barrier -- reads the first fragments of the other stage. The body has
+        // no branches, so the compiler can interleave all of it with the matrix
+        // instructions; slices at or past K load as zeros and are never used.
         for (int kt = 0; kt < nk; ++kt) {
             const uint8_t *cur = lds + (kt & 1) * STAGE_BYTES;
             uint8_t *nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                frag fa[4], fb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    fa[i] = *reinterpret_cast<const frag *>(cur + a_row + i * 32 * ROW_BYTES + kofs[kk]);
-                    fb[i] = *reinterpret_cast<const frag *>(cur + b_row + i * 32 * ROW_BYTES + kofs[kk]);
-                }
-                if (kk == 2 && kt + 1 < nk) {
-                    st.commit(nxt);
-                    if (kt + 2 < nk)
-                        st.load((kt + 2) * BK);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = Staging::mma(fb[j], fa[i], acc[i][j]);
-            }
-            __syncthreads();
+
+            read_frags(cur, 1, fa1, fb1);
+            mma_all(fa0, fb0);
+            schedule_reads_with_mma();
+            SCHED_FENCE();
+
+            read_frags(cur, 2, fa0, fb0);
+            st.commit(nxt);
+            mma_all(fa1, fb1);
+            Staging::schedule_commit();
+            SCHED_FENCE();
+
+            read_frags(cur, 3, fa1, fb1);
+            st.load((kt + 2) * BK);
+            mma_all(fa0, fb0);
+            Staging::schedule_load();
+            SCHED_FENCE();
+
+            // every wave is done reading stage `nxt` (last step) and writing it (this step)
+            lds_barrier();
+            SCHED_FENCE();
+            read_frags(nxt, 0, fa0, fb0);
+            mma_all(fa1, fb1);
+            schedule_reads_with_mma();
+            SCHED_FENCE();
         }
 
         // Epilogue: lane holds C[m][nb + 8 g + 4 half + e] in acc[i][j][4 g + e].
