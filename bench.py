@@ -48,7 +48,7 @@ WORKLOADS = {
 }
 CONFIG_INDEX = {"bf16_256": 0, "bf16_4096": 1, "bf16_8192": 2, "bf16_8000": 3, "bf16_skinny": 3,
                 "fp4_8192": 4}
-KERNEL_NAME = {"bf16": "gemm_nt_kernel<Bf16Staging>", "fp4": "gemm_nt_kernel<Fp4Staging>"}
+KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel"}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libgemm355.so")
 SOURCES = [os.path.join(CSRC, "gemm355.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("gemm_kernels.hpp", "schedule.hpp")] + \
+HEADERS = [os.path.join(CSRC, f) for f in ("common.hpp", "gemm_bf16.hpp", "gemm_fp4.hpp", "schedule.hpp")] + \
     [os.path.join(INCLUDE, "gemm355.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -22,6 +22,8 @@ FLAGS = [
     "-fPIC",
     "-shared",
     "-Wall",
+    # the LDS copies clobber m0 on purpose (the compiler uses m0 nowhere else)
+    "-Wno-inline-asm",
     # packed FP32 instructions stay off: the compiler must not form them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

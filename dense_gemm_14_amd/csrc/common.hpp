@@ -1,0 +1,128 @@
+// common.hpp -- pieces shared by the gfx950 kernels of libgemm355: vector
+// types, the problem descriptor, buffer resources, barriers, scheduling hints
+// and the epilogue that turns the FP32 accumulators of one 256 x 256 tile into
+// BF16 rows of C.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "schedule.hpp"
+
+namespace gemm355 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256;                      // output tile rows (M)
+constexpr int BN = 256;                      // output tile columns (N)
+constexpr int THREADS = 256;                 // 4 waves of 64 lanes, 2 x 2 over the tile
+constexpr int OOB = (int)0x80000000;         // buffer offset beyond every range
+constexpr unsigned RSRC_WORD3 = 0x00020000u; // raw buffer, 32-bit data format
+
+struct Problem {
+    const void *a;    // BF16 A, or E2M1 codes of A
+    const void *b;    // BF16 B, or E2M1 codes of B
+    const void *sfa;  // E4M3 scales of A (FP4 only)
+    const void *sfb;  // E4M3 scales of B (FP4 only)
+    void *c;
+    int M, N, K;
+    int tiles_m, tiles_n, tiles;
+    int supergroup;
+    int grid;
+};
+
+// A buffer resource whose range ends at the operand's last byte: loads past it
+// return 0 and stores past it are dropped, which makes row tails (m >= M,
+// n >= N) free and lets an offset of OOB switch one access off.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, RSRC_WORD3);
+}
+
+__device__ inline unsigned pack_bf16(float lo, float hi)
+{
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2)); // round to nearest even
+}
+
+// Make this wave's LDS writes visible to the workgroup and wait for all waves.
+// Only LDS is fenced: global loads still in flight stay in flight.
+__device__ inline void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3..0 and 15..14, expcnt
+// 6..4, lgkmcnt 11..8). vmcnt_le(n) waits until at most n vector-memory
+// operations of this wave are outstanding and leaves the other counters alone.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(waitcnt_vm(n))
+#define WAIT_ALL() __builtin_amdgcn_s_waitcnt(0)
+
+// ---- instruction interleaving hints ---------------------------------------
+//
+// Each hint asks the scheduler for `n` instructions of one class at this point
+// of the region's order (classes: matrix, LDS read, LDS write, global read,
+// vector ALU); SCHED_FENCE stops the scheduler from moving anything across.
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200 };
+#define SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// One sub-step: 16 matrix instructions with 8 fragment reads threaded in,
+// one read after each of the first 8.
+__device__ inline void schedule_reads_with_mma()
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        SCHED(SG_MFMA, 1);
+        SCHED(SG_DS_READ, 1);
+    }
+    SCHED(SG_MFMA, 8);
+}
+
+// ---- epilogue ------------------------------------------------------------------
+//
+// The matrix instruction is fed B rows as its first operand and A rows as its
+// second, so each 32 x 32 result block arrives transposed: lane (l32, half)
+// of block (i, j) holds C[m][nb + 8 g + 4 half + e] in acc[i][j][4 g + e],
+// m = row of the lane. Pairs of 4-column runs are exchanged between the two
+// half-waves (v_permlane32_swap) so every lane stores one 16-byte row segment;
+// a wave's store instruction covers 32 rows x 32 bytes.
+__device__ inline void store_tile(f32x16 (&acc)[4][4], const __amdgpu_buffer_rsrc_t &rc, int M, int N,
+                                  int m0, int n0, int l32, int half)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + i * 32 + l32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int nb = n0 + j * 32;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int g0 = 2 * q;
+                unsigned x0 = pack_bf16(acc[i][j][4 * g0 + 0], acc[i][j][4 * g0 + 1]);
+                unsigned x1 = pack_bf16(acc[i][j][4 * g0 + 2], acc[i][j][4 * g0 + 3]);
+                unsigned y0 = pack_bf16(acc[i][j][4 * g0 + 4], acc[i][j][4 * g0 + 5]);
+                unsigned y1 = pack_bf16(acc[i][j][4 * g0 + 6], acc[i][j][4 * g0 + 7]);
+                // the lower half-wave keeps group g0 and receives the upper
+                // half's part of it; the upper half-wave ends up with g0 + 1
+                auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+                auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+                const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+                const int n = nb + (g0 + half) * 8;
+                const int off = (m < M && n < N) ? (m * N + n) * 2 : OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(out, rc, off, 0, 0);
+            }
+        }
+    }
+}
+
+} // namespace gemm355

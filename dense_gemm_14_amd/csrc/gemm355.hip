@@ -1,13 +1,14 @@
 // gemm355.hip -- host side of libgemm355: argument checks, grid sizing and
-// launches of the gfx950 kernels in gemm_kernels.hpp. The C ABI is declared
-// in include/gemm355.h.
+// launches of the gfx950 kernels in gemm_bf16.hpp and gemm_fp4.hpp. The C ABI
+// is declared in include/gemm355.h.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
 #include <stdint.h>
 
 #include "gemm355.h"
-#include "gemm_kernels.hpp"
+#include "gemm_bf16.hpp"
+#include "gemm_fp4.hpp"
 #include "schedule.hpp"
 
 namespace {
@@ -59,8 +60,8 @@ bool extent_ok(int64_t rows, int64_t row_bytes)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <class Staging>
-int launch(Problem p, void *stream)
+template <class Kernel>
+int launch(Kernel kernel, Problem p, void *stream)
 {
     int cus = 0;
     const int rc = compute_units(&cus);
@@ -72,8 +73,7 @@ int launch(Problem p, void *stream)
     p.supergroup = kSupergroup;
     p.grid = gemm355::persistent_grid(p.tiles, cus);
     (void)hipGetLastError(); // clear a stale error so the check below is ours
-    hipLaunchKernelGGL(gemm355::gemm_nt_kernel<Staging>, dim3(p.grid), dim3(gemm355::THREADS), 0,
-                       static_cast<hipStream_t>(stream), p);
+    hipLaunchKernelGGL(kernel, dim3(p.grid), dim3(gemm355::THREADS), 0, static_cast<hipStream_t>(stream), p);
     return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 
@@ -104,7 +104,7 @@ extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, v
     p.M = M;
     p.N = N;
     p.K = K;
-    return launch<gemm355::Bf16Staging>(p, stream);
+    return launch(gemm355::bf16::gemm_bf16_nt_kernel, p, stream);
 }
 
 extern "C" int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
@@ -136,7 +136,7 @@ extern "C" int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SF
     p.M = M;
     p.N = N;
     p.K = K;
-    return launch<gemm355::Fp4Staging>(p, stream);
+    return launch(gemm355::fp4::gemm_nvfp4_nt_kernel, p, stream);
 }
 
 extern "C" const char *gemm355_status_string(int status)

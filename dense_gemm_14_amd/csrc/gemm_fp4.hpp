@@ -1,209 +1,45 @@
-// gemm_kernels.hpp -- gfx950 device code of libgemm355.
+// gemm_fp4.hpp -- persistent block-scaled FP4 NT GEMM for gfx950.
 //
-// One persistent kernel template computes C = A * B^T for row-major A (M x K)
-// and B (N x K); two staging policies feed it:
-//   * Bf16Staging: BF16 operands copied global -> registers -> LDS;
-//   * Fp4Staging:  E2M1 codes + E4M3 scales decoded exactly to FP16 while
-//     they are staged, so the same LDS layout and matrix-core loop follow.
+// The operands are E2M1 codes (two per byte, even k in the low nibble) with
+// one E4M3 scale per 16 consecutive K elements of a row ("NVFP4 GEMM on
+// Blackwell", section "NVFP4 Datatype"). They are decoded exactly to FP16
+// while being staged into LDS, so the matrix-core loop is the ordinary FP16
+// one (v_mfma_f32_32x32x16_f16, same rate as BF16).
 //
 // Work decomposition
 //   * Output tile 256 x 256 per workgroup, 4 waves in a 2 x 2 layout, each
 //     wave owning a 128 x 128 block = 4 x 4 MFMA blocks of 32 x 32 whose FP32
 //     accumulators (256 per lane) live in the accumulation registers.
 //   * K advances 64 at a time through a 2-stage LDS ring (2 x 64 KiB): while
-//     the matrix cores work on stage s, the next K slice already sitting in
-//     registers is written into stage s^1 and the slice after it is requested
-//     from memory, so each global load has a whole K step to arrive. One
+//     the matrix cores work on stage s, the next K slice sitting in registers
+//     (codes and scales, 18 registers per lane) is decoded and written into
+//     stage s^1, and the slice after it is requested from memory. One
 //     workgroup barrier per K step separates reuse of a stage.
-//   * LDS rows are 128 bytes (64 elements); the 16-byte chunk c of row r is
+//   * LDS rows are 128 bytes (64 FP16 values); the 16-byte chunk c of row r is
 //     stored at chunk position c ^ ((r >> 1) & 7). gfx950's LDS serves a
 //     ds_read_b128 16 lanes (256 bytes, 64 banks of 4 bytes) per cycle; the 16
 //     consecutive rows one such group reads at the same logical chunk then
 //     cover all 16 bank groups (row parity picks the 128-byte half of the bank
-//     space, (r >> 1) & 7 the chunk within it). Measured on the device: 4 LDS
-//     cycles per ds_read_b128 and no bank conflicts, against 8 cycles with the
-//     c ^ (r & 7) swizzle that suits a 32-bank LDS.
-//   * The matrix instruction is v_mfma_f32_32x32x16_{bf16,f16}. It is fed
-//     B rows as its first operand and A rows as its second, so the 32 x 32
-//     result block arrives transposed: each lane holds one row m of C and
-//     runs of 4 consecutive columns, which the epilogue pairs across the two
-//     half-waves (v_permlane32_swap) into 16-byte row segments.
-//   * Operands are read through buffer resources whose range ends at the
-//     operand's last byte: rows past M or N read as zero, and a K tail or
-//     masked store uses an offset beyond every range (loads return 0, stores
-//     are dropped), so no tile needs a bounds branch.
+//     space, (r >> 1) & 7 the chunk within it), so the reads are conflict-free.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "schedule.hpp"
+#include "common.hpp"
 
 namespace gemm355 {
+namespace fp4 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int BM = 256;                      // output tile rows (M)
-constexpr int BN = 256;                      // output tile columns (N)
 constexpr int BK = 64;                       // K elements per pipeline step
-constexpr int THREADS = 256;                 // 4 waves of 64 lanes
-constexpr int ROW_BYTES = BK * 2;            // one LDS tile row: 64 x 16-bit
+constexpr int ROW_BYTES = BK * 2;            // one LDS tile row: 64 x FP16
 constexpr int TILE_BYTES = BM * ROW_BYTES;   // 32 KiB per operand per stage
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // A tile then B tile
 constexpr int STAGES = 2;
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-constexpr int OOB = (int)0x80000000;         // beyond every buffer range
-constexpr unsigned RSRC_WORD3 = 0x00020000u; // raw buffer, 32-bit data format
-
-static_assert(BM == BN, "the staging maps assume square tiles");
-
-struct Problem {
-    const void *a;    // BF16 A, or E2M1 codes of A
-    const void *b;    // BF16 B, or E2M1 codes of B
-    const void *sfa;  // E4M3 scales of A (FP4 only)
-    const void *sfb;  // E4M3 scales of B (FP4 only)
-    void *c;
-    int M, N, K;
-    int tiles_m, tiles_n, tiles;
-    int supergroup;
-    int grid;
-};
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, RSRC_WORD3);
-}
 
 // Physical 16-byte chunk position of logical chunk `chunk` in LDS tile row `row`.
 __device__ inline int swizzle(int row, int chunk)
 {
     return chunk ^ ((row >> 1) & 7);
 }
-
-// Byte offset of 16-byte chunk `chunk` of LDS tile row `row`.
-__device__ inline int lds_offset(int row, int chunk)
-{
-    return row * ROW_BYTES + (swizzle(row, chunk) << 4);
-}
-
-__device__ inline unsigned pack_bf16(float lo, float hi)
-{
-    f32x2 v = {lo, hi};
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2)); // RNE
-}
-
-// ---- instruction interleaving hints ---------------------------------------
-//
-// Each hint asks the scheduler for `n` instructions of one class at this point
-// of the region's order (classes: matrix, LDS read, LDS write, global read,
-// vector ALU). A K step issues 64 matrix instructions of 32 cycles each per
-// wave; everything else is threaded between them so that the matrix pipe never
-// waits for an issue slot.
-enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200 };
-#define SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-
-// Nothing is moved across this point by the scheduler.
-#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-// One sub-step: 16 matrix instructions with the 8 fragment reads of the next
-// sub-step threaded in, one read after each of the first 8.
-__device__ inline void schedule_reads_with_mma()
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        SCHED(SG_MFMA, 1);
-        SCHED(SG_DS_READ, 1);
-    }
-    SCHED(SG_MFMA, 8);
-}
-
-// ---- BF16 operands --------------------------------------------------------
-//
-// Each thread copies, per operand and K step, 8 chunks of 16 bytes: rows
-// (tid / 8) + 32 i, chunk tid % 8 -- eight consecutive lanes cover one
-// 128-byte row segment, so every load instruction reads whole cache lines.
-struct Bf16Staging {
-    typedef bf16x8 frag;
-    __amdgpu_buffer_rsrc_t ra, rb;
-    int a_row_off, b_row_off; // byte offset of this thread's first row + its chunk
-    int chunk_k;              // K index of this thread's chunk within a step
-    int lds_off;              // LDS byte offset of this thread's first chunk
-    int K;
-    u32x4 a_reg[8], b_reg[8];
-
-    __device__ void init(const Problem &p, int tm, int tn, int tid)
-    {
-        ra = make_rsrc(p.a, (unsigned)p.M * (unsigned)p.K * 2u);
-        rb = make_rsrc(p.b, (unsigned)p.N * (unsigned)p.K * 2u);
-        const int row = tid >> 3, chunk = tid & 7;
-        K = p.K;
-        chunk_k = chunk * 8;
-        a_row_off = ((tm * BM + row) * p.K + chunk_k) * 2;
-        b_row_off = ((tn * BN + row) * p.K + chunk_k) * 2;
-        lds_off = lds_offset(row, chunk);
-    }
-
-    __device__ void load(int k0)
-    {
-        const bool valid = k0 + chunk_k < K;   // K % 8 == 0: a chunk is all in or all out
-        const int step = 32 * K * 2;           // 32 rows further down
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int oa = valid ? a_row_off + i * step + k0 * 2 : OOB;
-            const int ob = valid ? b_row_off + i * step + k0 * 2 : OOB;
-            a_reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, oa, 0, 0));
-            b_reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, ob, 0, 0));
-        }
-    }
-
-    __device__ void commit(uint8_t *stage)
-    {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            *reinterpret_cast<u32x4 *>(stage + lds_off + i * 32 * ROW_BYTES) = a_reg[i];
-            *reinterpret_cast<u32x4 *>(stage + TILE_BYTES + lds_off + i * 32 * ROW_BYTES) = b_reg[i];
-        }
-    }
-
-    static __device__ f32x16 mma(frag s0, frag s1, f32x16 acc)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0, s1, acc, 0, 0, 0);
-    }
-
-    // Sub-step 1: 16 matrix instructions, 8 fragment reads, the 16 LDS
-    // writes of the next slice.
-    static __device__ void schedule_commit()
-    {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            SCHED(SG_MFMA, 1);
-            SCHED(SG_DS_READ, 1);
-            SCHED(SG_DS_WRITE, 1);
-            SCHED(SG_MFMA, 1);
-            SCHED(SG_DS_WRITE, 1);
-        }
-    }
-
-    // Sub-step 2: 16 matrix instructions, 8 fragment reads, the 16 global
-    // reads of the slice after next.
-    static __device__ void schedule_load()
-    {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            SCHED(SG_MFMA, 1);
-            SCHED(SG_DS_READ, 1);
-            SCHED(SG_VMEM_READ, 2);
-            SCHED(SG_MFMA, 1);
-        }
-    }
-};
 
 // ---- block-scaled FP4 operands ---------------------------------------------
 //
@@ -333,21 +169,12 @@ struct Fp4Staging {
 
 // ---- the persistent kernel --------------------------------------------------
 
-// Make this wave's LDS writes visible to the workgroup and wait for all waves.
-// Only LDS is fenced: global loads still in flight stay in flight.
-__device__ inline void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-template <class Staging>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
-void gemm_nt_kernel(Problem p)
+void gemm_nvfp4_nt_kernel(Problem p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-    typedef typename Staging::frag frag;
+    typedef Fp4Staging Staging;
+    typedef Staging::frag frag;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -447,32 +274,9 @@ void gemm_nt_kernel(Problem p)
             SCHED_FENCE();
         }
 
-        // Epilogue: lane holds C[m][nb + 8 g + 4 half + e] in acc[i][j][4 g + e].
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = tm * BM + wm * 128 + i * 32 + l32;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int nb = tn * BN + wn * 128 + j * 32;
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int g0 = 2 * q;
-                    unsigned x0 = pack_bf16(acc[i][j][4 * g0 + 0], acc[i][j][4 * g0 + 1]);
-                    unsigned x1 = pack_bf16(acc[i][j][4 * g0 + 2], acc[i][j][4 * g0 + 3]);
-                    unsigned y0 = pack_bf16(acc[i][j][4 * g0 + 4], acc[i][j][4 * g0 + 5]);
-                    unsigned y1 = pack_bf16(acc[i][j][4 * g0 + 6], acc[i][j][4 * g0 + 7]);
-                    // lower half-wave keeps group g0 and receives the upper half's
-                    // part of it; the upper half-wave ends up with group g0 + 1.
-                    auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-                    auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-                    const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
-                    const int n = nb + (g0 + half) * 8;
-                    const int off = (m < p.M && n < p.N) ? (m * p.N + n) * 2 : OOB;
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc, off, 0, 0);
-                }
-            }
-        }
+        store_tile(acc, rc, p.M, p.N, tm * BM + wm * 128, tn * BN + wn * 128, l32, half);
     }
 }
 
+} // namespace fp4
 } // namespace gemm355
