@@ -136,7 +136,7 @@ def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
     g = np.random.Generator(np.random.PCG64(seed))
     cores = oracle.max_threads()
     # calibrate on a small batch, then size the timed sample to the target
-    n0 = max(64, cores * 8)
+    n0 = max(256, cores * 64)
     t0 = time.perf_counter()
     fn(g.integers(0, M, n0).astype(np.int32), g.integers(0, N, n0).astype(np.int32))
     rate = n0 / max(time.perf_counter() - t0, 1e-6)
@@ -185,7 +185,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="bf16_8192", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (used for profiler runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args(argv)
