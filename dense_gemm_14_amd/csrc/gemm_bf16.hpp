@@ -1,55 +1,76 @@
-// gemm_bf16.hpp -- persistent BF16 NT GEMM for gfx950 with operands copied
-// straight from global memory into LDS (buffer_load_dwordx4 ... lds).
+// gemm_bf16.hpp -- persistent BF16 NT GEMM for gfx950: v_mfma_f32_16x16x32_bf16
+// on operands copied straight from global memory into a ring of LDS slots.
 //
 // Work decomposition
 //   * Output tile 256 x 256 per workgroup, 4 waves in a 2 x 2 layout; each
-//     wave owns a 128 x 128 block = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16
-//     whose FP32 accumulators (256 per lane) stay in the accumulation registers
-//     for the whole K loop.
-//   * K advances 64 at a time through two LDS stages of 64 KiB (A tile
-//     256 x 64, then B tile 256 x 64, BF16). Each 1 KiB block of a stage is
-//     written by one copy instruction of the memory pipeline (lane i fills
-//     bytes 16 i .. 16 i + 15 of the block: 8 rows x 128 bytes), so operands
-//     pass through no registers and no LDS-write instructions, and every
-//     request is one whole 128-byte row segment of A or B.
-//   * LDS tile rows are 128 bytes (64 elements, eight 16-byte chunks); logical
-//     chunk c of row r sits at chunk position c ^ ((r >> 1) & 7). gfx950 serves
-//     a ds_read_b128 16 lanes (256 bytes over 64 four-byte banks) per cycle;
-//     the 16 lanes read 16 consecutive rows at one logical chunk, row parity
-//     picks the 128-byte half of the bank space and (r >> 1) & 7 the chunk
-//     within it, so the 16 lanes hit 16 distinct bank groups (measured: 4
-//     cycles per read, no conflicts). The swizzle is applied on the global
-//     side: the lane that fills position p of row r fetches logical chunk
-//     p ^ ((r >> 1) & 7).
-//   * Step kt (one barrier): sub-steps 0..2 run 16 matrix instructions each
-//     on stage kt & 1 while the next sub-step's fragments are read; each wave
-//     then waits for its own copies of slice kt + 1 (vmcnt), the barrier makes
-//     all of them visible and releases stage kt & 1, and sub-step 3 runs while
-//     the first fragments of slice kt + 1 are read and slice kt + 2 is
-//     requested into the stage just released.
+//     wave owns a 128 x 128 block = 8 x 8 blocks of 16 x 16 whose FP32
+//     accumulators (256 per lane) stay in the accumulation registers for the
+//     whole K loop. The 16 x 16 x 32 instruction moves half the accumulator
+//     data per multiply-add of the 32 x 32 x 16 one, which lowers the energy
+//     per product and so the clock throttling under the board power limit.
+//   * K advances 64 per step. A step is split into two half-steps of K = 32;
+//     a half-step is 64 matrix instructions on one set of fragments (8 A
+//     blocks, 8 B blocks, 16 bytes per lane each) while the other set is
+//     read from LDS.
+//   * LDS is a ring of five 32 KiB slots; a slot holds one unit, the A tile
+//     (256 rows x 64 K) or the B tile of one step, as 256 rows of 128 bytes.
+//     Unit 2 s + op (op 0 = A, 1 = B) lives in slot (2 s + op) mod 5. Each 1
+//     KiB block of a unit is written by one copy instruction of the memory
+//     pipeline (lane i fills bytes 16 i .. 16 i + 15 of the block: 8 rows x
+//     128 bytes), so operands pass through no registers and no LDS-write
+//     instructions, and every request is one whole 128-byte row segment.
+//   * One barrier per step, between its two half-steps. Before it each wave
+//     has finished reading step s (so both of its slots are free) and its
+//     copies of step s + 1 have landed. The barrier opens a copy window that
+//     runs until the next barrier: the B tile of step s + 2 (into the slot of
+//     A_s, needed one step later) and the A tile of step s + 3 (into the slot
+//     of B_s, needed two steps later). Five slots give every copy at least a
+//     whole step, and half of them two steps, between issue and first use.
+//   * LDS rows are 128 bytes (eight 16-byte chunks); logical chunk c of row r
+//     sits at chunk position c ^ ((r >> 1) & 7). A fragment read serves 16
+//     lanes (256 bytes over the 64 four-byte banks) per cycle; those lanes
+//     read 16 consecutive rows at one logical chunk, row parity picks the
+//     128-byte half of the bank space and (r >> 1) & 7 the chunk within it,
+//     so the 16 lanes hit 16 distinct bank groups. The swizzle is applied on
+//     the global side: the lane that fills position p of row r fetches
+//     logical chunk p ^ ((r >> 1) & 7).
 #pragma once
 
 #include "common.hpp"
 
+#include <utility>
+
 namespace gemm355 {
 namespace bf16 {
 
-constexpr int BK = 64;                       // K elements per pipeline step
+constexpr int BK = 64;                       // K elements per step
 constexpr int ROW_BYTES = BK * 2;            // 128-byte LDS rows
-constexpr int TILE_BYTES = BM * ROW_BYTES;   // 32 KiB per operand per stage
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // A tile then B tile
-constexpr int STAGES = 2;
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-constexpr int COPIES = 16;                   // 1 KiB copies per wave per step (8 A + 8 B)
+constexpr int UNIT_BYTES = BM * ROW_BYTES;   // one operand tile of one step: 32 KiB
+constexpr int SLOTS = 5;
+constexpr int LDS_BYTES = SLOTS * UNIT_BYTES;
+constexpr int UNIT_COPIES = 8;               // 1 KiB copies per wave per unit (64 rows)
+constexpr int WINDOW_COPIES = 2 * UNIT_COPIES;
 
 static_assert(LDS_BYTES <= 163840, "LDS ring exceeds the 160 KiB of a gfx950 workgroup");
 static_assert(BM == 256 && BN == 256 && THREADS == 256, "the copy map assumes 256 x 256 tiles and 4 waves");
 
-// Physical 16-byte chunk position of logical chunk c in LDS tile row r (an
-// involution: it also gives the logical chunk stored at position c).
+// Instruction positions inside a half-step of 64 matrix instructions.
+// Fragment read r (0..15) follows matrix instruction read_at(r): all reads are
+// issued in the first three quarters so they have landed by the half-step's end.
+constexpr int read_at(int r) { return 3 * r + 1; }
+// Copy c of a window (0..7: B tile, 8..15: A tile) at window position
+// copy_at(c): positions 0..63 are the second half of the step that opened the
+// window, 64..127 the first half of the next step. One copy every eight
+// matrix instructions keeps the copy pipeline at about half load throughout.
+constexpr int copy_at(int c) { return c < UNIT_COPIES ? 8 * c + 1 : 68 + 8 * (c - UNIT_COPIES); }
+// Fragment read order: A0, B0..B7, A1..A7, so the first matrix instructions of
+// a half-step (A block 0 against every B block) wait for two reads only.
+constexpr int read_block(int r) { return r == 0 ? 0 : r <= 8 ? 8 + (r - 1) : r - 8; }
+
 __device__ inline int swizzle(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource as four scalar words, for the inline-assembly copies.
 __device__ inline i32x4 rsrc_words(const void *p, unsigned bytes)
@@ -74,6 +95,21 @@ __device__ inline void copy_1k(const i32x4 &rsrc, unsigned lds_addr, int voff)
 
 // Every copy this wave issued has landed in LDS (stores too).
 __device__ inline void wait_all_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// At most N copies of this wave are still in flight (they complete in order).
+template <int N>
+__device__ inline void wait_copies_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// Every LDS read this wave issued has returned.
+__device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Compile-time loop: f(Int<0>{}), ..., f(Int<N - 1>{}).
+template <int V> struct Int { static constexpr int value = V; };
+template <class F, int... I>
+__device__ inline void static_for_impl(F &&f, std::integer_sequence<int, I...>) { (f(Int<I>{}), ...); }
+template <int N, class F>
+__device__ inline void static_for(F &&f) { static_for_impl(f, std::make_integer_sequence<int, N>{}); }
+
+// LDS byte offset of the slot that holds unit 2 s + op.
+__device__ inline int slot_offset(int s, int op) { return ((2 * s + op) % SLOTS) * UNIT_BYTES; }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_kernel(Problem p)
@@ -85,25 +121,20 @@ void gemm_bf16_nt_kernel(Problem p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1;   // wave's 128-row half of the tile (A rows)
     const int wn = wave >> 1;  // wave's 128-column half (B rows)
-    const int l32 = lane & 31;
-    const int half = lane >> 5;
+    const int l16 = lane & 15;
+    const int grp = lane >> 4;
     const int K = p.K;
 
-    // Fragment reads: row l32 + 32 i of the wave's block, logical chunk
-    // 2 kk + half for sub-step kk (rows differ from l32 by multiples of 32,
-    // which leaves the swizzle unchanged).
-    const int a_frag = (wm * 128 + l32) * ROW_BYTES;
-    const int b_frag = TILE_BYTES + (wn * 128 + l32) * ROW_BYTES;
-    int kofs[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        kofs[kk] = swizzle(l32, 2 * kk + half) << 4;
-
-    // Copies: wave w fills blocks 8 w .. 8 w + 7 (rows 64 w .. 64 w + 63) of the
-    // A tile and of the B tile; lane i fills position i & 7 of row 8 b + i / 8.
+    // Fragment of a 16-row block: lane (l16, grp) reads row l16 of the block,
+    // logical chunk grp (first half-step) or 4 + grp (second half-step).
+    // Blocks start at multiples of 16 rows, which leaves the swizzle unchanged.
+    const int kofs0 = swizzle(l16, grp) << 4;
+    const int kofs1 = swizzle(l16, 4 + grp) << 4;
+    const int a_frag = (wm * 128 + l16) * ROW_BYTES;
+    const int b_frag = (wn * 128 + l16) * ROW_BYTES;
     const int copy_row = lane >> 3;
-    const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
 
+    const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
     const i32x4 ra = rsrc_words(p.a, (unsigned)p.M * (unsigned)K * 2u);
     const i32x4 rb = rsrc_words(p.b, (unsigned)p.N * (unsigned)K * 2u);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
@@ -116,111 +147,165 @@ void gemm_bf16_nt_kernel(Problem p)
         int tm, tn;
         supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
 
-        // per block: byte offset of this lane's chunk in its A row and B row,
-        // and the chunk's first K index (the K tail switches whole chunks off)
-        int a_off[8], b_off[8], chunk_k[8];
+        // Copies: wave w fills blocks 8 w .. 8 w + 7 (rows 64 w .. 64 w + 63) of
+        // every unit; lane i fills position i & 7 of row 8 b + i / 8. Per block:
+        // byte offset of this lane's chunk in its A row and B row, and the
+        // chunk's first K index (the K tail switches whole chunks off).
+        int a_off[UNIT_COPIES], b_off[UNIT_COPIES], chunk_k[UNIT_COPIES];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = 8 * (8 * wave + j) + copy_row;
+        for (int j = 0; j < UNIT_COPIES; ++j) {
+            const int row = 8 * (UNIT_COPIES * wave + j) + copy_row;
             const int c = swizzle(row, lane & 7);   // logical chunk stored at position lane & 7
             chunk_k[j] = 8 * c;
             a_off[j] = ((tm * BM + row) * K + 8 * c) * 2;
             b_off[j] = ((tn * BN + row) * K + 8 * c) * 2;
         }
+        // Per-step bases, hidden from the optimiser again at every step so
+        // that addresses are formed where they are used instead of being
+        // hoisted out of the loop into registers (which would spill).
+        unsigned copy_base = lds_base + (unsigned)(UNIT_COPIES * wave * 1024);
+        int a_ofs[2] = {a_frag + kofs0, a_frag + kofs1};
+        int b_ofs[2] = {b_frag + kofs0, b_frag + kofs1};
 
-        // Copy t (0..15) of K slice `slice` into its stage: block 8 w + t / 2
-        // of A for even t, of B for odd t. Slices at or past K, and the K tail,
-        // read as zeros; rows past M or N fall outside the buffer and do too.
-        auto copy = [&](int slice, int t) {
-            const int k0 = slice * BK;
-            const int j = t >> 1;
-            const bool valid = k0 + chunk_k[j] < K;
-            const unsigned dst = lds_base + (unsigned)((slice % STAGES) * STAGE_BYTES +
-                                                       ((t & 1) ? TILE_BYTES : 0) + (8 * wave + j) * 1024);
-            const int off = (t & 1) ? b_off[j] : a_off[j];
-            copy_1k((t & 1) ? rb : ra, dst, valid ? off + k0 * 2 : OOB);
+        // Copy j of unit 2 s + op. Steps at or past the end of K, and the K
+        // tail, read as zeros; rows past M or N fall outside the buffer and do
+        // too.
+        auto copy = [&](int s, int op, int j) {
+            const int k0 = s * BK;
+            const bool valid = s < nk && k0 + chunk_k[j] < K;
+            const unsigned dst = copy_base + (unsigned)(slot_offset(s, op) + j * 1024);
+            copy_1k(op ? rb : ra, dst, valid ? (op ? b_off[j] : a_off[j]) + k0 * 2 : OOB);
         };
-
-        f32x16 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = f32x16{};
-
-        bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-        // fragment read r (0..7): A block r for r < 4, B block r - 4 otherwise
-        auto read_frag = [&](const uint8_t *stage, int kofs, bf16x8 *fa, bf16x8 *fb, int r) {
-            if (r < 4)
-                fa[r] = *reinterpret_cast<const bf16x8 *>(stage + a_frag + r * 32 * ROW_BYTES + kofs);
+        // Copy c of the window opened by the barrier of step s.
+        auto window_copy = [&](int s, int c) {
+            if (c < UNIT_COPIES)
+                copy(s + 2, 1, c);
             else
-                fb[r - 4] = *reinterpret_cast<const bf16x8 *>(stage + b_frag + (r - 4) * 32 * ROW_BYTES + kofs);
-        };
-        // matrix instruction t (0..15) of a sub-step: block (t / 4, t % 4)
-        auto mma = [&](const bf16x8 *fa, const bf16x8 *fb, int t) {
-            const int i = t >> 2, j = t & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+                copy(s + 3, 0, c - UNIT_COPIES);
         };
 
-        // Copies of the previous tile (including its zero slices past K) and its
-        // stores have landed before the stages are refilled.
+        f32x4 acc[8][8];
+        bf16x8 fa[2][8], fb[2][8];
+        // Read r of half-step h of step s into fragment set h.
+        auto read = [&](int s, int h, int r) {
+            const int q = read_block(r);
+            if (q < 8)
+                fa[h][q] = *reinterpret_cast<const bf16x8 *>(lds + (a_ofs[h] + slot_offset(s, 0)) + q * 16 * ROW_BYTES);
+            else
+                fb[h][q - 8] = *reinterpret_cast<const bf16x8 *>(lds + (b_ofs[h] + slot_offset(s, 1)) +
+                                                                 (q - 8) * 16 * ROW_BYTES);
+        };
+        // Matrix instruction t of a half-step: block (t / 8, t % 8). B rows are
+        // the first operand and A rows the second, so each 16 x 16 result
+        // arrives transposed (one C row per lane, four adjacent columns).
+        auto mma = [&](int h, int t, bool first) {
+            const int i = t >> 3, j = t & 7;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], first ? f32x4{} : acc[i][j], 0, 0, 0);
+        };
+
+        // Copies of the previous tile (including its zero units past K), its
+        // reads and its stores are done before the ring is refilled.
+        wait_reads();
         wait_all_copies();
         lds_barrier();
+        // units A0, B0, A1, B1, A2 fill the ring
 #pragma unroll
-        for (int t = 0; t < COPIES; ++t)
-            copy(0, t);
-        wait_all_copies();
+        for (int u = 0; u < SLOTS; ++u)
+#pragma unroll
+            for (int j = 0; j < UNIT_COPIES; ++j)
+                copy(u >> 1, u & 1, j);
+        wait_copies_le<3 * UNIT_COPIES>();   // A0 and B0 have landed
         lds_barrier();
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            read_frag(lds, kofs[0], fa0, fb0, r);
-#pragma unroll
-        for (int t = 0; t < COPIES; ++t)
-            copy(1, t);
+        for (int r = 0; r < 16; ++r)
+            read(0, 0, r);
         SCHED_FENCE();
 
-        // The instruction order inside a step is fixed by hand (SCHED_FENCE
-        // after every group): each matrix instruction is followed by at most
-        // one fragment read and one copy.
-        for (int kt = 0; kt < nk; ++kt) {
-            const uint8_t *cur = lds + (kt % STAGES) * STAGE_BYTES;
-            const uint8_t *nxt = lds + ((kt + 1) % STAGES) * STAGE_BYTES;
+        // Step s. The instruction order inside each half-step is fixed by hand
+        // (SCHED_FENCE after every matrix instruction and what follows it).
+        auto step = [&](int s, auto first_c) {
+            constexpr bool first = decltype(first_c)::value;
+            asm volatile("" : "+v"(a_ofs[0]), "+v"(a_ofs[1]), "+v"(b_ofs[0]), "+v"(b_ofs[1]), "+s"(copy_base));
+            // first half-step: fragments 0; read the second half of step s;
+            // finish the window of step s - 1 (the prologue filled step 0's)
+            static_for<64>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                mma(0, t, first);
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                mma(fa0, fb0, t);
-                if (t < 8)
-                    read_frag(cur, kofs[1], fa1, fb1, t);
-                SCHED_FENCE();
-            }
+                for (int r = 0; r < 16; ++r)
+                    if (t == read_at(r))
+                        read(s, 1, r);
+                if (!first) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                mma(fa1, fb1, t);
-                if (t < 8)
-                    read_frag(cur, kofs[2], fa0, fb0, t);
+                    for (int c = 0; c < WINDOW_COPIES; ++c)
+                        if (64 + t == copy_at(c))
+                            window_copy(s - 1, c);
+                }
                 SCHED_FENCE();
-            }
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                mma(fa0, fb0, t);
-                if (t < 8)
-                    read_frag(cur, kofs[3], fa1, fb1, t);
-                SCHED_FENCE();
-            }
-            wait_all_copies();     // this wave's copies of slice kt + 1 have landed
-            lds_barrier();         // ... and everybody's; stage `cur` is released
+            });
+            // step s is fully read by this wave and its copies of step s + 1
+            // (the B tile of step s + 1 and everything issued before it) have
+            // landed; only the A tile of step s + 2 may still be in flight
+            wait_reads();
+            wait_copies_le<UNIT_COPIES>();
+            lds_barrier();
             SCHED_FENCE();
+            // second half-step: fragments 1; read the first half of step s + 1;
+            // open the window of step s
+            static_for<64>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                mma(1, t, false);
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                mma(fa1, fb1, t);
-                if (t < 8)
-                    read_frag(nxt, kofs[0], fa0, fb0, t);
-                copy(kt + 2, t);   // slice kt + 2 into the released stage
+                for (int r = 0; r < 16; ++r)
+                    if (t == read_at(r))
+                        read(s + 1, 0, r);
+#pragma unroll
+                for (int c = 0; c < WINDOW_COPIES; ++c)
+                    if (t == copy_at(c))
+                        window_copy(s, c);
                 SCHED_FENCE();
-            }
+            });
+        };
+
+        if (nk == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[i][j] = f32x4{};
+        } else {
+            step(0, Int<1>{});
+            for (int s = 1; s < nk; ++s)
+                step(s, Int<0>{});
         }
 
-        store_tile(acc, rc, p.M, p.N, tm * BM + wm * 128, tn * BN + wn * 128, l32, half);
+        // Epilogue. Lane (l16, grp) of block (i, j) holds C[m][n .. n + 3] with
+        // m = m0 + 16 i + l16 and n = n0 + 16 j + 4 grp. For a pair of blocks
+        // (x = block 2 jp, y = block 2 jp + 1) v_permlane16_swap exchanges
+        // lane groups so that group 0 holds columns 0..7 of x, group 1 columns
+        // 0..7 of y, group 2 columns 8..15 of x and group 3 columns 8..15 of
+        // y: one 16-byte store per lane, 64 contiguous bytes per C row.
+        const int m = tm * BM + wm * 128 + l16;
+        const int n0 = tn * BN + wn * 128 + 16 * (grp & 1) + 8 * (grp >> 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int jp = 0; jp < 4; ++jp) {
+                const f32x4 &x = acc[i][2 * jp];
+                const f32x4 &y = acc[i][2 * jp + 1];
+                const unsigned x0 = pack_bf16(x[0], x[1]), x1 = pack_bf16(x[2], x[3]);
+                const unsigned y0 = pack_bf16(y[0], y[1]), y1 = pack_bf16(y[2], y[3]);
+                const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
+                const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+                const int mm = m + 16 * i;
+                const int n = n0 + 32 * jp;
+                const int off = (mm < p.M && n < p.N) ? (mm * p.N + n) * 2 : OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(out, rc, off, 0, 0);
+            }
+        }
     }
+    wait_reads();
     wait_all_copies(); // no copy may still be writing LDS when the workgroup ends
 }
 
