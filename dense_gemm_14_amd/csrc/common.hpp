@@ -75,6 +75,8 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200 };
 #define SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+// Like SCHED_FENCE, but plain vector ALU instructions may still cross.
+#define SCHED_VALU_ONLY() __builtin_amdgcn_sched_barrier(SG_VALU)
 
 // One sub-step: 16 matrix instructions with 8 fragment reads threaded in,
 // one read after each of the first 8.

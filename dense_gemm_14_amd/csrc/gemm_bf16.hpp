@@ -221,8 +221,12 @@ void gemm_bf16_nt_kernel(Problem p)
             read(0, 0, r);
         SCHED_FENCE();
 
-        // Step s. The instruction order inside each half-step is fixed by hand
-        // (SCHED_FENCE after every matrix instruction and what follows it).
+        // Step s. The order of matrix instructions, LDS reads, copies and
+        // scalar instructions inside each half-step is fixed by hand (a
+        // scheduling barrier after every matrix instruction and what follows
+        // it); only plain vector ALU work (address arithmetic) may move across
+        // those barriers, so its dependency chains spread over several matrix
+        // instructions instead of stalling the issue of the next one.
         auto step = [&](int s, auto first_c) {
             constexpr bool first = decltype(first_c)::value;
             asm volatile("" : "+v"(a_ofs[0]), "+v"(a_ofs[1]), "+v"(b_ofs[0]), "+v"(b_ofs[1]), "+s"(copy_base));
@@ -241,7 +245,7 @@ void gemm_bf16_nt_kernel(Problem p)
                         if (64 + t == copy_at(c))
                             window_copy(s - 1, c);
                 }
-                SCHED_FENCE();
+                SCHED_VALU_ONLY();
             });
             // step s is fully read by this wave and its copies of step s + 1
             // (the B tile of step s + 1 and everything issued before it) have
@@ -263,7 +267,7 @@ void gemm_bf16_nt_kernel(Problem p)
                 for (int c = 0; c < WINDOW_COPIES; ++c)
                     if (t == copy_at(c))
                         window_copy(s, c);
-                SCHED_FENCE();
+                SCHED_VALU_ONLY();
             });
         };
 
