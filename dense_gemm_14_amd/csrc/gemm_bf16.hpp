@@ -108,9 +108,6 @@ __device__ inline void static_for_impl(F &&f, std::integer_sequence<int, I...>) 
 template <int N, class F>
 __device__ inline void static_for(F &&f) { static_for_impl(f, std::make_integer_sequence<int, N>{}); }
 
-// LDS byte offset of the slot that holds unit 2 s + op.
-__device__ inline int slot_offset(int s, int op) { return ((2 * s + op) % SLOTS) * UNIT_BYTES; }
-
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_kernel(Problem p)
 {
@@ -170,30 +167,38 @@ void gemm_bf16_nt_kernel(Problem p)
         // Copy j of unit 2 s + op. Steps at or past the end of K, and the K
         // tail, read as zeros; rows past M or N fall outside the buffer and do
         // too.
-        auto copy = [&](int s, int op, int j) {
+        auto copy = [&](int s, int op, int j, int slot) {
             const int k0 = s * BK;
             const bool valid = s < nk && k0 + chunk_k[j] < K;
-            const unsigned dst = copy_base + (unsigned)(slot_offset(s, op) + j * 1024);
+            const unsigned dst = copy_base + (unsigned)(slot + j * 1024);
             copy_1k(op ? rb : ra, dst, valid ? (op ? b_off[j] : a_off[j]) + k0 * 2 : OOB);
         };
-        // Copy c of the window opened by the barrier of step s.
-        auto window_copy = [&](int s, int c) {
+        // ring[x]: LDS offset of the slot of unit 2 s + x during step s (x =
+        // 0..4). The next step sees the same slots rotated by two units, so the
+        // offsets are carried in scalar registers and renamed, never computed.
+        int ring[SLOTS];
+#pragma unroll
+        for (int x = 0; x < SLOTS; ++x)
+            ring[x] = x * UNIT_BYTES;
+        // Copy c of the window opened by the barrier of step s - d, issued
+        // during step s (d = 0: second half-step, d = 1: first half-step).
+        auto window_copy = [&](int s, int d, int c) {
             if (c < UNIT_COPIES)
-                copy(s + 2, 1, c);
+                copy(s - d + 2, 1, c, ring[(5 - 2 * d) % SLOTS]);   // unit 2 s + 5 - 2 d
             else
-                copy(s + 3, 0, c - UNIT_COPIES);
+                copy(s - d + 3, 0, c - UNIT_COPIES, ring[(6 - 2 * d) % SLOTS]);
         };
 
         f32x4 acc[8][8];
         bf16x8 fa[2][8], fb[2][8];
         // Read r of half-step h of step s into fragment set h.
-        auto read = [&](int s, int h, int r) {
+        // Read r of half-step h of the step whose units sit in slots sa, sb.
+        auto read = [&](int sa, int sb, int h, int r) {
             const int q = read_block(r);
             if (q < 8)
-                fa[h][q] = *reinterpret_cast<const bf16x8 *>(lds + (a_ofs[h] + slot_offset(s, 0)) + q * 16 * ROW_BYTES);
+                fa[h][q] = *reinterpret_cast<const bf16x8 *>(lds + (a_ofs[h] + sa) + q * 16 * ROW_BYTES);
             else
-                fb[h][q - 8] = *reinterpret_cast<const bf16x8 *>(lds + (b_ofs[h] + slot_offset(s, 1)) +
-                                                                 (q - 8) * 16 * ROW_BYTES);
+                fb[h][q - 8] = *reinterpret_cast<const bf16x8 *>(lds + (b_ofs[h] + sb) + (q - 8) * 16 * ROW_BYTES);
         };
         // Matrix instruction t of a half-step: block (t / 8, t % 8). B rows are
         // the first operand and A rows the second, so each 16 x 16 result
@@ -213,12 +218,12 @@ void gemm_bf16_nt_kernel(Problem p)
         for (int u = 0; u < SLOTS; ++u)
 #pragma unroll
             for (int j = 0; j < UNIT_COPIES; ++j)
-                copy(u >> 1, u & 1, j);
+                copy(u >> 1, u & 1, j, u * UNIT_BYTES);
         wait_copies_le<3 * UNIT_COPIES>();   // A0 and B0 have landed
         lds_barrier();
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            read(0, 0, r);
+            read(ring[0], ring[1], 0, r);
         SCHED_FENCE();
 
         // Step s. The order of matrix instructions, LDS reads, copies and
@@ -238,12 +243,12 @@ void gemm_bf16_nt_kernel(Problem p)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (t == read_at(r))
-                        read(s, 1, r);
+                        read(ring[0], ring[1], 1, r);
                 if (!first) {
 #pragma unroll
                     for (int c = 0; c < WINDOW_COPIES; ++c)
                         if (64 + t == copy_at(c))
-                            window_copy(s - 1, c);
+                            window_copy(s, 1, c);
                 }
                 SCHED_VALU_ONLY();
             });
@@ -262,11 +267,11 @@ void gemm_bf16_nt_kernel(Problem p)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (t == read_at(r))
-                        read(s + 1, 0, r);
+                        read(ring[2], ring[3], 0, r);
 #pragma unroll
                 for (int c = 0; c < WINDOW_COPIES; ++c)
                     if (t == copy_at(c))
-                        window_copy(s, c);
+                        window_copy(s, 0, c);
                 SCHED_VALU_ONLY();
             });
         };
@@ -278,9 +283,20 @@ void gemm_bf16_nt_kernel(Problem p)
                 for (int j = 0; j < 8; ++j)
                     acc[i][j] = f32x4{};
         } else {
+            auto rotate = [&]() {
+                const int r0 = ring[0], r1 = ring[1];
+                ring[0] = ring[2];
+                ring[1] = ring[3];
+                ring[2] = ring[4];
+                ring[3] = r0;
+                ring[4] = r1;
+            };
             step(0, Int<1>{});
-            for (int s = 1; s < nk; ++s)
+            rotate();
+            for (int s = 1; s < nk; ++s) {
                 step(s, Int<0>{});
+                rotate();
+            }
         }
 
         // Epilogue. Lane (l16, grp) of block (i, j) holds C[m][n .. n + 3] with
