@@ -48,7 +48,16 @@ WORKLOADS = {
 }
 CONFIG_INDEX = {"bf16_256": 0, "bf16_4096": 1, "bf16_8192": 2, "bf16_8000": 3, "bf16_skinny": 3,
                 "fp4_8192": 4}
-KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel"}
+KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel",
+               "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel"}
+
+
+def kernel_for(kind: str, M: int, N: int) -> str:
+    """The kernel gemm_bf16_nt / gemm_nvfp4_nt launches for this shape (the
+    library's rule: fewer than 128 tiles of 256 x 256 -> 64 x 64 tiles)."""
+    if kind == "bf16" and (-(-M // 256)) * (-(-N // 256)) < 128:
+        return KERNEL_NAME["bf16_small"]
+    return KERNEL_NAME[kind]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -236,17 +245,17 @@ def main(argv=None):
 
     dtype = "bf16" if kind == "bf16" else "fp16"  # FP4 operands are decoded to FP16 for the MFMA
     traffic = read_traffic(args.workload, flops)
-    roofline = {
-        "bound": "mfma",
-        "kernel": KERNEL_NAME[kind],
-        "achieved": round(tflops, 2),
-        "peak": PEAK_TFLOPS[dtype],
-        "unit": "TFLOP/s",
-        "frac": round(tflops / PEAK_TFLOPS[dtype], 4),
-        "traffic": traffic,
-        "algorithmic_bytes": algorithmic_bytes(kind, M, N, K),
-        "mean_launch_ms": round(ms_step, 5),
-    }
+    alg_bytes = algorithmic_bytes(kind, M, N, K)
+    ridge = PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
+    if flops / alg_bytes >= ridge:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+                    "frac": round(tflops / PEAK_TFLOPS[dtype], 4)}
+    else:  # below the ridge the kernel is bound by HBM: algorithmic bytes per launch time
+        gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roofline.update({"kernel": kernel_for(kind, M, N), "traffic": traffic, "algorithmic_bytes": alg_bytes,
+                     "mean_launch_ms": round(ms_step, 5)})
     out = {
         "metric": "TFLOP/s for BF16 C=A·B^T at M=N=K=8192; % of MI355X dense BF16 peak"
         if args.workload == "bf16_8192" else "TFLOP/s for %s C=A·B^T at %dx%dx%d" % (kind, M, N, K),

@@ -8,6 +8,7 @@ The functions mirror the C entry points declared in ``include/gemm355.h``:
 
     gemm_bf16_nt(M, N, K, A, B, C, stream=None)
     gemm_nvfp4_nt(M, N, K, Aq, SFA, Bq, SFB, C, stream=None)
+    force_instance(instance)          # BF16 instance override (diagnostic)
 
 Operands may be torch tensors on a ROCm device (their storage is checked
 against the sizes before the call, since the C side cannot see it) or raw
@@ -30,6 +31,10 @@ ERR_INVALID_ARG = 1
 ERR_UNSUPPORTED = 2
 ERR_NO_DEVICE = 3
 ERR_LAUNCH = 4
+
+INSTANCE_AUTO = 0    # gemm_bf16_nt picks 256 x 256 or 64 x 64 tiles by shape
+INSTANCE_LARGE = 1   # 256 x 256 output tiles
+INSTANCE_SMALL = 2   # 64 x 64 output tiles
 
 _lib = None
 
@@ -63,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.gemm355_tile_order.restype = i
     lib.gemm355_schedule.argtypes = [i, i, p, i]
     lib.gemm355_schedule.restype = i
+    lib.gemm355_force_instance.argtypes = [i]
+    lib.gemm355_force_instance.restype = i
     _lib = lib
     return lib
 
@@ -137,6 +144,12 @@ def gemm_nvfp4_nt(M: int, N: int, K: int, Aq, SFA, Bq, SFB, C, stream=None) -> N
     sfb = _addr(SFB, N * K // 16 if nz else 0, "SFB")
     c = _addr(C, M * N * 2 if nz else 0, "C")
     _check(lib.gemm_nvfp4_nt(M, N, K, aq, sfa, bq, sfb, c, _stream(stream)), "gemm_nvfp4_nt")
+
+
+def force_instance(instance: int) -> None:
+    """Force gemm_bf16_nt's kernel instance for the whole process
+    (INSTANCE_AUTO, INSTANCE_LARGE or INSTANCE_SMALL)."""
+    _check(load().gemm355_force_instance(instance), "gemm355_force_instance")
 
 
 def tile_order(tiles_m: int, tiles_n: int, supergroup: int):

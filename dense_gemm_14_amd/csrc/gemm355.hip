@@ -3,11 +3,13 @@
 // is declared in include/gemm355.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 #include <stdint.h>
 
 #include "gemm355.h"
 #include "gemm_bf16.hpp"
+#include "gemm_bf16_small.hpp"
 #include "gemm_fp4.hpp"
 #include "schedule.hpp"
 
@@ -19,6 +21,14 @@ using gemm355::Problem;
 
 constexpr int kMaxDevices = 64;
 constexpr int kSupergroup = 8; // adjacent N tiles per band of the visiting order
+
+// BF16 kernel instance: 0 = chosen by shape, 1 = 256 x 256 tiles, 2 = 64 x 64
+// tiles (set through gemm355_force_instance, for tests and measurements).
+std::atomic<int> g_bf16_instance{0};
+
+// The 256 x 256 kernel needs enough tiles to occupy the compute units; below
+// half of them (128 tiles) the 64 x 64 kernel streams the operands faster.
+constexpr int64_t kSmallTileThreshold = 128;
 
 std::mutex g_cu_lock;
 int g_cu_count[kMaxDevices];   // 0 = not queried yet
@@ -61,14 +71,14 @@ bool extent_ok(int64_t rows, int64_t row_bytes)
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <class Kernel>
-int launch(Kernel kernel, Problem p, void *stream)
+int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n = BN)
 {
     int cus = 0;
     const int rc = compute_units(&cus);
     if (rc != GEMM355_OK)
         return rc;
-    p.tiles_m = (int)ceil_div(p.M, BM);
-    p.tiles_n = (int)ceil_div(p.N, BN);
+    p.tiles_m = (int)ceil_div(p.M, tile_m);
+    p.tiles_n = (int)ceil_div(p.N, tile_n);
     p.tiles = p.tiles_m * p.tiles_n;
     p.supergroup = kSupergroup;
     p.grid = gemm355::persistent_grid(p.tiles, cus);
@@ -104,7 +114,21 @@ extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, v
     p.M = M;
     p.N = N;
     p.K = K;
+    int instance = g_bf16_instance.load(std::memory_order_relaxed);
+    if (instance == 0)
+        instance = ceil_div(M, BM) * ceil_div(N, BN) < kSmallTileThreshold ? 2 : 1;
+    if (instance == 2)
+        return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel, p, stream, gemm355::bf16_small::TM,
+                      gemm355::bf16_small::TN);
     return launch(gemm355::bf16::gemm_bf16_nt_kernel, p, stream);
+}
+
+extern "C" int gemm355_force_instance(int instance)
+{
+    if (instance < 0 || instance > 2)
+        return GEMM355_ERR_INVALID_ARG;
+    g_bf16_instance.store(instance, std::memory_order_relaxed);
+    return GEMM355_OK;
 }
 
 extern "C" int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,

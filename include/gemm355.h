@@ -24,7 +24,8 @@
  *    happen during the asynchronous execution surface at the caller's next
  *    synchronisation, as usual for HIP.
  *  - Calls are thread-safe: the library holds no mutable state apart from a
- *    per-device cache of the compute-unit count, filled once under a lock.
+ *    per-device cache of the compute-unit count, filled once under a lock,
+ *    and the instance override set by gemm355_force_instance.
  */
 #ifndef GEMM355_H
 #define GEMM355_H
@@ -59,8 +60,25 @@ typedef enum gemm355_status {
  * Requirements, else GEMM355_ERR_UNSUPPORTED: A, B, C 16-byte aligned;
  * K % 8 == 0 and N % 8 == 0 (whole 16-byte row segments); every operand,
  * padded up to a multiple of 256 rows, spans less than 2^31 bytes.
+ * Two kernel instances compute it: 256 x 256 output tiles, or 64 x 64 tiles
+ * when the 256 x 256 tiling has fewer than 128 tiles (too few to occupy the
+ * compute units: a problem then bound by operand traffic, such as M = 128
+ * with N = K = 8192). Both give results within the same bound; they may sum
+ * in different orders.
  */
 int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, void *stream);
+
+/*
+ * gemm355_force_instance -- override the choice of gemm_bf16_nt's instance.
+ *
+ * A diagnostic for tests and measurements (it is not defined by the pages):
+ * instance 0 restores the choice by shape, 1 forces 256 x 256 tiles, 2 forces
+ * 64 x 64 tiles, for every later gemm_bf16_nt call in the process. Returns
+ * GEMM355_OK, or GEMM355_ERR_INVALID_ARG for any other value (the setting is
+ * then unchanged). Calls racing with gemm_bf16_nt on other threads see either
+ * the old or the new setting. No HIP call is made.
+ */
+int gemm355_force_instance(int instance);
 
 /*
  * gemm_nvfp4_nt -- block-scaled FP4 operands, BF16 output.

@@ -112,3 +112,11 @@ def test_schedule_keeps_an_xcds_tiles_compact():
             ms = {tm[p] for p in pos}
             ns = {tn[p] for p in pos}
             assert len(ms) == 4 and len(ns) == 8, (r, x, ms, ns)
+
+
+def test_force_instance_accepts_only_known_instances():
+    lib = g.load()
+    for bad in (-1, 3, 99):
+        assert lib.gemm355_force_instance(bad) == g.ERR_INVALID_ARG
+    for ok in (g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_AUTO):
+        assert lib.gemm355_force_instance(ok) == g.OK

@@ -1,0 +1,86 @@
+"""Both BF16 kernel instances (256 x 256 and 64 x 64 output tiles), each forced
+through gemm355_force_instance, against the oracle: ragged shapes element by
+element, exactly summable inputs bitwise, K = 0, and B = I bitwise. The
+automatic choice routes small problems to the 64 x 64 instance, so without
+forcing, the 256 x 256 instance would only see the large workload shapes."""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_14_amd as g
+import oracle
+import synthetic as syn
+from tests import tolerance
+from tests.gpu_util import GuardedC, need_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+INSTANCES = [g.INSTANCE_LARGE, g.INSTANCE_SMALL]
+
+
+@pytest.fixture
+def forced(request):
+    need_gpu()
+    g.force_instance(request.param)
+    yield request.param
+    g.force_instance(g.INSTANCE_AUTO)
+
+
+def run_bf16(A_bits, B_bits, M, N, K):
+    A = to_dev(A_bits) if A_bits is not None else None
+    B = to_dev(B_bits) if B_bits is not None else None
+    C = GuardedC(M, N)
+    g.gemm_bf16_nt(M, N, K, A, B, C.view)
+    torch.cuda.synchronize()
+    assert C.guards_intact(), "write outside C"
+    return C.bits()
+
+
+SHAPES = [(1, 8, 8), (63, 72, 40), (65, 64, 136), (257, 264, 520), (300, 8, 1000), (128, 1032, 4104),
+          (520, 264, 72)]
+
+
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_forced_instance_matches_oracle(forced, M, N, K):
+    A = syn.bf16_uniform(M, K, seed=5 * M + N + 3 * K)
+    B = syn.bf16_uniform(N, K, seed=5 * M + N + 3 * K + 1)
+    C = run_bf16(A, B, M, N, K)
+    res = tolerance.check(C, oracle.gemm_bf16_nt(A, B), K)
+    assert res, res
+
+
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("M,N,K", [(200, 136, 2056), (64, 64, 64), (513, 520, 264)])
+def test_forced_instance_exact_sums_bitwise(forced, M, N, K):
+    A = syn.bf16_sixteenths(M, K, seed=31 + K)
+    B = syn.bf16_sixteenths(N, K, seed=32 + K)
+    assert np.array_equal(run_bf16(A, B, M, N, K), oracle.gemm_bf16_nt(A, B))
+
+
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+def test_forced_instance_k_zero(forced):
+    assert np.array_equal(run_bf16(None, None, 70, 72, 0), np.zeros((70, 72), np.uint16))
+
+
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+def test_forced_instance_identity(forced):
+    M, K = 96, 520
+    A = syn.bf16_uniform(M, K, seed=77)
+    B = syn.bf16_identity(K)
+    assert np.array_equal(run_bf16(A, B, M, K, K), A)
+
+
+def test_instances_agree_within_bound_at_a_medium_shape():
+    need_gpu()
+    M, N, K = 1024, 1024, 1024   # 16 tiles of 256 x 256: the automatic choice is 64 x 64
+    A = syn.bf16_uniform(M, K, seed=91)
+    B = syn.bf16_uniform(N, K, seed=92)
+    ref = oracle.gemm_bf16_nt(A, B)
+    try:
+        for inst in (g.INSTANCE_AUTO, g.INSTANCE_LARGE, g.INSTANCE_SMALL):
+            g.force_instance(inst)
+            res = tolerance.check(run_bf16(A, B, M, N, K), ref, K)
+            assert res, (inst, res)
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
