@@ -7,9 +7,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "schedule.hpp"
 
 namespace gemm355 {
+
+// Compile-time loop: f(Int<0>{}), ..., f(Int<N - 1>{}).
+template <int V> struct Int { static constexpr int value = V; };
+template <class F, int... I>
+__device__ inline void static_for_impl(F &&f, std::integer_sequence<int, I...>) { (f(Int<I>{}), ...); }
+template <int N, class F>
+__device__ inline void static_for(F &&f) { static_for_impl(f, std::make_integer_sequence<int, N>{}); }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -101,12 +101,6 @@ __device__ inline void wait_copies_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"
 // Every LDS read this wave issued has returned.
 __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Compile-time loop: f(Int<0>{}), ..., f(Int<N - 1>{}).
-template <int V> struct Int { static constexpr int value = V; };
-template <class F, int... I>
-__device__ inline void static_for_impl(F &&f, std::integer_sequence<int, I...>) { (f(Int<I>{}), ...); }
-template <int N, class F>
-__device__ inline void static_for(F &&f) { static_for_impl(f, std::make_integer_sequence<int, N>{}); }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_kernel(Problem p)

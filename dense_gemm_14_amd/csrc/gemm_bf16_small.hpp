@@ -81,11 +81,6 @@ __device__ inline void copy_1k_at(const i32x4 &rsrc, unsigned voff)
 
 __device__ inline void wait_all_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int V> struct Int { static constexpr int value = V; };
-template <class F, int... I>
-__device__ inline void static_for_impl(F &&f, std::integer_sequence<int, I...>) { (f(Int<I>{}), ...); }
-template <int N, class F>
-__device__ inline void static_for(F &&f) { static_for_impl(f, std::make_integer_sequence<int, N>{}); }
 template <int N>
 __device__ inline void wait_copies_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

@@ -25,6 +25,8 @@
 
 #include "common.hpp"
 
+#include <utility>
+
 namespace gemm355 {
 namespace fp4 {
 
@@ -44,7 +46,9 @@ __device__ inline int swizzle(int row, int chunk)
 // ---- block-scaled FP4 operands ---------------------------------------------
 //
 // Thread t stages row t of the A tile and row t of the B tile: per K step of
-// 64 elements that is 32 bytes of packed codes and 4 scale bytes per row.
+// 64 elements that is 32 bytes of packed codes and 4 scale bytes per row,
+// held in one of two register sets (the step being written to LDS and the
+// step after it, already requested from memory).
 // Decoding ("NVFP4 GEMM on Blackwell", section "NVFP4 Datatype"): each code
 // pair converts to two FP16 E2M1 values (v_cvt_scalef32_pk_f16_fp4 with a unit
 // scale), then one packed FP16 multiply applies the E4M3 scale of its 16-element
@@ -54,127 +58,54 @@ __device__ inline int swizzle(int row, int chunk)
 // the E4M3 mantissa goes through the multiply, and FP16 rather than BF16 is
 // used because gfx950 has a packed FP16 multiply but no packed BF16 one; the
 // FP16 and BF16 matrix instructions have the same rate.)
-struct Fp4Staging {
-    typedef f16x8 frag;
-    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
-    int a_code_off, b_code_off, a_sf_off, b_sf_off;
-    int lds_off;
-    int K;
+struct StageRegs {
     u32x4 a_code[2], b_code[2];
     unsigned a_sf, b_sf;
-
-    __device__ void init(const Problem &p, int tm, int tn, int tid)
-    {
-        const unsigned kc = (unsigned)p.K / 2, ks = (unsigned)p.K / 16;
-        K = p.K;
-        ra = make_rsrc(p.a, (unsigned)p.M * kc);
-        rb = make_rsrc(p.b, (unsigned)p.N * kc);
-        rsa = make_rsrc(p.sfa, (unsigned)p.M * ks);
-        rsb = make_rsrc(p.sfb, (unsigned)p.N * ks);
-        a_code_off = (tm * BM + tid) * (int)kc;
-        b_code_off = (tn * BN + tid) * (int)kc;
-        a_sf_off = (tm * BM + tid) * (int)ks;
-        b_sf_off = (tn * BN + tid) * (int)ks;
-        lds_off = tid * ROW_BYTES;
-    }
-
-    __device__ void load(int k0)
-    {
-        // K % 64 == 0: every step is whole; a step at or past K reads zeros
-        const bool valid = k0 < K;
-        const int oc = k0 / 2, os = k0 / 16;
-        const int ac = valid ? a_code_off + oc : OOB, bc = valid ? b_code_off + oc : OOB;
-        a_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, ac, 0, 0));
-        a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, ac + 16, 0, 0));
-        b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, bc, 0, 0));
-        b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, bc + 16, 0, 0));
-        a_sf = __builtin_amdgcn_raw_buffer_load_b32(rsa, valid ? a_sf_off + os : OOB, 0, 0);
-        b_sf = __builtin_amdgcn_raw_buffer_load_b32(rsb, valid ? b_sf_off + os : OOB, 0, 0);
-    }
-
-    // 8 codes (one dword) scaled by `s` -> 8 FP16 values.
-    static __device__ f16x8 decode8(unsigned codes, f16x2 s)
-    {
-        f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
-        f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
-        f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
-        f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
-        f16x8 r = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
-        return r;
-    }
-
-    // Scale block BLK (elements 16 BLK .. 16 BLK + 15 of the step) of one row.
-    template <int BLK>
-    static __device__ void decode_block(uint8_t *row_base, int row, const u32x4 *code, unsigned sf)
-    {
-        const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sf, BLK); // exact
-        const f16x2 s2 = {s, s};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {                    // two dwords = 16 elements
-            const int d = BLK * 2 + h;                   // 16-byte chunk d of the row
-            const unsigned codes = code[d >> 2][d & 3];
-            *reinterpret_cast<f16x8 *>(row_base + (swizzle(row, d) << 4)) = decode8(codes, s2);
-        }
-    }
-
-    static __device__ void decode_row(uint8_t *row_base, int row, const u32x4 *code, unsigned sf)
-    {
-        decode_block<0>(row_base, row, code, sf);
-        decode_block<1>(row_base, row, code, sf);
-        decode_block<2>(row_base, row, code, sf);
-        decode_block<3>(row_base, row, code, sf);
-    }
-
-    __device__ void commit(uint8_t *stage)
-    {
-        const int row = lds_off / ROW_BYTES;
-        decode_row(stage + lds_off, row, a_code, a_sf);
-        decode_row(stage + TILE_BYTES + lds_off, row, b_code, b_sf);
-    }
-
-    static __device__ f32x16 mma(frag s0, frag s1, f32x16 acc)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(s0, s1, acc, 0, 0, 0);
-    }
-
-    // Sub-step 1: 16 matrix instructions, 8 fragment reads, the decode
-    // (vector ALU) and 16 LDS writes of the next slice.
-    static __device__ void schedule_commit()
-    {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            SCHED(SG_MFMA, 1);
-            SCHED(SG_DS_READ, 1);
-            SCHED(SG_VALU, 9);
-            SCHED(SG_DS_WRITE, 1);
-            SCHED(SG_MFMA, 1);
-            SCHED(SG_VALU, 9);
-            SCHED(SG_DS_WRITE, 1);
-        }
-    }
-
-    // Sub-step 2: 16 matrix instructions, 8 fragment reads, the 6 global
-    // reads of the slice after next.
-    static __device__ void schedule_load()
-    {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            SCHED(SG_MFMA, 1);
-            SCHED(SG_DS_READ, 1);
-            SCHED(SG_VMEM_READ, 1);
-            SCHED(SG_MFMA, 1);
-        }
-    }
 };
 
+// 8 codes (one dword) scaled by `s` -> 8 FP16 values.
+__device__ inline f16x8 decode8(unsigned codes, f16x2 s)
+{
+    f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
+    f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
+    f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
+    f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
+    f16x8 r = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+    return r;
+}
+
+// E4M3 scale byte BLK of the dword `sf`, as an FP16 pair (exact).
+template <int BLK>
+__device__ inline f16x2 scale2(unsigned sf)
+{
+    const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sf, BLK);
+    return f16x2{s, s};
+}
+
 // ---- the persistent kernel --------------------------------------------------
+//
+// Step kt computes on LDS stage kt & 1 in four sub-steps of 16 matrix
+// instructions (K = 16 each); each sub-step's fragments are read during the
+// previous one. During sub-steps 0..2 the register set holding step kt + 1 is
+// decoded and written into the other stage, 16-byte chunk by chunk (one chunk
+// every three matrix instructions, so the decode arithmetic fits in the issue
+// gaps of the matrix pipe), and step kt + 2 is requested into the register set
+// step kt occupied. The step's single barrier, before sub-step 3, makes the
+// new stage visible and releases the current one. Fragment reads are spread
+// one per two matrix instructions. Matrix instructions, LDS accesses and loads
+// keep their hand-fixed order; the decode arithmetic may move across the
+// scheduling barriers, so the dependent conversions and multiplies of a chunk
+// spread over several matrix instructions (on gfx950 a wave fits about four
+// vector instructions under one 32 x 32 x 16 matrix instruction before the
+// matrix rate drops; measured).
+constexpr int CHUNK_EVERY = 3;   // matrix instructions per written chunk
+constexpr int LOAD_AT = 2;       // first of the six loads (one every 4 instructions)
 
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_nvfp4_nt_kernel(Problem p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-    typedef Fp4Staging Staging;
-    typedef Staging::frag frag;
+    typedef f16x8 frag;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -183,6 +114,7 @@ void gemm_nvfp4_nt_kernel(Problem p)
     const int wn = wave >> 1;  // wave's 128-column half (B rows)
     const int l32 = lane & 31;
     const int half = lane >> 5;
+    const int K = p.K;
 
     // Per-lane LDS fragment addresses: row (l32 + 32 i) of the wave's block,
     // logical chunk (2 kk + half) for K sub-step kk of 16 elements.
@@ -192,17 +124,19 @@ void gemm_nvfp4_nt_kernel(Problem p)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
         kofs[kk] = swizzle(l32, 2 * kk + half) << 4;   // rows differ from l32 by multiples of 32
-
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
-    const int nk = (p.K + BK - 1) / BK;
-
-    auto read_frags = [&](const uint8_t *stage, int kk, frag *fa, frag *fb) {
+    // chunk positions of this thread's staged row (row tid of each tile)
+    int wpos[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            fa[i] = *reinterpret_cast<const frag *>(stage + a_row + i * 32 * ROW_BYTES + kofs[kk]);
-            fb[i] = *reinterpret_cast<const frag *>(stage + b_row + i * 32 * ROW_BYTES + kofs[kk]);
-        }
-    };
+    for (int d = 0; d < 8; ++d)
+        wpos[d] = tid * ROW_BYTES + (swizzle(tid, d) << 4);
+
+    const unsigned kc = (unsigned)K / 2, ks = (unsigned)K / 16;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (unsigned)p.M * kc);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b, (unsigned)p.N * kc);
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sfa, (unsigned)p.M * ks);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.sfb, (unsigned)p.N * ks);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
+    const int nk = (K + BK - 1) / BK;
 
     for (int round = 0;; ++round) {
         const int pos = schedule_position(blockIdx.x, round, p.grid);
@@ -211,67 +145,119 @@ void gemm_nvfp4_nt_kernel(Problem p)
         int tm, tn;
         supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
 
-        f32x16 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = f32x16{};
+        const int a_code_off = (tm * BM + tid) * (int)kc, b_code_off = (tn * BN + tid) * (int)kc;
+        const int a_sf_off = (tm * BM + tid) * (int)ks, b_sf_off = (tn * BN + tid) * (int)ks;
+        StageRegs regs[2];
+        // load q (0..5) of step kt into register set `set`; K % 64 == 0, so a
+        // step is whole or past K, where it reads zeros
+        auto load = [&](int kt, int set, int q) {
+            const int k0 = kt * BK;
+            const bool valid = k0 < K;
+            StageRegs &r = regs[set];
+            switch (q) {
+            case 0: r.a_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, valid ? a_code_off + k0 / 2 : OOB, 0, 0)); break;
+            case 1: r.a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, valid ? a_code_off + k0 / 2 + 16 : OOB, 0, 0)); break;
+            case 2: r.a_sf = __builtin_amdgcn_raw_buffer_load_b32(rsa, valid ? a_sf_off + k0 / 16 : OOB, 0, 0); break;
+            case 3: r.b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, valid ? b_code_off + k0 / 2 : OOB, 0, 0)); break;
+            case 4: r.b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, valid ? b_code_off + k0 / 2 + 16 : OOB, 0, 0)); break;
+            default: r.b_sf = __builtin_amdgcn_raw_buffer_load_b32(rsb, valid ? b_sf_off + k0 / 16 : OOB, 0, 0); break;
+            }
+        };
+        // chunk c (0..15) of register set `set` into `stage`: c < 8 is chunk c
+        // of the A row, otherwise chunk c - 8 of the B row
+        auto write_chunk = [&](uint8_t *stage, int set, auto c_c) {
+            constexpr int c = decltype(c_c)::value;
+            constexpr int d = c & 7;
+            const StageRegs &r = regs[set];
+            const unsigned codes = (c < 8 ? r.a_code : r.b_code)[d >> 2][d & 3];
+            const f16x2 s = scale2<d / 2>(c < 8 ? r.a_sf : r.b_sf);
+            *reinterpret_cast<f16x8 *>(stage + (c < 8 ? 0 : TILE_BYTES) + wpos[d]) = decode8(codes, s);
+        };
 
-        auto mma_all = [&](const frag *fa, const frag *fb) {
+        f32x16 acc[4][4];
+        frag fa[2][4], fb[2][4];
+        auto read_frags = [&](const uint8_t *stage, int kk, int set) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                fa[set][i] = *reinterpret_cast<const frag *>(stage + a_row + i * 32 * ROW_BYTES + kofs[kk]);
+                fb[set][i] = *reinterpret_cast<const frag *>(stage + b_row + i * 32 * ROW_BYTES + kofs[kk]);
+            }
+        };
+        // fragment read r (0..7): A block r for r < 4, else B block r - 4
+        auto read_frag = [&](const uint8_t *stage, int kk, int set, int r) {
+            if (r < 4)
+                fa[set][r] = *reinterpret_cast<const frag *>(stage + a_row + r * 32 * ROW_BYTES + kofs[kk]);
+            else
+                fb[set][r - 4] = *reinterpret_cast<const frag *>(stage + b_row + (r - 4) * 32 * ROW_BYTES + kofs[kk]);
+        };
+        auto mma = [&](int set, int t, bool first) {
+            const int i = (t >> 2) & 3, j = t & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[set][j], fa[set][i], first ? f32x16{} : acc[i][j], 0, 0, 0);
+        };
+
+        // Prologue: step 0 into stage 0, step 1 requested into set 1.
+        lds_barrier();            // every wave is done with the previous tile's stages
+#pragma unroll
+        for (int q = 0; q < 6; ++q)
+            load(0, 0, q);
+#pragma unroll
+        for (int q = 0; q < 6; ++q)
+            load(1, 1, q);
+        static_for<16>([&](auto c) { write_chunk(lds, 0, c); });
+        lds_barrier();
+        read_frags(lds, 0, 0);
+        SCHED_FENCE();
+
+        // par = kt & 1, a compile-time value so that the register sets are
+        // named statically (a runtime index would put them in scratch memory)
+        auto step = [&](int kt, auto par_c, auto first_c) {
+            constexpr int par = decltype(par_c)::value;
+            constexpr bool first = decltype(first_c)::value;
+            uint8_t *cur = lds + par * STAGE_BYTES;
+            uint8_t *nxt = lds + (par ^ 1) * STAGE_BYTES;
+            constexpr int set_next = par ^ 1;   // holds step kt + 1
+            constexpr int set_free = par;       // held step kt, already written
+            // sub-steps 0..2: fragments of sub-step kk + 1 read during sub-step kk
+            static_for<48>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                constexpr int kk = t >> 4;
+                mma(kk & 1, t & 15, first && kk == 0);
+                if constexpr ((t & 15) % 2 == 0)
+                    read_frag(cur, kk + 1, (kk + 1) & 1, (t & 15) / 2);
+                if constexpr (t % CHUNK_EVERY == 1 && t / CHUNK_EVERY < 16)
+                    write_chunk(nxt, set_next, Int<t / CHUNK_EVERY>{});
+                if constexpr (t >= LOAD_AT && (t - LOAD_AT) % 4 == 0 && (t - LOAD_AT) / 4 < 6)
+                    load(kt + 2, set_free, (t - LOAD_AT) / 4);
+                SCHED_VALU_ONLY();
+            });
+            // the next stage is written by every wave, the current one fully read
+            lds_barrier();
+            SCHED_FENCE();
+            // sub-step 3 on fragments set 1, first fragments of the next stage
+            static_for<16>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
+                mma(1, t, false);
+                if constexpr (t % 2 == 0)
+                    read_frag(nxt, 0, 0, t / 2);
+                SCHED_VALU_ONLY();
+            });
+        };
+
+        if (nk == 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = Staging::mma(fb[j], fa[i], acc[i][j]);
-        };
-
-        Staging st;
-        st.init(p, tm, tn, tid);
-        frag fa0[4], fb0[4], fa1[4], fb1[4];
-        st.load(0);
-        lds_barrier();            // every wave is done with the previous tile's stages
-        st.commit(lds);
-        st.load(BK);
-        lds_barrier();
-        read_frags(lds, 0, fa0, fb0);
-
-        // Software pipeline over K steps. Step kt computes on LDS stage kt & 1
-        // in four sub-steps of 16; each sub-step's fragments were read from LDS
-        // during the previous sub-step's matrix instructions. Along the way the
-        // step writes the registers holding slice kt + 1 into the other stage,
-        // requests slice kt + 2 from memory, and -- after the step's single
-        // barrier -- reads the first fragments of the other stage. The body has
-        // no branches, so the compiler can interleave all of it with the matrix
-        // instructions; slices at or past K load as zeros and are never used.
-        for (int kt = 0; kt < nk; ++kt) {
-            const uint8_t *cur = lds + (kt & 1) * STAGE_BYTES;
-            uint8_t *nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
-
-            read_frags(cur, 1, fa1, fb1);
-            mma_all(fa0, fb0);
-            schedule_reads_with_mma();
-            SCHED_FENCE();
-
-            read_frags(cur, 2, fa0, fb0);
-            st.commit(nxt);
-            mma_all(fa1, fb1);
-            Staging::schedule_commit();
-            SCHED_FENCE();
-
-            read_frags(cur, 3, fa1, fb1);
-            st.load((kt + 2) * BK);
-            mma_all(fa0, fb0);
-            Staging::schedule_load();
-            SCHED_FENCE();
-
-            // every wave is done reading stage `nxt` (last step) and writing it (this step)
-            lds_barrier();
-            SCHED_FENCE();
-            read_frags(nxt, 0, fa0, fb0);
-            mma_all(fa1, fb1);
-            schedule_reads_with_mma();
-            SCHED_FENCE();
+                    acc[i][j] = f32x16{};
+        } else {
+            step(0, Int<0>{}, Int<1>{});
+            int kt = 1;
+            for (; kt + 1 < nk; kt += 2) {
+                step(kt, Int<1>{}, Int<0>{});
+                step(kt + 1, Int<0>{}, Int<0>{});
+            }
+            if (kt < nk)
+                step(kt, Int<1>{}, Int<0>{});
         }
 
         store_tile(acc, rc, p.M, p.N, tm * BM + wm * 128, tn * BN + wn * 128, l32, half);
