@@ -52,10 +52,11 @@ KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel", "fp4": "gemm355::fp
                "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel"}
 
 
-def kernel_for(kind: str, M: int, N: int) -> str:
+def kernel_for(kind: str, M: int, N: int, K: int) -> str:
     """The kernel gemm_bf16_nt / gemm_nvfp4_nt launches for this shape (the
-    library's rule: fewer than 128 tiles of 256 x 256 -> 64 x 64 tiles)."""
-    if kind == "bf16" and (-(-M // 256)) * (-(-N // 256)) < 128:
+    library's rule: fewer than 128 tiles of 256 x 256, or K <= 128 -> 64 x 64
+    tiles)."""
+    if kind == "bf16" and ((-(-M // 256)) * (-(-N // 256)) < 128 or K <= 128):
         return KERNEL_NAME["bf16_small"]
     return KERNEL_NAME[kind]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -254,7 +255,7 @@ def main(argv=None):
         gbs = alg_bytes / (ms_step * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    roofline.update({"kernel": kernel_for(kind, M, N), "traffic": traffic, "algorithmic_bytes": alg_bytes,
+    roofline.update({"kernel": kernel_for(kind, M, N, K), "traffic": traffic, "algorithmic_bytes": alg_bytes,
                      "mean_launch_ms": round(ms_step, 5)})
     out = {
         "metric": "TFLOP/s for BF16 C=A·B^T at M=N=K=8192; % of MI355X dense BF16 peak"

@@ -50,9 +50,13 @@ constexpr int SLOTS = 5;
 constexpr int LDS_BYTES = SLOTS * UNIT_BYTES;
 constexpr int UNIT_COPIES = 8;               // 1 KiB copies per wave per unit (64 rows)
 constexpr int WINDOW_COPIES = 2 * UNIT_COPIES;
+constexpr int EPILOGUE_STORES = 32;          // 16-byte stores per wave per tile
 
 static_assert(LDS_BYTES <= 163840, "LDS ring exceeds the 160 KiB of a gfx950 workgroup");
 static_assert(BM == 256 && BN == 256 && THREADS == 256, "the copy map assumes 256 x 256 tiles and 4 waves");
+// Most vector memory operations a wave has in flight: after a tile change
+// the 32 epilogue stores and the copies of A2, B2 and A3 of the new tile.
+static_assert(3 * UNIT_COPIES + EPILOGUE_STORES <= 63, "vmcnt counts at most 63 outstanding operations");
 
 // Instruction positions inside a half-step of 64 matrix instructions.
 // Fragment read r (0..15) follows matrix instruction read_at(r): all reads are
@@ -63,6 +67,10 @@ constexpr int read_at(int r) { return 3 * r + 1; }
 // window, 64..127 the first half of the next step. One copy every eight
 // matrix instructions keeps the copy pipeline at about half load throughout.
 constexpr int copy_at(int c) { return c < UNIT_COPIES ? 8 * c + 1 : 68 + 8 * (c - UNIT_COPIES); }
+// In the last step of a tile the B copies (the next tile's B1) come one every
+// four matrix instructions, so that they have landed by the epilogue, which
+// waits for every copy before its stores.
+constexpr int copy_at_last(int c) { return 4 * c + 1; }
 // Fragment read order: A0, B0..B7, A1..A7, so the first matrix instructions of
 // a half-step (A block 0 against every B block) wait for two reads only.
 constexpr int read_block(int r) { return r == 0 ? 0 : r <= 8 ? 8 + (r - 1) : r - 8; }
@@ -102,6 +110,15 @@ __device__ inline void wait_copies_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"
 __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 
+// Lane index recomputed where it is used (volatile, so it is not hoisted
+// into a register that would have to live through the whole tile loop).
+__device__ inline int fresh_lane_id()
+{
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_kernel(Problem p)
 {
@@ -129,196 +146,240 @@ void gemm_bf16_nt_kernel(Problem p)
     const i32x4 ra = rsrc_words(p.a, (unsigned)p.M * (unsigned)K * 2u);
     const i32x4 rb = rsrc_words(p.b, (unsigned)p.N * (unsigned)K * 2u);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (K + BK - 1) / BK;   // >= 3: smaller K goes to the 64 x 64 instance
 
-    for (int round = 0;; ++round) {
-        const int pos = schedule_position(blockIdx.x, round, p.grid);
+    int round = 0;
+    int tm, tn;
+    {
+        const int pos = schedule_position(blockIdx.x, 0, p.grid);
         if (pos >= p.tiles)
-            break;
-        int tm, tn;
+            return;
         supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
-
-        // Copies: wave w fills blocks 8 w .. 8 w + 7 (rows 64 w .. 64 w + 63) of
-        // every unit; lane i fills position i & 7 of row 8 b + i / 8. Per block:
-        // byte offset of this lane's chunk in its A row and B row, and the
-        // chunk's first K index (the K tail switches whole chunks off).
-        int a_off[UNIT_COPIES], b_off[UNIT_COPIES], chunk_k[UNIT_COPIES];
-#pragma unroll
-        for (int j = 0; j < UNIT_COPIES; ++j) {
-            const int row = 8 * (UNIT_COPIES * wave + j) + copy_row;
-            const int c = swizzle(row, lane & 7);   // logical chunk stored at position lane & 7
-            chunk_k[j] = 8 * c;
-            a_off[j] = ((tm * BM + row) * K + 8 * c) * 2;
-            b_off[j] = ((tn * BN + row) * K + 8 * c) * 2;
-        }
-        // Per-step bases, hidden from the optimiser again at every step so
-        // that addresses are formed where they are used instead of being
-        // hoisted out of the loop into registers (which would spill).
-        unsigned copy_base = lds_base + (unsigned)(UNIT_COPIES * wave * 1024);
-        int a_ofs[2] = {a_frag + kofs0, a_frag + kofs1};
-        int b_ofs[2] = {b_frag + kofs0, b_frag + kofs1};
-
-        // Copy j of unit 2 s + op. Steps at or past the end of K, and the K
-        // tail, read as zeros; rows past M or N fall outside the buffer and do
-        // too.
-        auto copy = [&](int s, int op, int j, int slot) {
-            const int k0 = s * BK;
-            const bool valid = s < nk && k0 + chunk_k[j] < K;
-            const unsigned dst = copy_base + (unsigned)(slot + j * 1024);
-            copy_1k(op ? rb : ra, dst, valid ? (op ? b_off[j] : a_off[j]) + k0 * 2 : OOB);
-        };
-        // ring[x]: LDS offset of the slot of unit 2 s + x during step s (x =
-        // 0..4). The next step sees the same slots rotated by two units, so the
-        // offsets are carried in scalar registers and renamed, never computed.
-        int ring[SLOTS];
-#pragma unroll
-        for (int x = 0; x < SLOTS; ++x)
-            ring[x] = x * UNIT_BYTES;
-        // Copy c of the window opened by the barrier of step s - d, issued
-        // during step s (d = 0: second half-step, d = 1: first half-step).
-        auto window_copy = [&](int s, int d, int c) {
-            if (c < UNIT_COPIES)
-                copy(s - d + 2, 1, c, ring[(5 - 2 * d) % SLOTS]);   // unit 2 s + 5 - 2 d
-            else
-                copy(s - d + 3, 0, c - UNIT_COPIES, ring[(6 - 2 * d) % SLOTS]);
-        };
-
-        f32x4 acc[8][8];
-        bf16x8 fa[2][8], fb[2][8];
-        // Read r of half-step h of step s into fragment set h.
-        // Read r of half-step h of the step whose units sit in slots sa, sb.
-        auto read = [&](int sa, int sb, int h, int r) {
-            const int q = read_block(r);
-            if (q < 8)
-                fa[h][q] = *reinterpret_cast<const bf16x8 *>(lds + (a_ofs[h] + sa) + q * 16 * ROW_BYTES);
-            else
-                fb[h][q - 8] = *reinterpret_cast<const bf16x8 *>(lds + (b_ofs[h] + sb) + (q - 8) * 16 * ROW_BYTES);
-        };
-        // Matrix instruction t of a half-step: block (t / 8, t % 8). B rows are
-        // the first operand and A rows the second, so each 16 x 16 result
-        // arrives transposed (one C row per lane, four adjacent columns).
-        auto mma = [&](int h, int t, bool first) {
-            const int i = t >> 3, j = t & 7;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], first ? f32x4{} : acc[i][j], 0, 0, 0);
-        };
-
-        // Copies of the previous tile (including its zero units past K), its
-        // reads and its stores are done before the ring is refilled.
-        wait_reads();
-        wait_all_copies();
-        lds_barrier();
-        // units A0, B0, A1, B1, A2 fill the ring
-#pragma unroll
-        for (int u = 0; u < SLOTS; ++u)
-#pragma unroll
-            for (int j = 0; j < UNIT_COPIES; ++j)
-                copy(u >> 1, u & 1, j, u * UNIT_BYTES);
-        wait_copies_le<3 * UNIT_COPIES>();   // A0 and B0 have landed
-        lds_barrier();
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            read(ring[0], ring[1], 0, r);
-        SCHED_FENCE();
-
-        // Step s. The order of matrix instructions, LDS reads, copies and
-        // scalar instructions inside each half-step is fixed by hand (a
-        // scheduling barrier after every matrix instruction and what follows
-        // it); only plain vector ALU work (address arithmetic) may move across
-        // those barriers, so its dependency chains spread over several matrix
-        // instructions instead of stalling the issue of the next one.
-        auto step = [&](int s, auto first_c) {
-            constexpr bool first = decltype(first_c)::value;
-            asm volatile("" : "+v"(a_ofs[0]), "+v"(a_ofs[1]), "+v"(b_ofs[0]), "+v"(b_ofs[1]), "+s"(copy_base));
-            // first half-step: fragments 0; read the second half of step s;
-            // finish the window of step s - 1 (the prologue filled step 0's)
-            static_for<64>([&](auto tc) {
-                constexpr int t = decltype(tc)::value;
-                mma(0, t, first);
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (t == read_at(r))
-                        read(ring[0], ring[1], 1, r);
-                if (!first) {
-#pragma unroll
-                    for (int c = 0; c < WINDOW_COPIES; ++c)
-                        if (64 + t == copy_at(c))
-                            window_copy(s, 1, c);
-                }
-                SCHED_VALU_ONLY();
-            });
-            // step s is fully read by this wave and its copies of step s + 1
-            // (the B tile of step s + 1 and everything issued before it) have
-            // landed; only the A tile of step s + 2 may still be in flight
-            wait_reads();
-            wait_copies_le<UNIT_COPIES>();
-            lds_barrier();
-            SCHED_FENCE();
-            // second half-step: fragments 1; read the first half of step s + 1;
-            // open the window of step s
-            static_for<64>([&](auto tc) {
-                constexpr int t = decltype(tc)::value;
-                mma(1, t, false);
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (t == read_at(r))
-                        read(ring[2], ring[3], 0, r);
-#pragma unroll
-                for (int c = 0; c < WINDOW_COPIES; ++c)
-                    if (t == copy_at(c))
-                        window_copy(s, 0, c);
-                SCHED_VALU_ONLY();
-            });
-        };
-
-        if (nk == 0) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = f32x4{};
-        } else {
-            auto rotate = [&]() {
-                const int r0 = ring[0], r1 = ring[1];
-                ring[0] = ring[2];
-                ring[1] = ring[3];
-                ring[2] = ring[4];
-                ring[3] = r0;
-                ring[4] = r1;
-            };
-            step(0, Int<1>{});
-            rotate();
-            for (int s = 1; s < nk; ++s) {
-                step(s, Int<0>{});
-                rotate();
-            }
-        }
-
-        // Epilogue. Lane (l16, grp) of block (i, j) holds C[m][n .. n + 3] with
-        // m = m0 + 16 i + l16 and n = n0 + 16 j + 4 grp. For a pair of blocks
-        // (x = block 2 jp, y = block 2 jp + 1) v_permlane16_swap exchanges
-        // lane groups so that group 0 holds columns 0..7 of x, group 1 columns
-        // 0..7 of y, group 2 columns 8..15 of x and group 3 columns 8..15 of
-        // y: one 16-byte store per lane, 64 contiguous bytes per C row.
-        const int m = tm * BM + wm * 128 + l16;
-        const int n0 = tn * BN + wn * 128 + 16 * (grp & 1) + 8 * (grp >> 1);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-#pragma unroll
-            for (int jp = 0; jp < 4; ++jp) {
-                const f32x4 &x = acc[i][2 * jp];
-                const f32x4 &y = acc[i][2 * jp + 1];
-                const unsigned x0 = pack_bf16(x[0], x[1]), x1 = pack_bf16(x[2], x[3]);
-                const unsigned y0 = pack_bf16(y[0], y[1]), y1 = pack_bf16(y[2], y[3]);
-                const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
-                const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
-                const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
-                const int mm = m + 16 * i;
-                const int n = n0 + 32 * jp;
-                const int off = (mm < p.M && n < p.N) ? (mm * p.N + n) * 2 : OOB;
-                __builtin_amdgcn_raw_buffer_store_b128(out, rc, off, 0, 0);
-            }
-        }
     }
+
+    f32x4 acc[8][8];
+    // Epilogue of one pair of blocks. Lane (l16, grp) of block (i, j) holds
+    // C[m][n .. n + 3] with m = m0 + 16 i + l16 and n = n0 + 16 j + 4 grp. For
+    // x = block (i, 2 jp) and y = block (i, 2 jp + 1), v_permlane16_swap
+    // exchanges lane groups so that group 0 holds columns 0..7 of x, group 1
+    // columns 0..7 of y, group 2 columns 8..15 of x and group 3 columns 8..15
+    // of y: one 16-byte store per lane, 64 contiguous bytes per C row.
+    auto store_pair = [&](int ctm, int ctn, int i, int jp, int ln) {
+        const int l16 = ln & 15, grp = ln >> 4;
+        const f32x4 &x = acc[i][2 * jp];
+        const f32x4 &y = acc[i][2 * jp + 1];
+        const unsigned x0 = pack_bf16(x[0], x[1]), x1 = pack_bf16(x[2], x[3]);
+        const unsigned y0 = pack_bf16(y[0], y[1]), y1 = pack_bf16(y[2], y[3]);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
+        const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+        const int mm = ctm * BM + wm * 128 + l16 + 16 * i;
+        const int n = ctn * BN + wn * 128 + 16 * (grp & 1) + 8 * (grp >> 1) + 32 * jp;
+        const int off = (mm < p.M && n < p.N) ? (mm * p.N + n) * 2 : OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(out, rc, off, 0, 0);
+    };
+
+    // The workgroup's tiles run as one continuous sequence of steps: the ring,
+    // the copy windows and the fragment reads carry on across tile
+    // boundaries, so the copies of a tile's first units are issued during the
+    // previous tile's last steps, and the previous tile's accumulators are
+    // converted and stored while the first half-step of the next tile
+    // overwrites them block by block (its matrix instructions start from 0).
+
+    // Copies: wave w fills blocks 8 w .. 8 w + 7 (rows 64 w .. 64 w + 63) of
+    // every unit; lane i fills position i & 7 of row 8 b + i / 8. The
+    // logical chunk a lane fetches depends only on the parity of the block
+    // (row / 2 & 7 = 4 (b & 1) + lane / 16), so per parity q: byte offset of
+    // this lane's chunk in its A row and B row of block q for the current
+    // tile (block j adds j / 2 * 16 rows), and the chunk's first K index (the
+    // K tail switches whole chunks off).
+    int a_off[2], b_off[2], chunk_k[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = 8 * (UNIT_COPIES * wave + q) + copy_row;
+        const int c = swizzle(row, lane & 7);   // logical chunk stored at position lane & 7
+        chunk_k[q] = 8 * c;
+        a_off[q] = ((tm * BM + row) * K + 8 * c) * 2;
+        b_off[q] = ((tn * BN + row) * K + 8 * c) * 2;
+    }
+    const int block_pair_bytes = 16 * K * 2;   // 16 rows
+    // The next tile of this workgroup, as byte deltas of its operand rows.
+    bool has_next = false;
+    int ntm = 0, ntn = 0, da = 0, db = 0;
+    auto find_next = [&]() {
+        const int pos = schedule_position(blockIdx.x, round + 1, p.grid);
+        has_next = pos < p.tiles;
+        if (has_next) {
+            supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, ntm, ntn);
+            da = (ntm - tm) * BM * K * 2;
+            db = (ntn - tn) * BN * K * 2;
+        }
+    };
+    find_next();
+
+    // Per-step bases, hidden from the optimiser again at every step so that
+    // addresses are formed where they are used instead of being hoisted out
+    // of the loop into registers (which would spill).
+    unsigned copy_base = lds_base + (unsigned)(UNIT_COPIES * wave * 1024);
+    int a_ofs[2] = {a_frag + kofs0, a_frag + kofs1};
+    int b_ofs[2] = {b_frag + kofs0, b_frag + kofs1};
+
+    // Copy j of unit 2 S + op, S counted from the current tile's first step:
+    // S >= nk belongs to the next tile (its step S - nk). Steps past the last
+    // tile or past K, and the K tail, read as zeros; rows past M or N fall
+    // outside the buffer and do too.
+    auto copy = [&](int S, int op, int j, int slot) {
+        const bool cur = S < nk;
+        const int ks = cur ? S : S - nk;
+        const bool tile_ok = cur || (has_next && ks < nk);
+        const int add = (cur ? 0 : (op ? db : da)) + ks * BK * 2 + (j >> 1) * block_pair_bytes;
+        const bool valid = tile_ok && ks * BK + chunk_k[j & 1] < K;
+        const unsigned dst = __builtin_amdgcn_readfirstlane(copy_base + (unsigned)(slot + j * 1024));
+        copy_1k(op ? rb : ra, dst, valid ? (op ? b_off[j & 1] : a_off[j & 1]) + add : OOB);
+    };
+    // ring[x]: LDS offset of the slot of unit 2 s + x during step s (x =
+    // 0..4). The next step sees the same slots rotated by two units, so the
+    // offsets are carried in scalar registers and renamed, never computed.
+    int ring[SLOTS];
+#pragma unroll
+    for (int x = 0; x < SLOTS; ++x)
+        ring[x] = x * UNIT_BYTES;
+    auto rotate = [&]() {
+        const int r0 = ring[0], r1 = ring[1];
+        ring[0] = ring[2];
+        ring[1] = ring[3];
+        ring[2] = ring[4];
+        ring[3] = r0;
+        ring[4] = r1;
+    };
+    // Copy c of the window opened by the barrier of step s - d, issued
+    // during step s (d = 0: second half-step, d = 1: first half-step).
+    auto window_copy = [&](int s, int d, int c) {
+        if (c < UNIT_COPIES)
+            copy(s - d + 2, 1, c, ring[(5 - 2 * d) % SLOTS]);   // unit 2 s + 5 - 2 d
+        else
+            copy(s - d + 3, 0, c - UNIT_COPIES, ring[(6 - 2 * d) % SLOTS]);
+    };
+
+    bf16x8 fa[2][8], fb[2][8];
+    // Read r of half-step h of the step whose units sit in slots sa, sb.
+    auto read = [&](int sa, int sb, int h, int r) {
+        const int q = read_block(r);
+        if (q < 8)
+            fa[h][q] = *reinterpret_cast<const bf16x8 *>(lds + (a_ofs[h] + sa) + q * 16 * ROW_BYTES);
+        else
+            fb[h][q - 8] = *reinterpret_cast<const bf16x8 *>(lds + (b_ofs[h] + sb) + (q - 8) * 16 * ROW_BYTES);
+    };
+    // Matrix instruction t of a half-step: block (t / 8, t % 8). B rows are
+    // the first operand and A rows the second, so each 16 x 16 result arrives
+    // transposed (one C row per lane, four adjacent columns).
+    auto mma = [&](int h, int t, bool first) {
+        const int i = t >> 3, j = t & 7;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], first ? f32x4{} : acc[i][j], 0, 0, 0);
+    };
+
+    // Prologue of the workgroup's first tile: units A0, B0, A1, B1 (A2 comes
+    // with the first step's window, as for every later tile). All four have
+    // landed before the first barrier, as the epilogue of every later tile
+    // waits for the next tile's first two steps.
+#pragma unroll
+    for (int u = 0; u < SLOTS - 1; ++u)
+#pragma unroll
+        for (int j = 0; j < UNIT_COPIES; ++j)
+            copy(u >> 1, u & 1, j, u * UNIT_BYTES);
+    wait_all_copies();
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        read(ring[0], ring[1], 0, r);
+    SCHED_FENCE();
+
+    // Step s of the current tile. KIND 0: a middle step; 1: the last step
+    // (the next tile's B1 is copied early in its second half); 2: the first
+    // step, whose matrix instructions start from 0 and whose barrier needs no
+    // wait: the copies of steps 0 and 1 had all landed before the previous
+    // tile's epilogue stores (or before the prologue's barrier). Only the
+    // copies' order among themselves is relied on, never their order
+    // relative to stores.
+    // The order of matrix instructions, LDS reads, copies, stores and scalar
+    // instructions inside each half-step is fixed by hand (a scheduling
+    // barrier after every matrix instruction and what follows it); only plain
+    // vector ALU work may move across those barriers, so its dependency
+    // chains spread over several matrix instructions instead of stalling the
+    // issue of the next one.
+
+    auto step = [&](int s, auto kind_c) {
+        constexpr int kind = decltype(kind_c)::value;
+        asm volatile("" : "+v"(a_ofs[0]), "+v"(a_ofs[1]), "+v"(b_ofs[0]), "+v"(b_ofs[1]), "+s"(copy_base));
+        // first half-step: fragments 0; read the second half of step s;
+        // finish the window of step s - 1
+        static_for<64>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            mma(0, t, kind == 2);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (t == read_at(r))
+                    read(ring[0], ring[1], 1, r);
+#pragma unroll
+            for (int c = 0; c < WINDOW_COPIES; ++c)
+                if (64 + t == copy_at(c))
+                    window_copy(s, 1, c);
+            SCHED_VALU_ONLY();
+        });
+        // step s is fully read by this wave and its copies of step s + 1
+        // have landed; only the A tile of step s + 2 (and, after a tile
+        // change, the previous tile's stores) may still be in flight
+        wait_reads();
+        if constexpr (kind != 2)
+            wait_copies_le<UNIT_COPIES>();
+        lds_barrier();
+        SCHED_FENCE();
+        // second half-step: fragments 1; read the first half of step s + 1
+        // (the next tile's first step after a tile's last); open the window
+        // of step s
+        static_for<64>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            mma(1, t, false);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (t == read_at(r))
+                    read(ring[2], ring[3], 0, r);
+#pragma unroll
+            for (int c = 0; c < WINDOW_COPIES; ++c)
+                if (t == (kind == 1 && c < UNIT_COPIES ? copy_at_last(c) : copy_at(c)))
+                    window_copy(s, 0, c);
+            SCHED_VALU_ONLY();
+        });
+        rotate();
+    };
+
+    for (;;) {
+        step(0, Int<2>{});
+        for (int s = 1; s < nk - 1; ++s)
+            step(s, Int<0>{});
+        step(nk - 1, Int<1>{});
+        // epilogue; the next tile's first two steps are in LDS or landing
+        wait_all_copies();
+        const int ln = fresh_lane_id();
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int jp = 0; jp < 4; ++jp)
+                store_pair(tm, tn, i, jp, ln);
+        if (!has_next)
+            break;
+        // switch to the next tile
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            a_off[q] += da;
+            b_off[q] += db;
+        }
+        tm = ntm;
+        tn = ntn;
+        ++round;
+        find_next();
+    }
+
     wait_reads();
     wait_all_copies(); // no copy may still be writing LDS when the workgroup ends
 }

@@ -11,7 +11,7 @@ import dense_gemm_14_amd as g
 import oracle
 import synthetic as syn
 from tests import tolerance
-from tests.gpu_util import GuardedC, need_gpu, to_dev
+from tests.gpu_util import GuardedC, need_gpu, sample_positions, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +84,45 @@ def test_instances_agree_within_bound_at_a_medium_shape():
             assert res, (inst, res)
     finally:
         g.force_instance(g.INSTANCE_AUTO)
+
+
+# Shapes with more 256 x 256 tiles than workgroups, so workgroups run several
+# tiles back to back (the next tile's first units are copied during the
+# previous tile's last steps): ragged M and N, K tails, K just above the
+# 128 that the 256 x 256 instance needs.
+MULTI_TILE = [(4352, 4104, 520), (4400, 4400, 136), (4360, 4352, 1000)]
+
+
+@pytest.mark.parametrize("M,N,K", MULTI_TILE)
+def test_large_instance_multi_tile_sampled(M, N, K):
+    need_gpu()
+    A = syn.bf16_uniform(M, K, seed=M + 2 * K)
+    B = syn.bf16_uniform(N, K, seed=N + 2 * K + 1)
+    try:
+        g.force_instance(g.INSTANCE_LARGE)
+        C = run_bf16(A, B, M, N, K)
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+    ms, ns = sample_positions(M, N, 3000, seed=M + N + K)
+    res = tolerance.check(C[ms, ns], oracle.gemm_bf16_nt_at(A, B, ms, ns), K)
+    assert res, res
+
+
+def test_large_instance_multi_tile_exact_every_element():
+    # Multiples of 1/16: every partial sum is exact in FP32, so the answer is
+    # unique; the exact sums are formed in float64 and rounded once by the
+    # oracle's BF16 rounding, and the oracle itself is compared on a sample.
+    need_gpu()
+    M, N, K = 4352, 4104, 1032
+    A = syn.bf16_sixteenths(M, K, seed=61)
+    B = syn.bf16_sixteenths(N, K, seed=62)
+    try:
+        g.force_instance(g.INSTANCE_LARGE)
+        C = run_bf16(A, B, M, N, K)
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+    want = oracle.bf16_from_double(tolerance.bf16_bits_to_f64(A) @ tolerance.bf16_bits_to_f64(B).T)
+    ms, ns = sample_positions(M, N, 300, seed=9)
+    assert np.array_equal(oracle.gemm_bf16_nt_at(A, B, ms, ns), want[ms, ns])
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
