@@ -92,10 +92,11 @@ __device__ inline i32x4 rsrc_words(const void *p, unsigned bytes)
 // compiler does not treat the in-flight LDS write as aliasing every later LDS
 // read (it would wait for all copies before each read); the kernel orders the
 // copies itself with explicit vmcnt waits and barriers. m0 holds the LDS base;
-// nothing else in this kernel uses m0.
+// nothing else in this kernel uses m0. On gfx9 an LDS-DMA instruction must not
+// directly follow a scalar write of m0 (one wait state), hence the s_nop.
 __device__ inline void copy_1k(const i32x4 &rsrc, unsigned lds_addr, int voff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(lds_addr), "v"(voff), "s"(rsrc)
                  : "memory", "m0");

@@ -68,7 +68,9 @@ constexpr int SHIFT = 3072;
 constexpr unsigned OOB_SHIFTED = 0xFFFF0000u;
 
 // Set the LDS base of the following copies.
-__device__ inline void set_m0(unsigned lds_addr) { asm volatile("s_mov_b32 m0, %0" ::"s"(lds_addr) : "memory", "m0"); }
+// The s_nop: on gfx9 an LDS-DMA instruction must not directly follow a scalar
+// write of m0 (one wait state).
+__device__ inline void set_m0(unsigned lds_addr) { asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" ::"s"(lds_addr) : "memory", "m0"); }
 
 // One 1 KiB global -> LDS copy: lane i's 16 bytes at buffer offset voff + IMM
 // land at LDS byte m0 + IMM + 16 i (inline assembly for the same reason as in
