@@ -54,9 +54,9 @@ KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel", "fp4": "gemm355::fp
 
 def kernel_for(kind: str, M: int, N: int, K: int) -> str:
     """The kernel gemm_bf16_nt / gemm_nvfp4_nt launches for this shape (the
-    library's rule: fewer than 128 tiles of 256 x 256, or K <= 128 -> 64 x 64
+    library's rule: fewer than 128 tiles of 256 x 256, or K <= 192 -> 64 x 64
     tiles)."""
-    if kind == "bf16" and ((-(-M // 256)) * (-(-N // 256)) < 128 or K <= 128):
+    if kind == "bf16" and ((-(-M // 256)) * (-(-N // 256)) < 128 or K <= 192):
         return KERNEL_NAME["bf16_small"]
     return KERNEL_NAME[kind]
 PROFILE_DIR = os.path.join(ROOT, "profiles")

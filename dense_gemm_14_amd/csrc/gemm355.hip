@@ -117,8 +117,8 @@ extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, v
     int instance = g_bf16_instance.load(std::memory_order_relaxed);
     if (instance == 0)
         instance = ceil_div(M, BM) * ceil_div(N, BN) < kSmallTileThreshold ? 2 : 1;
-    if (K <= 2 * gemm355::bf16::BK)
-        instance = 2;   // the 256 x 256 kernel runs its tiles back to back and needs K > 128
+    if (K <= 3 * gemm355::bf16::BK)
+        instance = 2;   // the 256 x 256 kernel runs its tiles back to back and needs K > 192
     if (instance == 2)
         return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel, p, stream, gemm355::bf16_small::TM,
                       gemm355::bf16_small::TN);

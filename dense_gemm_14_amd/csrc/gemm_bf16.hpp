@@ -49,7 +49,6 @@ constexpr int UNIT_BYTES = BM * ROW_BYTES;   // one operand tile of one step: 32
 constexpr int SLOTS = 5;
 constexpr int LDS_BYTES = SLOTS * UNIT_BYTES;
 constexpr int UNIT_COPIES = 8;               // 1 KiB copies per wave per unit (64 rows)
-constexpr int WINDOW_COPIES = 2 * UNIT_COPIES;
 constexpr int EPILOGUE_STORES = 32;          // 16-byte stores per wave per tile
 
 static_assert(LDS_BYTES <= 163840, "LDS ring exceeds the 160 KiB of a gfx950 workgroup");
@@ -62,18 +61,31 @@ static_assert(3 * UNIT_COPIES + EPILOGUE_STORES <= 63, "vmcnt counts at most 63 
 // Fragment read r (0..15) follows matrix instruction read_at(r): all reads are
 // issued in the first three quarters so they have landed by the half-step's end.
 constexpr int read_at(int r) { return 3 * r + 1; }
-// Copy c of a window (0..7: B tile, 8..15: A tile) at window position
-// copy_at(c): positions 0..63 are the second half of the step that opened the
-// window, 64..127 the first half of the next step. One copy every eight
-// matrix instructions keeps the copy pipeline at about half load throughout.
-constexpr int copy_at(int c) { return c < UNIT_COPIES ? 8 * c + 1 : 68 + 8 * (c - UNIT_COPIES); }
-// In the last step of a tile the B copies (the next tile's B1) come one every
-// four matrix instructions, so that they have landed by the epilogue, which
-// waits for every copy before its stores.
-constexpr int copy_at_last(int c) { return 4 * c + 1; }
+// The copies of a unit go out in four pairs (blocks 2 p and 2 p + 1 of the
+// wave's eight), one pair every sixteen matrix instructions: A pairs in the
+// first half-step, B pairs in the second. In the last step of a tile the B
+// pairs (the next tile's B1) come one every four matrix instructions, so that
+// they have landed by the epilogue, which waits for every copy.
+constexpr int a_pair_at(int p) { return 16 * p + 4; }
+constexpr int b_pair_at(int p, bool last) { return last ? 4 * p + 1 : 16 * p + 1; }
 // Fragment read order: A0, B0..B7, A1..A7, so the first matrix instructions of
 // a half-step (A block 0 against every B block) wait for two reads only.
 constexpr int read_block(int r) { return r == 0 ? 0 : r <= 8 ? 8 + (r - 1) : r - 8; }
+
+// Buffer resources for the copies start SHIFT bytes before their operand (and
+// span SHIFT bytes more): block j of a pair is addressed with instruction
+// offset 1024 (j % 4), which moves the LDS destination and the global address
+// alike, and the per-lane offset (global offset + SHIFT - 1024 (j % 4)) stays
+// non-negative. OOB_OFF is beyond every range even after the scalar step
+// offset and the instruction offset are added (operand extents are < 2^31).
+constexpr int SHIFT = 3072;
+constexpr int OOB_OFF = (int)0x80000000;
+
+// Step kinds of a tile (at least four steps; smaller K goes to the 64 x 64
+// instance): FIRST (step 0, matrix instructions start from zero), MID (1 ..
+// nk - 4), TAIL (nk - 3: copies step nk - 1, the only one with a K tail),
+// NEXT0 and NEXT1 (nk - 2, nk - 1: copy the next tile's steps 0 and 1).
+enum StepKind : int { FIRST, MID, TAIL, NEXT0, NEXT1 };
 
 __device__ inline int swizzle(int r, int c) { return c ^ ((r >> 1) & 7); }
 
@@ -87,18 +99,23 @@ __device__ inline i32x4 rsrc_words(const void *p, unsigned bytes)
     return i32x4{(int)(unsigned)a, (int)(unsigned)(a >> 32), (int)bytes, (int)RSRC_WORD3};
 }
 
-// One 1 KiB global -> LDS copy: lane i's 16 bytes at byte offset `voff` of the
-// buffer land at LDS byte lds_addr + 16 i. Written as inline assembly so the
-// compiler does not treat the in-flight LDS write as aliasing every later LDS
-// read (it would wait for all copies before each read); the kernel orders the
-// copies itself with explicit vmcnt waits and barriers. m0 holds the LDS base;
-// nothing else in this kernel uses m0. On gfx9 an LDS-DMA instruction must not
-// directly follow a scalar write of m0 (one wait state), hence the s_nop.
-__device__ inline void copy_1k(const i32x4 &rsrc, unsigned lds_addr, int voff)
+// Two 1 KiB global -> LDS copies: lane i's 16 bytes at buffer offset
+// v + soff + O land at LDS byte lds_addr + O + 16 i (v = v0, O = O0 and v =
+// v1, O = O1). Written as inline assembly so the compiler does not treat the
+// in-flight LDS writes as aliasing every later LDS read (it would wait for all
+// copies before each read); the kernel orders the copies itself with explicit
+// vmcnt waits and barriers. m0 holds the LDS base; nothing else in this kernel
+// uses m0. On gfx9 an LDS-DMA instruction must not directly follow a scalar
+// write of m0 (one wait state), hence the s_nop.
+template <int O0, int O1>
+__device__ inline void copy_pair(const i32x4 &rsrc, unsigned lds_addr, int v0, int v1, int soff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    static_assert(O0 >= 0 && O1 >= 0 && O0 <= SHIFT && O1 <= SHIFT, "instruction offsets must stay within SHIFT");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %3, %4 offen offset:%5 lds\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen offset:%6 lds"
                  :
-                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "s"(lds_addr), "v"(v0), "v"(v1), "s"(rsrc), "s"(soff), "n"(O0), "n"(O1)
                  : "memory", "m0");
 }
 
@@ -109,6 +126,9 @@ template <int N>
 __device__ inline void wait_copies_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 // Every LDS read this wave issued has returned.
 __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// The same as an instruction the compiler knows about, so that it drops its
+// own waits for the fragments read before it.
+__device__ inline void wait_reads_known() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
 
 
 // Lane index recomputed where it is used (volatile, so it is not hoisted
@@ -144,10 +164,10 @@ void gemm_bf16_nt_kernel(Problem p)
     const int copy_row = lane >> 3;
 
     const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
-    const i32x4 ra = rsrc_words(p.a, (unsigned)p.M * (unsigned)K * 2u);
-    const i32x4 rb = rsrc_words(p.b, (unsigned)p.N * (unsigned)K * 2u);
+    const i32x4 ra = rsrc_words(static_cast<const uint8_t *>(p.a) - SHIFT, (unsigned)p.M * (unsigned)K * 2u + SHIFT);
+    const i32x4 rb = rsrc_words(static_cast<const uint8_t *>(p.b) - SHIFT, (unsigned)p.N * (unsigned)K * 2u + SHIFT);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
-    const int nk = (K + BK - 1) / BK;   // >= 3: smaller K goes to the 64 x 64 instance
+    const int nk = (K + BK - 1) / BK;   // >= 4: smaller K goes to the 64 x 64 instance
 
     int round = 0;
     int tm, tn;
@@ -188,32 +208,40 @@ void gemm_bf16_nt_kernel(Problem p)
     // overwrites them block by block (its matrix instructions start from 0).
 
     // Copies: wave w fills blocks 8 w .. 8 w + 7 (rows 64 w .. 64 w + 63) of
-    // every unit; lane i fills position i & 7 of row 8 b + i / 8. The
-    // logical chunk a lane fetches depends only on the parity of the block
-    // (row / 2 & 7 = 4 (b & 1) + lane / 16), so per parity q: byte offset of
-    // this lane's chunk in its A row and B row of block q for the current
-    // tile (block j adds j / 2 * 16 rows), and the chunk's first K index (the
-    // K tail switches whole chunks off).
-    int a_off[2], b_off[2], chunk_k[2];
+    // every unit; copy j of the wave fills block 8 w + j, lane i position
+    // i & 7 of its row i / 8. voff[op][j]: this lane's offset for copy j of
+    // operand op (0 = A, 1 = B) at step 0 of the current tile, in the shifted
+    // buffer and less the instruction offset 1024 (j % 4); a step adds 128
+    // bytes per K step through the scalar offset. nvoff: the same for the
+    // next tile (equal to voff after the last tile, so the copies a last tile
+    // issues for its successor read valid rows and are never used). Rows past
+    // M or N lie beyond the buffer range and read as zeros.
+    int voff[2][UNIT_COPIES], nvoff[2][UNIT_COPIES];
+    bool tail_ok[2];   // per block parity: this lane's chunk of step nk - 1 lies below K
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int row = 8 * (UNIT_COPIES * wave + q) + copy_row;
+    for (int j = 0; j < UNIT_COPIES; ++j) {
+        const int row = 8 * (UNIT_COPIES * wave + j) + copy_row;
         const int c = swizzle(row, lane & 7);   // logical chunk stored at position lane & 7
-        chunk_k[q] = 8 * c;
-        a_off[q] = ((tm * BM + row) * K + 8 * c) * 2;
-        b_off[q] = ((tn * BN + row) * K + 8 * c) * 2;
+        voff[0][j] = ((tm * BM + row) * K + 8 * c) * 2 + SHIFT - 1024 * (j & 3);
+        voff[1][j] = ((tn * BN + row) * K + 8 * c) * 2 + SHIFT - 1024 * (j & 3);
+        if (j < 2)
+            tail_ok[j] = (nk - 1) * BK + 8 * c < K;
     }
-    const int block_pair_bytes = 16 * K * 2;   // 16 rows
-    // The next tile of this workgroup, as byte deltas of its operand rows.
     bool has_next = false;
-    int ntm = 0, ntn = 0, da = 0, db = 0;
+    int ntm = 0, ntn = 0;
     auto find_next = [&]() {
         const int pos = schedule_position(blockIdx.x, round + 1, p.grid);
         has_next = pos < p.tiles;
+        int da = 0, db = 0;
         if (has_next) {
             supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, ntm, ntn);
             da = (ntm - tm) * BM * K * 2;
             db = (ntn - tn) * BN * K * 2;
+        }
+#pragma unroll
+        for (int j = 0; j < UNIT_COPIES; ++j) {
+            nvoff[0][j] = voff[0][j] + da;
+            nvoff[1][j] = voff[1][j] + db;
         }
     };
     find_next();
@@ -221,23 +249,11 @@ void gemm_bf16_nt_kernel(Problem p)
     // Per-step bases, hidden from the optimiser again at every step so that
     // addresses are formed where they are used instead of being hoisted out
     // of the loop into registers (which would spill).
-    unsigned copy_base = lds_base + (unsigned)(UNIT_COPIES * wave * 1024);
+    unsigned copy_base[2] = {lds_base + (unsigned)(UNIT_COPIES * wave * 1024),
+                             lds_base + (unsigned)(UNIT_COPIES * wave * 1024 + 4096)};
     int a_ofs[2] = {a_frag + kofs0, a_frag + kofs1};
     int b_ofs[2] = {b_frag + kofs0, b_frag + kofs1};
 
-    // Copy j of unit 2 S + op, S counted from the current tile's first step:
-    // S >= nk belongs to the next tile (its step S - nk). Steps past the last
-    // tile or past K, and the K tail, read as zeros; rows past M or N fall
-    // outside the buffer and do too.
-    auto copy = [&](int S, int op, int j, int slot) {
-        const bool cur = S < nk;
-        const int ks = cur ? S : S - nk;
-        const bool tile_ok = cur || (has_next && ks < nk);
-        const int add = (cur ? 0 : (op ? db : da)) + ks * BK * 2 + (j >> 1) * block_pair_bytes;
-        const bool valid = tile_ok && ks * BK + chunk_k[j & 1] < K;
-        const unsigned dst = __builtin_amdgcn_readfirstlane(copy_base + (unsigned)(slot + j * 1024));
-        copy_1k(op ? rb : ra, dst, valid ? (op ? b_off[j & 1] : a_off[j & 1]) + add : OOB);
-    };
     // ring[x]: LDS offset of the slot of unit 2 s + x during step s (x =
     // 0..4). The next step sees the same slots rotated by two units, so the
     // offsets are carried in scalar registers and renamed, never computed.
@@ -253,13 +269,18 @@ void gemm_bf16_nt_kernel(Problem p)
         ring[3] = r0;
         ring[4] = r1;
     };
-    // Copy c of the window opened by the barrier of step s - d, issued
-    // during step s (d = 0: second half-step, d = 1: first half-step).
-    auto window_copy = [&](int s, int d, int c) {
-        if (c < UNIT_COPIES)
-            copy(s - d + 2, 1, c, ring[(5 - 2 * d) % SLOTS]);   // unit 2 s + 5 - 2 d
-        else
-            copy(s - d + 3, 0, c - UNIT_COPIES, ring[(6 - 2 * d) % SLOTS]);
+    // Pair p of operand op's unit at K step ks_off / 128 into slot `slot`;
+    // NEXT: the next tile's rows; TAIL: chunks at or past K read as zeros.
+    auto copies = [&](int op, auto p_c, int slot, int ks_off, bool next, bool tail) {
+        constexpr int p = decltype(p_c)::value;
+        constexpr int j0 = 2 * p, j1 = 2 * p + 1;
+        int v0 = next ? nvoff[op][j0] : voff[op][j0];
+        int v1 = next ? nvoff[op][j1] : voff[op][j1];
+        if (tail) {
+            v0 = tail_ok[0] ? v0 : OOB_OFF;
+            v1 = tail_ok[1] ? v1 : OOB_OFF;
+        }
+        copy_pair<1024 * (j0 & 3), 1024 * (j1 & 3)>(op ? rb : ra, copy_base[p >> 1] + (unsigned)slot, v0, v1, ks_off);
     };
 
     bf16x8 fa[2][8], fb[2][8];
@@ -280,14 +301,12 @@ void gemm_bf16_nt_kernel(Problem p)
     };
 
     // Prologue of the workgroup's first tile: units A0, B0, A1, B1 (A2 comes
-    // with the first step's window, as for every later tile). All four have
+    // with the first step's copies, as for every later tile). All four have
     // landed before the first barrier, as the epilogue of every later tile
     // waits for the next tile's first two steps.
 #pragma unroll
     for (int u = 0; u < SLOTS - 1; ++u)
-#pragma unroll
-        for (int j = 0; j < UNIT_COPIES; ++j)
-            copy(u >> 1, u & 1, j, u * UNIT_BYTES);
+        static_for<UNIT_COPIES / 2>([&](auto pr) { copies(u & 1, pr, u * UNIT_BYTES, (u >> 1) * ROW_BYTES, false, false); });
     wait_all_copies();
     lds_barrier();
 #pragma unroll
@@ -295,49 +314,45 @@ void gemm_bf16_nt_kernel(Problem p)
         read(ring[0], ring[1], 0, r);
     SCHED_FENCE();
 
-    // Step s of the current tile. KIND 0: a middle step; 1: the last step
-    // (the next tile's B1 is copied early in its second half); 2: the first
-    // step, whose matrix instructions start from 0 and whose barrier needs no
-    // wait: the copies of steps 0 and 1 had all landed before the previous
-    // tile's epilogue stores (or before the prologue's barrier). Only the
-    // copies' order among themselves is relied on, never their order
-    // relative to stores.
-    // The order of matrix instructions, LDS reads, copies, stores and scalar
-    // instructions inside each half-step is fixed by hand (a scheduling
-    // barrier after every matrix instruction and what follows it); only plain
-    // vector ALU work may move across those barriers, so its dependency
-    // chains spread over several matrix instructions instead of stalling the
-    // issue of the next one.
-
+    // Step s of the current tile. Its copies fetch step s + 2: the A tile
+    // during the first half-step into the slot of B_{s-1} (freed by the
+    // previous barrier), the B tile during the second into the slot of A_s.
+    // The barrier between the half-steps follows this wave's last read of
+    // step s and the landing of its copies of step s + 1; FIRST needs no
+    // wait there, since the copies of steps 0 and 1 had all landed before the
+    // previous tile's epilogue stores (or before the prologue's barrier).
+    // Only the copies' order among themselves is relied on, never their order
+    // relative to stores. The order of matrix instructions, LDS reads, copies
+    // and scalar instructions inside each half-step is fixed by hand (a
+    // scheduling barrier after every matrix instruction and what follows
+    // it); only plain vector ALU work may move across those barriers, so its
+    // dependency chains spread over several matrix instructions instead of
+    // stalling the issue of the next one.
     auto step = [&](int s, auto kind_c) {
         constexpr int kind = decltype(kind_c)::value;
-        asm volatile("" : "+v"(a_ofs[0]), "+v"(a_ofs[1]), "+v"(b_ofs[0]), "+v"(b_ofs[1]), "+s"(copy_base));
-        // first half-step: fragments 0; read the second half of step s;
-        // finish the window of step s - 1
+        constexpr bool first = kind == FIRST, next = kind == NEXT0 || kind == NEXT1, tail = kind == TAIL;
+        asm volatile("" : "+v"(a_ofs[0]), "+v"(a_ofs[1]), "+v"(b_ofs[0]), "+v"(b_ofs[1]), "+s"(copy_base[0]), "+s"(copy_base[1]));
+        // byte offset of the K step the copies fetch (step 0 or 1 of the next tile for NEXT0 / NEXT1)
+        const int ks_off = kind == NEXT0 ? 0 : kind == NEXT1 ? ROW_BYTES : (kind == TAIL ? nk - 1 : s + 2) * ROW_BYTES;
+        // first half-step: fragments 0; read the second half of step s
         static_for<64>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
-            mma(0, t, kind == 2);
+            mma(0, t, first);
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (t == read_at(r))
                     read(ring[0], ring[1], 1, r);
-#pragma unroll
-            for (int c = 0; c < WINDOW_COPIES; ++c)
-                if (64 + t == copy_at(c))
-                    window_copy(s, 1, c);
+            if constexpr (t >= a_pair_at(0) && (t - a_pair_at(0)) % 16 == 0 && t <= a_pair_at(UNIT_COPIES / 2 - 1))
+                copies(0, Int<(t - a_pair_at(0)) / 16>{}, ring[4], ks_off, next, tail);
             SCHED_VALU_ONLY();
         });
-        // step s is fully read by this wave and its copies of step s + 1
-        // have landed; only the A tile of step s + 2 (and, after a tile
-        // change, the previous tile's stores) may still be in flight
         wait_reads();
-        if constexpr (kind != 2)
+        if constexpr (!first)
             wait_copies_le<UNIT_COPIES>();
         lds_barrier();
         SCHED_FENCE();
         // second half-step: fragments 1; read the first half of step s + 1
-        // (the next tile's first step after a tile's last); open the window
-        // of step s
+        // (the next tile's first step after a tile's last)
         static_for<64>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             mma(1, t, false);
@@ -345,20 +360,24 @@ void gemm_bf16_nt_kernel(Problem p)
             for (int r = 0; r < 16; ++r)
                 if (t == read_at(r))
                     read(ring[2], ring[3], 0, r);
-#pragma unroll
-            for (int c = 0; c < WINDOW_COPIES; ++c)
-                if (t == (kind == 1 && c < UNIT_COPIES ? copy_at_last(c) : copy_at(c)))
-                    window_copy(s, 0, c);
+            constexpr int b_step = b_pair_at(1, kind == NEXT1) - b_pair_at(0, kind == NEXT1);
+            constexpr int b0 = b_pair_at(0, kind == NEXT1);
+            if constexpr (t >= b0 && (t - b0) % b_step == 0 && (t - b0) / b_step < UNIT_COPIES / 2)
+                copies(1, Int<(t - b0) / b_step>{}, ring[0], ks_off, next, tail);
             SCHED_VALU_ONLY();
         });
+        wait_reads_known();
+        SCHED_FENCE();
         rotate();
     };
 
     for (;;) {
-        step(0, Int<2>{});
-        for (int s = 1; s < nk - 1; ++s)
-            step(s, Int<0>{});
-        step(nk - 1, Int<1>{});
+        step(0, Int<FIRST>{});
+        for (int s = 1; s < nk - 3; ++s)
+            step(s, Int<MID>{});
+        step(nk - 3, Int<TAIL>{});
+        step(nk - 2, Int<NEXT0>{});
+        step(nk - 1, Int<NEXT1>{});
         // epilogue; the next tile's first two steps are in LDS or landing
         wait_all_copies();
         const int ln = fresh_lane_id();
@@ -371,9 +390,9 @@ void gemm_bf16_nt_kernel(Problem p)
             break;
         // switch to the next tile
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            a_off[q] += da;
-            b_off[q] += db;
+        for (int j = 0; j < UNIT_COPIES; ++j) {
+            voff[0][j] = nvoff[0][j];
+            voff[1][j] = nvoff[1][j];
         }
         tm = ntm;
         tn = ntn;

@@ -63,7 +63,7 @@ typedef enum gemm355_status {
  * Two kernel instances compute it: 256 x 256 output tiles, or 64 x 64 tiles
  * when the 256 x 256 tiling has fewer than 128 tiles (too few to occupy the
  * compute units: a problem then bound by operand traffic, such as M = 128
- * with N = K = 8192) or when K <= 128. Both give results within the same
+ * with N = K = 8192) or when K <= 192. Both give results within the same
  * bound; they may sum in different orders.
  */
 int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, void *stream);
@@ -73,7 +73,7 @@ int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, voi
  *
  * A diagnostic for tests and measurements (it is not defined by the pages):
  * instance 0 restores the choice by shape, 1 forces 256 x 256 tiles (except
- * for K <= 128, which always takes the 64 x 64 instance), 2 forces 64 x 64
+ * for K <= 192, which always takes the 64 x 64 instance), 2 forces 64 x 64
  * tiles, for every later gemm_bf16_nt call in the process. Returns
  * GEMM355_OK, or GEMM355_ERR_INVALID_ARG for any other value (the setting is
  * then unchanged). Calls racing with gemm_bf16_nt on other threads see either
