@@ -118,8 +118,8 @@ void gemm_nvfp4_nt_kernel(Problem p)
 
     // Per-lane LDS fragment addresses: row (l32 + 32 i) of the wave's block,
     // logical chunk (2 kk + half) for K sub-step kk of 16 elements.
-    const int a_row = (wm * 128 + l32) * ROW_BYTES;
-    const int b_row = TILE_BYTES + (wn * 128 + l32) * ROW_BYTES;
+    int a_row = (wm * 128 + l32) * ROW_BYTES;
+    int b_row = TILE_BYTES + (wn * 128 + l32) * ROW_BYTES;
     int kofs[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -217,6 +217,12 @@ void gemm_nvfp4_nt_kernel(Problem p)
             uint8_t *nxt = lds + (par ^ 1) * STAGE_BYTES;
             constexpr int set_next = par ^ 1;   // holds step kt + 1
             constexpr int set_free = par;       // held step kt, already written
+            // LDS address bases, hidden from the optimiser again at every step so
+            // that the addresses of both stages are formed where they are used
+            // instead of all being hoisted out of the loop (which spills)
+            asm volatile("" : "+v"(wpos[0]), "+v"(wpos[1]), "+v"(wpos[2]), "+v"(wpos[3]), "+v"(wpos[4]), "+v"(wpos[5]),
+                         "+v"(wpos[6]), "+v"(wpos[7]), "+v"(kofs[0]), "+v"(kofs[1]), "+v"(kofs[2]), "+v"(kofs[3]),
+                         "+v"(a_row), "+v"(b_row));
             // sub-steps 0..2: fragments of sub-step kk + 1 read during sub-step kk
             static_for<48>([&](auto tc) {
                 constexpr int t = decltype(tc)::value;
