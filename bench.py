@@ -49,16 +49,21 @@ WORKLOADS = {
 CONFIG_INDEX = {"bf16_256": 0, "bf16_4096": 1, "bf16_8192": 2, "bf16_8000": 3, "bf16_skinny": 3,
                 "fp4_8192": 4}
 KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel",
-               "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel"}
+               "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel",
+               "bf16_splitk": "gemm355::bf16_splitk::gemm_bf16_nt_splitk_kernel",
+               "bf16_splitk_reduce": "gemm355::bf16_splitk::splitk_reduce_kernel"}
 
 
-def kernel_for(kind: str, M: int, N: int, K: int) -> str:
-    """The kernel gemm_bf16_nt / gemm_nvfp4_nt launches for this shape (the
-    library's rule: fewer than 128 tiles of 256 x 256, or K <= 192 -> 64 x 64
-    tiles)."""
-    if kind == "bf16" and ((-(-M // 256)) * (-(-N // 256)) < 128 or K <= 192):
-        return KERNEL_NAME["bf16_small"]
-    return KERNEL_NAME[kind]
+def kernels_for(kind: str, M: int, N: int, K: int, compute_units: int = 256) -> list:
+    """The kernels gemm_bf16_nt / gemm_nvfp4_nt launches for this shape, in
+    launch order (the library's own choice, gemm355_bf16_plan)."""
+    if kind != "bf16":
+        return [KERNEL_NAME[kind]]
+    import dense_gemm_14_amd as g
+    instance, _ = g.bf16_plan(M, N, K, compute_units)
+    if instance == 3:
+        return [KERNEL_NAME["bf16_splitk"], KERNEL_NAME["bf16_splitk_reduce"]]
+    return [KERNEL_NAME["bf16_small" if instance == 2 else "bf16"]]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -255,8 +260,9 @@ def main(argv=None):
         gbs = alg_bytes / (ms_step * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    roofline.update({"kernel": kernel_for(kind, M, N, K), "traffic": traffic, "algorithmic_bytes": alg_bytes,
-                     "mean_launch_ms": round(ms_step, 5)})
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    roofline.update({"kernel": " + ".join(kernels_for(kind, M, N, K, cus)), "traffic": traffic,
+                     "algorithmic_bytes": alg_bytes, "mean_launch_ms": round(ms_step, 5)})
     out = {
         "metric": "TFLOP/s for BF16 C=A·B^T at M=N=K=8192; % of MI355X dense BF16 peak"
         if args.workload == "bf16_8192" else "TFLOP/s for %s C=A·B^T at %dx%dx%d" % (kind, M, N, K),

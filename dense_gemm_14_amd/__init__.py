@@ -9,6 +9,7 @@ The functions mirror the C entry points declared in ``include/gemm355.h``:
     gemm_bf16_nt(M, N, K, A, B, C, stream=None)
     gemm_nvfp4_nt(M, N, K, Aq, SFA, Bq, SFB, C, stream=None)
     force_instance(instance)          # BF16 instance override (diagnostic)
+    bf16_plan(M, N, K, compute_units)  # (instance, splits) gemm_bf16_nt would run
 
 Operands may be torch tensors on a ROCm device (their storage is checked
 against the sizes before the call, since the C side cannot see it) or raw
@@ -32,9 +33,10 @@ ERR_UNSUPPORTED = 2
 ERR_NO_DEVICE = 3
 ERR_LAUNCH = 4
 
-INSTANCE_AUTO = 0    # gemm_bf16_nt picks 256 x 256 or 64 x 64 tiles by shape
+INSTANCE_AUTO = 0    # gemm_bf16_nt picks the instance by shape
 INSTANCE_LARGE = 1   # 256 x 256 output tiles
 INSTANCE_SMALL = 2   # 64 x 64 output tiles
+INSTANCE_SPLITK = 3  # 128 x 128 output tiles, K split over workgroups, FP32 partials reduced
 
 _lib = None
 
@@ -70,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.gemm355_schedule.restype = i
     lib.gemm355_force_instance.argtypes = [i]
     lib.gemm355_force_instance.restype = i
+    lib.gemm355_bf16_plan.argtypes = [i, i, i, i, p, p]
+    lib.gemm355_bf16_plan.restype = i
     _lib = lib
     return lib
 
@@ -148,8 +152,18 @@ def gemm_nvfp4_nt(M: int, N: int, K: int, Aq, SFA, Bq, SFB, C, stream=None) -> N
 
 def force_instance(instance: int) -> None:
     """Force gemm_bf16_nt's kernel instance for the whole process
-    (INSTANCE_AUTO, INSTANCE_LARGE or INSTANCE_SMALL)."""
+    (INSTANCE_AUTO, INSTANCE_LARGE, INSTANCE_SMALL or INSTANCE_SPLITK)."""
     _check(load().gemm355_force_instance(instance), "gemm355_force_instance")
+
+
+def bf16_plan(M: int, N: int, K: int, compute_units: int):
+    """(instance, splits) that gemm_bf16_nt runs for this shape on a device
+    with `compute_units` compute units; host only."""
+    inst = ctypes.c_int(0)
+    splits = ctypes.c_int(0)
+    _check(load().gemm355_bf16_plan(M, N, K, compute_units, ctypes.byref(inst), ctypes.byref(splits)),
+           "gemm355_bf16_plan")
+    return inst.value, splits.value
 
 
 def tile_order(tiles_m: int, tiles_n: int, supergroup: int):

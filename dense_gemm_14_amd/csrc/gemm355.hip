@@ -3,13 +3,16 @@
 // is declared in include/gemm355.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <stdint.h>
+#include <vector>
 
 #include "gemm355.h"
 #include "gemm_bf16.hpp"
 #include "gemm_bf16_small.hpp"
+#include "gemm_bf16_splitk.hpp"
 #include "gemm_fp4.hpp"
 #include "schedule.hpp"
 
@@ -23,7 +26,8 @@ constexpr int kMaxDevices = 64;
 constexpr int kSupergroup = 8; // adjacent N tiles per band of the visiting order
 
 // BF16 kernel instance: 0 = chosen by shape, 1 = 256 x 256 tiles, 2 = 64 x 64
-// tiles (set through gemm355_force_instance, for tests and measurements).
+// tiles, 3 = 128 x 128 tiles with split K (set through gemm355_force_instance,
+// for tests and measurements).
 std::atomic<int> g_bf16_instance{0};
 
 // The 256 x 256 kernel needs enough tiles to occupy the compute units; below
@@ -32,6 +36,22 @@ constexpr int64_t kSmallTileThreshold = 128;
 
 std::mutex g_cu_lock;
 int g_cu_count[kMaxDevices];   // 0 = not queried yet
+
+// Workspace for the split-K partials: one buffer per (device, stream), used
+// only by work enqueued on that stream, so calls on one stream reuse it in
+// stream order and calls on different streams never share one. Buffers come
+// from a per-device memory pool of the library's own and grow with
+// stream-ordered allocation (the old buffer is freed on the same stream, after
+// the work already enqueued there); the pool keeps its memory.
+std::mutex g_pool_lock;
+hipMemPool_t g_pool[kMaxDevices];
+struct StreamWorkspace {
+    int dev;
+    hipStream_t stream;
+    void *ptr;
+    size_t bytes;
+};
+std::vector<StreamWorkspace> g_workspaces;   // guarded by g_pool_lock
 
 // Compute units of the current device, queried once per device.
 int compute_units(int *cus)
@@ -47,6 +67,47 @@ int compute_units(int *cus)
         g_cu_count[dev] = n;
     }
     *cus = g_cu_count[dev];
+    return GEMM355_OK;
+}
+
+// The workspace of `stream` on the current device, at least `bytes` long.
+int stream_workspace(hipStream_t stream, size_t bytes, void **ws)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GEMM355_ERR_NO_DEVICE;
+    std::lock_guard<std::mutex> guard(g_pool_lock);
+    if (!g_pool[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t created = nullptr;
+        if (hipMemPoolCreate(&created, &props) != hipSuccess)
+            return GEMM355_ERR_LAUNCH;
+        uint64_t keep = UINT64_MAX;   // never hand memory back between calls
+        (void)hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep);
+        g_pool[dev] = created;
+    }
+    for (StreamWorkspace &w : g_workspaces) {
+        if (w.dev != dev || w.stream != stream)
+            continue;
+        if (w.bytes < bytes) {
+            void *grown = nullptr;
+            if (hipMallocFromPoolAsync(&grown, bytes, g_pool[dev], stream) != hipSuccess)
+                return GEMM355_ERR_LAUNCH;
+            (void)hipFreeAsync(w.ptr, stream);
+            w.ptr = grown;
+            w.bytes = bytes;
+        }
+        *ws = w.ptr;
+        return GEMM355_OK;
+    }
+    void *fresh = nullptr;
+    if (hipMallocFromPoolAsync(&fresh, bytes, g_pool[dev], stream) != hipSuccess)
+        return GEMM355_ERR_LAUNCH;
+    g_workspaces.push_back({dev, stream, fresh, bytes});
+    *ws = fresh;
     return GEMM355_OK;
 }
 
@@ -87,6 +148,90 @@ int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n =
     return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 
+// Split-K plan for 128 x 128 tiles: enough splits to give every compute unit a
+// work item (at most MAX_SPLITS), each split at least 8 K steps long.
+void splitk_plan(int M, int N, int K, int cus, int *tiles_m, int *tiles_n, int *splits, int *steps_per_split)
+{
+    namespace sk = gemm355::bf16_splitk;
+    *tiles_m = (int)ceil_div(M, sk::TM);
+    *tiles_n = (int)ceil_div(N, sk::TN);
+    const int64_t tiles = int64_t(*tiles_m) * *tiles_n;
+    const int nk = (int)ceil_div(K, sk::BK);
+    int s = (int)std::max<int64_t>(1, cus / std::max<int64_t>(1, tiles));
+    s = std::min(s, sk::MAX_SPLITS);
+    s = std::max(1, std::min(s, nk / 8));
+    const int per = (int)std::max<int64_t>(1, ceil_div(nk, s));
+    *steps_per_split = per;
+    *splits = std::max(1, (int)ceil_div(nk, per));   // no empty split
+}
+
+// The BF16 instance for a problem (forced: 0 = by shape, else 1..3) and, for
+// instance 3, the number of K splits. Pure host arithmetic.
+int choose_bf16_instance(int M, int N, int K, int cus, int forced, int *splits)
+{
+    int tmn = 0, tnn = 0, per = 0;
+    splitk_plan(M, N, K, cus, &tmn, &tnn, splits, &per);
+    int instance = forced;
+    if (instance == 0) {
+        instance = 1;
+        if (ceil_div(M, BM) * ceil_div(N, BN) < kSmallTileThreshold) {
+            // Few output tiles: the time goes into streaming operands. Take
+            // the split when its busiest compute unit moves fewer bytes (a
+            // 64 x 64 tile streams 128 rows over all of K, a split work item
+            // 256 rows over its K range plus a 64 KiB partial tile), except
+            // when the 64 x 64 tiles fill the units in exactly one round:
+            // there both are bound by the copies in flight per unit over the
+            // memory's loaded latency, and the split's partials and second
+            // kernel cost more than its fewer bytes save (measured).
+            const int64_t tiles64 = ceil_div(M, 64) * ceil_div(N, 64);
+            const int64_t bytes64 = ceil_div(tiles64, cus) * 128 * int64_t(K) * 2;
+            const int64_t items = int64_t(tmn) * tnn * *splits;
+            const int64_t bytes_split = ceil_div(items, cus) * (256 * int64_t(per) * 64 * 2 + 65536);
+            const bool one_round = tiles64 >= cus && tiles64 < 2 * int64_t(cus);
+            instance = !one_round && *splits >= 2 && bytes_split < bytes64 ? 3 : 2;
+        }
+    }
+    if (instance == 1 && K <= 3 * gemm355::bf16::BK)
+        instance = 2;   // the 256 x 256 kernel runs its tiles back to back and needs K > 192
+    if (instance != 3)
+        *splits = 1;
+    return instance;
+}
+
+// Split-K instance: partial tiles into a stream-ordered workspace, then the
+// reduction into C, both on `stream`.
+int launch_splitk(const Problem &p, void *stream)
+{
+    namespace sk = gemm355::bf16_splitk;
+    int cus = 0;
+    int rc = compute_units(&cus);
+    if (rc != GEMM355_OK)
+        return rc;
+    sk::SplitProblem sp = {};
+    sp.a = p.a;
+    sp.b = p.b;
+    sp.c = p.c;
+    sp.M = p.M;
+    sp.N = p.N;
+    sp.K = p.K;
+    splitk_plan(p.M, p.N, p.K, cus, &sp.tiles_m, &sp.tiles_n, &sp.splits, &sp.steps_per_split);
+    const int64_t items = int64_t(sp.tiles_m) * sp.tiles_n * sp.splits;
+    if (items > (int64_t(1) << 30))
+        return GEMM355_ERR_UNSUPPORTED;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    rc = stream_workspace(s, size_t(items) * sk::TILE_FLOATS * sizeof(float), &ws);
+    if (rc != GEMM355_OK)
+        return rc;
+    sp.ws = static_cast<float *>(ws);
+    (void)hipGetLastError(); // clear a stale error so the check below is ours
+    hipLaunchKernelGGL(sk::gemm_bf16_nt_splitk_kernel, dim3((unsigned)items), dim3(gemm355::THREADS), 0, s, sp);
+    const int64_t outs = int64_t(p.M) * (p.N / 8);
+    hipLaunchKernelGGL(sk::splitk_reduce_kernel, dim3((unsigned)ceil_div(outs, sk::REDUCE_THREADS)),
+                       dim3(sk::REDUCE_THREADS), 0, s, sp);
+    return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
+}
+
 } // namespace
 
 extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, void *stream)
@@ -114,20 +259,31 @@ extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, v
     p.M = M;
     p.N = N;
     p.K = K;
-    int instance = g_bf16_instance.load(std::memory_order_relaxed);
-    if (instance == 0)
-        instance = ceil_div(M, BM) * ceil_div(N, BN) < kSmallTileThreshold ? 2 : 1;
-    if (K <= 3 * gemm355::bf16::BK)
-        instance = 2;   // the 256 x 256 kernel runs its tiles back to back and needs K > 192
+    int cus = 0;
+    const int rc = compute_units(&cus);
+    if (rc != GEMM355_OK)
+        return rc;
+    int splits = 0;
+    const int instance = choose_bf16_instance(M, N, K, cus, g_bf16_instance.load(std::memory_order_relaxed), &splits);
+    if (instance == 3)
+        return launch_splitk(p, stream);
     if (instance == 2)
         return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel, p, stream, gemm355::bf16_small::TM,
                       gemm355::bf16_small::TN);
     return launch(gemm355::bf16::gemm_bf16_nt_kernel, p, stream);
 }
 
+extern "C" int gemm355_bf16_plan(int M, int N, int K, int compute_units, int *instance, int *splits)
+{
+    if (M <= 0 || N <= 0 || K < 0 || compute_units <= 0 || !instance || !splits)
+        return GEMM355_ERR_INVALID_ARG;
+    *instance = choose_bf16_instance(M, N, K, compute_units, g_bf16_instance.load(std::memory_order_relaxed), splits);
+    return GEMM355_OK;
+}
+
 extern "C" int gemm355_force_instance(int instance)
 {
-    if (instance < 0 || instance > 2)
+    if (instance < 0 || instance > 3)
         return GEMM355_ERR_INVALID_ARG;
     g_bf16_instance.store(instance, std::memory_order_relaxed);
     return GEMM355_OK;

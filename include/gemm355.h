@@ -12,8 +12,9 @@
  *
  * Conventions shared by every entry point
  *  - All array pointers are DEVICE pointers owned by the caller. The library
- *    allocates nothing, keeps no per-call state and never synchronises: it
- *    enqueues the work on `stream` and returns. `stream` is a hipStream_t
+ *    keeps no per-call state and never synchronises: it enqueues the work on
+ *    `stream` and returns. It allocates device memory only for the split-K
+ *    workspace of gemm_bf16_nt (see there), stream-ordered. `stream` is a hipStream_t
  *    passed as void*; NULL means the default (null) stream.
  *  - Arrays are dense, row-major, with no padding between rows (the leading
  *    dimension of A and B is K, that of C is N). C must not overlap any input.
@@ -60,11 +61,23 @@ typedef enum gemm355_status {
  * Requirements, else GEMM355_ERR_UNSUPPORTED: A, B, C 16-byte aligned;
  * K % 8 == 0 and N % 8 == 0 (whole 16-byte row segments); every operand,
  * padded up to a multiple of 256 rows, spans less than 2^31 bytes.
- * Two kernel instances compute it: 256 x 256 output tiles, or 64 x 64 tiles
- * when the 256 x 256 tiling has fewer than 128 tiles (too few to occupy the
- * compute units: a problem then bound by operand traffic, such as M = 128
- * with N = K = 8192) or when K <= 192. Both give results within the same
- * bound; they may sum in different orders.
+ * Three kernel instances compute it: 256 x 256 output tiles; or, when the
+ * 256 x 256 tiling has fewer than 128 tiles (too few to occupy the compute
+ * units: a problem then bound by operand traffic), either 64 x 64 tiles or
+ * 128 x 128 tiles whose K range is split over 2 to 8 workgroups (at least 8
+ * steps of 64 each) writing FP32 partial tiles that a second kernel on the
+ * same stream adds in split order and rounds once to BF16 -- the split when
+ * its busiest compute unit moves fewer bytes, unless the 64 x 64 tiles fill
+ * the compute units in exactly one round (as for M = 128, N = K = 8192);
+ * whenever K <= 192, 64 x 64 tiles. gemm355_bf16_plan reports the choice.
+ * The split's partials live in one workspace per (device, stream), which only
+ * work enqueued on that stream uses; it comes from a memory pool of the
+ * library's own, grows by stream-ordered allocation, and is kept until the
+ * process ends (at most 8 x 64 KiB per 128 x 128 output tile). Calls on
+ * different streams never share a workspace; a stream handle reused after
+ * hipStreamDestroy while work of the old stream is still pending would.
+ * All instances give results within the same bound; they may sum in different
+ * orders. Each instance is deterministic: the same call gives the same bits.
  */
 int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, void *stream);
 
@@ -74,12 +87,27 @@ int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, voi
  * A diagnostic for tests and measurements (it is not defined by the pages):
  * instance 0 restores the choice by shape, 1 forces 256 x 256 tiles (except
  * for K <= 192, which always takes the 64 x 64 instance), 2 forces 64 x 64
- * tiles, for every later gemm_bf16_nt call in the process. Returns
+ * tiles, 3 forces 128 x 128 tiles with split K (one split when K is too
+ * short for two), for every later gemm_bf16_nt call in the process. Returns
  * GEMM355_OK, or GEMM355_ERR_INVALID_ARG for any other value (the setting is
  * then unchanged). Calls racing with gemm_bf16_nt on other threads see either
  * the old or the new setting. No HIP call is made.
  */
 int gemm355_force_instance(int instance);
+
+/*
+ * gemm355_bf16_plan -- the instance gemm_bf16_nt would run for M x N x K on
+ * a device with `compute_units` compute units, under the current
+ * gemm355_force_instance setting.
+ *
+ * A diagnostic for tests and measurements (it is not defined by the pages).
+ * Writes the instance (1 = 256 x 256, 2 = 64 x 64, 3 = 128 x 128 with split K)
+ * to *instance and the number of K splits (1 unless the instance is 3) to
+ * *splits. Returns GEMM355_OK, or GEMM355_ERR_INVALID_ARG for M <= 0,
+ * N <= 0, K < 0, compute_units <= 0 or a NULL output pointer (outputs then
+ * unchanged). Pure host arithmetic: no HIP call is made.
+ */
+int gemm355_bf16_plan(int M, int N, int K, int compute_units, int *instance, int *splits);
 
 /*
  * gemm_nvfp4_nt -- block-scaled FP4 operands, BF16 output.

@@ -2,6 +2,7 @@
 declares, rejects bad arguments before any HIP call, and its host-side tile
 schedule is a bijection with the documented order. No compute is launched.
 """
+import ctypes
 import os
 
 import numpy as np
@@ -116,7 +117,52 @@ def test_schedule_keeps_an_xcds_tiles_compact():
 
 def test_force_instance_accepts_only_known_instances():
     lib = g.load()
-    for bad in (-1, 3, 99):
+    for bad in (-1, 4, 99):
         assert lib.gemm355_force_instance(bad) == g.ERR_INVALID_ARG
-    for ok in (g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_AUTO):
+    for ok in (g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_SPLITK, g.INSTANCE_AUTO):
         assert lib.gemm355_force_instance(ok) == g.OK
+
+
+def test_bf16_plan_for_the_workload_shapes():
+    # 256 compute units: the square workloads take 256 x 256 tiles, the small
+    # one 64 x 64 tiles; the skinny one (M = 128) has exactly one round of 256
+    # tiles of 64 x 64, where that instance beats splitting K (measured).
+    g.force_instance(g.INSTANCE_AUTO)
+    assert g.bf16_plan(8192, 8192, 8192, 256) == (g.INSTANCE_LARGE, 1)
+    assert g.bf16_plan(8000, 8000, 8000, 256) == (g.INSTANCE_LARGE, 1)
+    assert g.bf16_plan(4096, 4096, 4096, 256) == (g.INSTANCE_LARGE, 1)
+    assert g.bf16_plan(256, 256, 256, 256) == (g.INSTANCE_SMALL, 1)
+    assert g.bf16_plan(128, 8192, 8192, 256) == (g.INSTANCE_SMALL, 1)
+    # fewer 64 x 64 tiles than compute units, or two rounds of them: split K
+    assert g.bf16_plan(64, 4096, 8192, 256) == (g.INSTANCE_SPLITK, 8)
+    assert g.bf16_plan(512, 4096, 8192, 256) == (g.INSTANCE_SPLITK, 2)
+    # short K: nothing to split
+    assert g.bf16_plan(128, 8192, 2048, 256) == (g.INSTANCE_SMALL, 1)
+    # K too short for the 256 x 256 instance's four kinds of step
+    assert g.bf16_plan(4096, 4096, 192, 256) == (g.INSTANCE_SMALL, 1)
+    assert g.bf16_plan(4096, 4096, 200, 256)[0] == g.INSTANCE_LARGE
+    # splitting never makes a split shorter than 8 steps of 64, or empty
+    for M, N, K in [(128, 1032, 4104), (64, 64, 4104), (512, 4096, 8192), (128, 2048, 520)]:
+        inst, splits = g.bf16_plan(M, N, K, 256)
+        if inst == g.INSTANCE_SPLITK:
+            steps = -(-K // 64)
+            per = -(-steps // splits)
+            assert 2 <= splits <= 8 and per >= 8 and (splits - 1) * per < steps, (M, N, K, splits)
+
+
+def test_bf16_plan_follows_the_forced_instance_and_checks_arguments():
+    lib = g.load()
+    try:
+        g.force_instance(g.INSTANCE_SMALL)
+        assert g.bf16_plan(8192, 8192, 8192, 256) == (g.INSTANCE_SMALL, 1)
+        g.force_instance(g.INSTANCE_SPLITK)
+        inst, splits = g.bf16_plan(8192, 8192, 8192, 256)
+        assert inst == g.INSTANCE_SPLITK and splits >= 1
+        g.force_instance(g.INSTANCE_LARGE)
+        assert g.bf16_plan(8192, 8192, 128, 256) == (g.INSTANCE_SMALL, 1)
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+    out = (ctypes.c_int * 2)()
+    for bad in [(0, 8, 8, 256), (8, -1, 8, 256), (8, 8, -8, 256), (8, 8, 8, 0)]:
+        assert lib.gemm355_bf16_plan(*bad, ctypes.byref(out, 0), ctypes.byref(out, 4)) == g.ERR_INVALID_ARG
+    assert lib.gemm355_bf16_plan(8, 8, 8, 256, None, ctypes.byref(out, 4)) == g.ERR_INVALID_ARG

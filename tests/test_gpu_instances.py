@@ -1,8 +1,9 @@
-"""Both BF16 kernel instances (256 x 256 and 64 x 64 output tiles), each forced
+"""The three BF16 kernel instances (256 x 256 output tiles, 64 x 64 tiles, and
+128 x 128 tiles with split K and a reduction of FP32 partials), each forced
 through gemm355_force_instance, against the oracle: ragged shapes element by
 element, exactly summable inputs bitwise, K = 0, and B = I bitwise. The
-automatic choice routes small problems to the 64 x 64 instance, so without
-forcing, the 256 x 256 instance would only see the large workload shapes."""
+automatic choice routes small and skinny problems away from the 256 x 256
+instance, so without forcing it would only see the large workload shapes."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +16,7 @@ from tests.gpu_util import GuardedC, need_gpu, sample_positions, to_dev
 
 pytestmark = pytest.mark.gpu
 
-INSTANCES = [g.INSTANCE_LARGE, g.INSTANCE_SMALL]
+INSTANCES = [g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_SPLITK]
 
 
 @pytest.fixture
@@ -78,7 +79,7 @@ def test_instances_agree_within_bound_at_a_medium_shape():
     B = syn.bf16_uniform(N, K, seed=92)
     ref = oracle.gemm_bf16_nt(A, B)
     try:
-        for inst in (g.INSTANCE_AUTO, g.INSTANCE_LARGE, g.INSTANCE_SMALL):
+        for inst in (g.INSTANCE_AUTO, g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_SPLITK):
             g.force_instance(inst)
             res = tolerance.check(run_bf16(A, B, M, N, K), ref, K)
             assert res, (inst, res)
@@ -89,8 +90,8 @@ def test_instances_agree_within_bound_at_a_medium_shape():
 # Shapes with more 256 x 256 tiles than workgroups, so workgroups run several
 # tiles back to back (the next tile's first units are copied during the
 # previous tile's last steps): ragged M and N, K tails, K just above the
-# 128 that the 256 x 256 instance needs.
-MULTI_TILE = [(4352, 4104, 520), (4400, 4400, 136), (4360, 4352, 1000)]
+# 192 that the 256 x 256 instance needs (four steps, the last one partial).
+MULTI_TILE = [(4352, 4104, 520), (4400, 4400, 200), (4360, 4352, 1000)]
 
 
 @pytest.mark.parametrize("M,N,K", MULTI_TILE)
@@ -126,3 +127,47 @@ def test_large_instance_multi_tile_exact_every_element():
     assert np.array_equal(oracle.gemm_bf16_nt_at(A, B, ms, ns), want[ms, ns])
     bad = np.argwhere(C != want)
     assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+
+
+def test_splitk_many_splits_exact_every_element():
+    # 2 x 9 tiles of 128 x 128 and 65 K steps: the automatic plan splits K
+    # eight ways (the last split has two steps, the last step a K tail). With
+    # multiples of 1/16 every partial sum and the sum of the partials is exact
+    # in FP32, so every element must match the correctly rounded sum.
+    need_gpu()
+    M, N, K = 136, 1032, 4104
+    A = syn.bf16_sixteenths(M, K, seed=71)
+    B = syn.bf16_sixteenths(N, K, seed=72)
+    C = run_bf16(A, B, M, N, K)
+    want = oracle.bf16_from_double(tolerance.bf16_bits_to_f64(A) @ tolerance.bf16_bits_to_f64(B).T)
+    assert np.array_equal(oracle.gemm_bf16_nt(A[:3], B), want[:3])
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+
+
+def test_splitk_streams_and_determinism():
+    # The partials live in stream-ordered memory: the same product on a side
+    # stream and on the default stream, and twice in a row, is bitwise equal
+    # (splits are added in a fixed order) and within the bound of the oracle.
+    need_gpu()
+    M, N, K = 128, 2048, 4096
+    A = syn.bf16_uniform(M, K, seed=81)
+    B = syn.bf16_uniform(N, K, seed=82)
+    s = torch.cuda.Stream()
+    dA, dB = to_dev(A), to_dev(B)
+    outs = []
+    torch.cuda.synchronize()
+    for stream in (s, None, None):
+        if stream is None:
+            C = GuardedC(M, N)
+            g.gemm_bf16_nt(M, N, K, dA, dB, C.view)
+        else:
+            with torch.cuda.stream(stream):
+                C = GuardedC(M, N)
+                g.gemm_bf16_nt(M, N, K, dA, dB, C.view, stream=stream)
+        torch.cuda.synchronize()
+        assert C.guards_intact(), "write outside C"
+        outs.append(C.bits())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    res = tolerance.check(outs[0], oracle.gemm_bf16_nt(A, B), K)
+    assert res, res
