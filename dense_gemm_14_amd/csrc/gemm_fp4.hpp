@@ -45,10 +45,14 @@ __device__ inline int swizzle(int row, int chunk)
 
 // ---- block-scaled FP4 operands ---------------------------------------------
 //
-// Thread t stages row t of the A tile and row t of the B tile: per K step of
-// 64 elements that is 32 bytes of packed codes and 4 scale bytes per row,
-// held in one of two register sets (the step being written to LDS and the
-// step after it, already requested from memory).
+// Thread t stages rows t / 2 and t / 2 + 128 of the A tile and of the B
+// tile, K half t % 2 of each step: 16 bytes of packed codes (32 elements) and
+// the row's 4 scale bytes (of which it uses the two of its half) per row and
+// operand, held in one of two register sets (the step being written to LDS
+// and the step after it, already requested from memory). The two threads of a
+// pair read the two halves of the same 32-byte row segment, so each load
+// instruction touches 32 rows instead of 64: the memory pipeline's cost
+// follows the number of distinct lines a load touches.
 // Decoding ("NVFP4 GEMM on Blackwell", section "NVFP4 Datatype"): each code
 // pair converts to two FP16 E2M1 values (v_cvt_scalef32_pk_f16_fp4 with a unit
 // scale), then one packed FP16 multiply applies the E4M3 scale of its 16-element
@@ -59,8 +63,8 @@ __device__ inline int swizzle(int row, int chunk)
 // used because gfx950 has a packed FP16 multiply but no packed BF16 one; the
 // FP16 and BF16 matrix instructions have the same rate.)
 struct StageRegs {
-    u32x4 a_code[2], b_code[2];
-    unsigned a_sf, b_sf;
+    u32x4 a_code[2], b_code[2];   // [row r0, r0 + 128]: this thread's 32 codes of each row
+    unsigned a_sf[2], b_sf[2];    // the rows' scale dwords (4 blocks of 16)
 };
 
 // 8 codes (one dword) scaled by `s` -> 8 FP16 values.
@@ -99,7 +103,8 @@ __device__ inline f16x2 scale2(unsigned sf)
 // vector instructions under one 32 x 32 x 16 matrix instruction before the
 // matrix rate drops; measured).
 constexpr int CHUNK_EVERY = 3;   // matrix instructions per written chunk
-constexpr int LOAD_AT = 2;       // first of the six loads (one every 4 instructions)
+constexpr int LOADS = 8;         // staging loads per thread and step
+constexpr int LOAD_AT = 2;       // first of them (then one every 4 instructions)
 
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_nvfp4_nt_kernel(Problem p)
@@ -124,11 +129,16 @@ void gemm_nvfp4_nt_kernel(Problem p)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
         kofs[kk] = swizzle(l32, 2 * kk + half) << 4;   // rows differ from l32 by multiples of 32
-    // chunk positions of this thread's staged row (row tid of each tile)
-    int wpos[8];
+    // Staged rows r0 = tid / 2 and r0 + 128 (same swizzle: they differ by a
+    // multiple of 16 rows), K half kh = tid % 2 of each step, i.e. logical
+    // chunks 4 kh .. 4 kh + 3 of each row. wpos[d]: LDS position of chunk
+    // 4 kh + d of row r0; row r0 + 128 is 128 rows further.
+    const int r0 = tid >> 1, kh = tid & 1;
+    const int sf_shift = 16 * kh;   // this half's two scale bytes, moved to bytes 0 and 1
+    int wpos[4];
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
-        wpos[d] = tid * ROW_BYTES + (swizzle(tid, d) << 4);
+    for (int d = 0; d < 4; ++d)
+        wpos[d] = r0 * ROW_BYTES + (swizzle(r0, 4 * kh + d) << 4);
 
     const unsigned kc = (unsigned)K / 2, ks = (unsigned)K / 16;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (unsigned)p.M * kc);
@@ -145,33 +155,37 @@ void gemm_nvfp4_nt_kernel(Problem p)
         int tm, tn;
         supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
 
-        const int a_code_off = (tm * BM + tid) * (int)kc, b_code_off = (tn * BN + tid) * (int)kc;
-        const int a_sf_off = (tm * BM + tid) * (int)ks, b_sf_off = (tn * BN + tid) * (int)ks;
+        const int a_code_off = (tm * BM + r0) * (int)kc + 16 * kh, b_code_off = (tn * BN + r0) * (int)kc + 16 * kh;
+        const int a_sf_off = (tm * BM + r0) * (int)ks, b_sf_off = (tn * BN + r0) * (int)ks;
+        const int row2_codes = 128 * (int)kc, row2_sf = 128 * (int)ks;   // row r0 + 128
         StageRegs regs[2];
-        // load q (0..5) of step kt into register set `set`; K % 64 == 0, so a
-        // step is whole or past K, where it reads zeros
+        // load q (0..7) of step kt into register set `set`: codes of row r0,
+        // codes of row r0 + 128, scales of r0, scales of r0 + 128, for A (q < 4)
+        // then B. K % 64 == 0, so a step is whole or past K, where it reads zeros.
         auto load = [&](int kt, int set, int q) {
             const int k0 = kt * BK;
             const bool valid = k0 < K;
             StageRegs &r = regs[set];
             switch (q) {
             case 0: r.a_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, valid ? a_code_off + k0 / 2 : OOB, 0, 0)); break;
-            case 1: r.a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, valid ? a_code_off + k0 / 2 + 16 : OOB, 0, 0)); break;
-            case 2: r.a_sf = __builtin_amdgcn_raw_buffer_load_b32(rsa, valid ? a_sf_off + k0 / 16 : OOB, 0, 0); break;
-            case 3: r.b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, valid ? b_code_off + k0 / 2 : OOB, 0, 0)); break;
-            case 4: r.b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, valid ? b_code_off + k0 / 2 + 16 : OOB, 0, 0)); break;
-            default: r.b_sf = __builtin_amdgcn_raw_buffer_load_b32(rsb, valid ? b_sf_off + k0 / 16 : OOB, 0, 0); break;
+            case 1: r.a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, valid ? a_code_off + row2_codes + k0 / 2 : OOB, 0, 0)); break;
+            case 2: r.a_sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, valid ? a_sf_off + k0 / 16 : OOB, 0, 0); break;
+            case 3: r.a_sf[1] = __builtin_amdgcn_raw_buffer_load_b32(rsa, valid ? a_sf_off + row2_sf + k0 / 16 : OOB, 0, 0); break;
+            case 4: r.b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, valid ? b_code_off + k0 / 2 : OOB, 0, 0)); break;
+            case 5: r.b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, valid ? b_code_off + row2_codes + k0 / 2 : OOB, 0, 0)); break;
+            case 6: r.b_sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, valid ? b_sf_off + k0 / 16 : OOB, 0, 0); break;
+            default: r.b_sf[1] = __builtin_amdgcn_raw_buffer_load_b32(rsb, valid ? b_sf_off + row2_sf + k0 / 16 : OOB, 0, 0); break;
             }
         };
-        // chunk c (0..15) of register set `set` into `stage`: c < 8 is chunk c
-        // of the A row, otherwise chunk c - 8 of the B row
+        // chunk c (0..15) of register set `set` into `stage`: A for c < 8,
+        // else B; row r0 + 128 * ((c / 4) & 1); chunk 4 kh + c % 4 of the row
         auto write_chunk = [&](uint8_t *stage, int set, auto c_c) {
             constexpr int c = decltype(c_c)::value;
-            constexpr int d = c & 7;
+            constexpr int rr = (c >> 2) & 1, d = c & 3;
             const StageRegs &r = regs[set];
-            const unsigned codes = (c < 8 ? r.a_code : r.b_code)[d >> 2][d & 3];
-            const f16x2 s = scale2<d / 2>(c < 8 ? r.a_sf : r.b_sf);
-            *reinterpret_cast<f16x8 *>(stage + (c < 8 ? 0 : TILE_BYTES) + wpos[d]) = decode8(codes, s);
+            const unsigned codes = (c < 8 ? r.a_code : r.b_code)[rr][d];
+            const f16x2 s = scale2<d / 2>((c < 8 ? r.a_sf : r.b_sf)[rr] >> sf_shift);
+            *reinterpret_cast<f16x8 *>(stage + (c < 8 ? 0 : TILE_BYTES) + rr * 128 * ROW_BYTES + wpos[d]) = decode8(codes, s);
         };
 
         f32x16 acc[4][4];
@@ -198,10 +212,10 @@ void gemm_nvfp4_nt_kernel(Problem p)
         // Prologue: step 0 into stage 0, step 1 requested into set 1.
         lds_barrier();            // every wave is done with the previous tile's stages
 #pragma unroll
-        for (int q = 0; q < 6; ++q)
+        for (int q = 0; q < LOADS; ++q)
             load(0, 0, q);
 #pragma unroll
-        for (int q = 0; q < 6; ++q)
+        for (int q = 0; q < LOADS; ++q)
             load(1, 1, q);
         static_for<16>([&](auto c) { write_chunk(lds, 0, c); });
         lds_barrier();
@@ -220,9 +234,8 @@ void gemm_nvfp4_nt_kernel(Problem p)
             // LDS address bases, hidden from the optimiser again at every step so
             // that the addresses of both stages are formed where they are used
             // instead of all being hoisted out of the loop (which spills)
-            asm volatile("" : "+v"(wpos[0]), "+v"(wpos[1]), "+v"(wpos[2]), "+v"(wpos[3]), "+v"(wpos[4]), "+v"(wpos[5]),
-                         "+v"(wpos[6]), "+v"(wpos[7]), "+v"(kofs[0]), "+v"(kofs[1]), "+v"(kofs[2]), "+v"(kofs[3]),
-                         "+v"(a_row), "+v"(b_row));
+            asm volatile("" : "+v"(wpos[0]), "+v"(wpos[1]), "+v"(wpos[2]), "+v"(wpos[3]), "+v"(kofs[0]),
+                         "+v"(kofs[1]), "+v"(kofs[2]), "+v"(kofs[3]), "+v"(a_row), "+v"(b_row));
             // sub-steps 0..2: fragments of sub-step kk + 1 read during sub-step kk
             static_for<48>([&](auto tc) {
                 constexpr int t = decltype(tc)::value;
@@ -232,7 +245,7 @@ void gemm_nvfp4_nt_kernel(Problem p)
                     read_frag(cur, kk + 1, (kk + 1) & 1, (t & 15) / 2);
                 if constexpr (t % CHUNK_EVERY == 1 && t / CHUNK_EVERY < 16)
                     write_chunk(nxt, set_next, Int<t / CHUNK_EVERY>{});
-                if constexpr (t >= LOAD_AT && (t - LOAD_AT) % 4 == 0 && (t - LOAD_AT) / 4 < 6)
+                if constexpr (t >= LOAD_AT && (t - LOAD_AT) % 4 == 0 && (t - LOAD_AT) / 4 < LOADS)
                     load(kt + 2, set_free, (t - LOAD_AT) / 4);
                 SCHED_VALU_ONLY();
             });
