@@ -9,6 +9,7 @@ The functions mirror the C entry points declared in ``include/gemm355.h``:
     gemm_bf16_nt(M, N, K, A, B, C, stream=None)
     gemm_nvfp4_nt(M, N, K, Aq, SFA, Bq, SFB, C, stream=None)
     force_instance(instance)          # BF16 instance override (diagnostic)
+    force_supergroup(width)           # band width of the tile order (diagnostic)
     bf16_plan(M, N, K, compute_units)  # (instance, splits) gemm_bf16_nt would run
 
 Operands may be torch tensors on a ROCm device (their storage is checked
@@ -72,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.gemm355_schedule.restype = i
     lib.gemm355_force_instance.argtypes = [i]
     lib.gemm355_force_instance.restype = i
+    lib.gemm355_force_supergroup.argtypes = [i]
+    lib.gemm355_force_supergroup.restype = i
     lib.gemm355_bf16_plan.argtypes = [i, i, i, i, p, p]
     lib.gemm355_bf16_plan.restype = i
     _lib = lib
@@ -154,6 +157,12 @@ def force_instance(instance: int) -> None:
     """Force gemm_bf16_nt's kernel instance for the whole process
     (INSTANCE_AUTO, INSTANCE_LARGE, INSTANCE_SMALL or INSTANCE_SPLITK)."""
     _check(load().gemm355_force_instance(instance), "gemm355_force_instance")
+
+
+def force_supergroup(width: int) -> None:
+    """Force the band width of the persistent kernels' supergroup tile order
+    for the whole process (0 = the default)."""
+    _check(load().gemm355_force_supergroup(width), "gemm355_force_supergroup")
 
 
 def bf16_plan(M: int, N: int, K: int, compute_units: int):

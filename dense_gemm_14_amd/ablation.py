@@ -1,0 +1,131 @@
+"""Shape ablations of gemm_bf16_nt on the GPU (measurement tool, not a test).
+
+    python -m dense_gemm_14_amd.ablation instances [--csv FILE]
+    python -m dense_gemm_14_amd.ablation supergroup [--csv FILE]
+
+``instances`` times the three BF16 instances (forced through
+gemm355_force_instance) and the automatic choice on the shape grid
+M, N, K in {1024, 2048, 4096, 8192, 16384} that the NVFP4 page ablates its
+configurations over ("NVFP4 GEMM on Blackwell", "Production Kernel"),
+restricted to shapes with fewer 256 x 256 tiles than 256, plus skinny and mid
+shapes. ``supergroup`` times the band width of the visiting order
+(gemm355_force_supergroup; the page's "Supergroup Size" ablation) on the
+large shapes M, N in {4096, 8192, 16384}, K in {1024, 4096, 16384}.
+
+Every configuration of a shape is timed in three round-robin passes and the
+minimum kept (the first configuration timed on fresh buffers runs slow).
+Operands are standard-normal values rounded to BF16, rotated over enough sets
+to exceed 512 MiB so that they come from HBM, not the last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import sys
+
+import torch
+
+import dense_gemm_14_amd as g
+
+GRID = [1024, 2048, 4096, 8192, 16384]
+EXTRA = [(64, 4096, 8192), (128, 2048, 8192), (256, 1024, 8192), (512, 4096, 8192), (128, 8192, 8192),
+         (128, 8192, 2048), (256, 256, 256), (1992, 2040, 2056), (3072, 3072, 3072), (2560, 2560, 4096),
+         (1536, 1536, 8192)]
+WIDTHS = [1, 2, 4, 8, 16, 32, 64]
+
+
+def _sets(M, N, K):
+    per = 2 * (M * K + N * K + M * N)
+    n = max(1, -(-(600 << 20) // per))
+    return [(torch.randn(M, K, device="cuda").to(torch.bfloat16), torch.randn(N, K, device="cuda").to(torch.bfloat16),
+             torch.empty(M, N, device="cuda", dtype=torch.bfloat16)) for _ in range(n)]
+
+
+def _time_us(M, N, K, sets, target_ms=20.0):
+    n = len(sets)
+    for i in range(2):
+        A, B, C = sets[i % n]
+        g.gemm_bf16_nt(M, N, K, A, B, C)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    A, B, C = sets[0]
+    g.gemm_bf16_nt(M, N, K, A, B, C)
+    e1.record()
+    torch.cuda.synchronize()
+    reps = max(3, min(100, int(target_ms / max(e0.elapsed_time(e1), 1e-3))))
+    e0.record()
+    for i in range(reps):
+        A, B, C = sets[i % n]
+        g.gemm_bf16_nt(M, N, K, A, B, C)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def _run(shape, configs):
+    """Min over three round-robin passes of each (instance, width) config."""
+    M, N, K = shape
+    sets = _sets(M, N, K)
+    best = {}
+    try:
+        for _ in range(3):
+            for inst, width in configs:
+                g.force_instance(inst)
+                g.force_supergroup(width)
+                t = _time_us(M, N, K, sets)
+                best[(inst, width)] = min(best.get((inst, width), float("inf")), t)
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+        g.force_supergroup(0)
+    del sets
+    torch.cuda.empty_cache()
+    return best
+
+
+def instances(csv):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    shapes = [(M, N, K) for M in GRID for N in GRID for K in GRID if -(-M // 256) * -(-N // 256) < 256] + EXTRA
+    worst = 1.0
+    print("#     M      N      K  plan(inst,splits)   auto  i1(256)  i2(64)  i3(128/split)  auto/best   [us]")
+    for shp in shapes:
+        r = _run(shp, [(g.INSTANCE_LARGE, 0), (g.INSTANCE_SMALL, 0), (g.INSTANCE_SPLITK, 0), (g.INSTANCE_AUTO, 0)])
+        best = min(r.values())
+        ratio = r[(0, 0)] / best
+        worst = max(worst, ratio)
+        print("%7d %6d %6d  %-17s %7.1f %8.1f %7.1f %14.1f  %9.3f" % (
+            *shp, g.bf16_plan(*shp, cus), r[(0, 0)], r[(1, 0)], r[(2, 0)], r[(3, 0)], ratio), flush=True)
+        if csv:
+            for (inst, _), us in r.items():
+                csv.write("%d,%d,%d,%d,%.2f\n" % (*shp, inst, us))
+    print("# worst automatic choice / fastest instance: %.3f over %d shapes" % (worst, len(shapes)))
+
+
+def supergroup(csv):
+    L = [4096, 8192, 16384]
+    print("#     M      N      K  " + " ".join("%8s" % ("w=%d" % w) for w in WIDTHS) + "   best  best/w8   [us]")
+    for shp in [(M, N, K) for M in L for N in L for K in (1024, 4096, 16384)]:
+        r = _run(shp, [(g.INSTANCE_LARGE, w) for w in WIDTHS])
+        b = min(r, key=r.get)
+        print("%7d %6d %6d  " % shp + " ".join("%8.1f" % r[(1, w)] for w in WIDTHS) +
+              "  %5d  %7.3f" % (b[1], r[b] / r[(1, 8)]), flush=True)
+        if csv:
+            for (_, w), us in r.items():
+                csv.write("%d,%d,%d,%d,%.2f\n" % (*shp, w, us))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("what", choices=["instances", "supergroup"])
+    ap.add_argument("--csv", default=None, help="also write M,N,K,config,us rows here")
+    args = ap.parse_args(argv)
+    if not torch.cuda.is_available():
+        sys.exit("the ablation needs a GPU")
+    csv = open(args.csv, "w") if args.csv else None
+    try:
+        (instances if args.what == "instances" else supergroup)(csv)
+    finally:
+        if csv:
+            csv.close()
+
+
+if __name__ == "__main__":
+    main()

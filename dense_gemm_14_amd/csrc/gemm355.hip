@@ -25,14 +25,30 @@ using gemm355::Problem;
 constexpr int kMaxDevices = 64;
 constexpr int kSupergroup = 8; // adjacent N tiles per band of the visiting order
 
+// Band width override for measurements (0 = kSupergroup); set through
+// gemm355_force_supergroup.
+std::atomic<int> g_supergroup{0};
+
 // BF16 kernel instance: 0 = chosen by shape, 1 = 256 x 256 tiles, 2 = 64 x 64
 // tiles, 3 = 128 x 128 tiles with split K (set through gemm355_force_instance,
 // for tests and measurements).
 std::atomic<int> g_bf16_instance{0};
 
-// The 256 x 256 kernel needs enough tiles to occupy the compute units; below
-// half of them (128 tiles) the 64 x 64 kernel streams the operands faster.
-constexpr int64_t kSmallTileThreshold = 128;
+// Instance choice for problems with fewer 256 x 256 tiles than half the
+// compute units (with more, the 256 x 256 kernel was the fastest at every
+// shape measured). The smaller instances are compared by an estimate of
+// their time in microseconds: the busiest compute unit's K steps at the
+// measured time of one step of its tile on a busy MI355X, or the operands
+// (plus the split's partials) at a loaded HBM rate, whichever is longer, plus
+// fixed costs, plus the split's reduction. The constants come from an
+// ablation over M, N, K in {1024, 2048, 4096, 8192, 16384} and skinny shapes
+// (M = 64 .. 512, N = 1024 .. 8192, K = 2048 .. 8192); only their ratios
+// decide.
+constexpr double kStep64 = 0.27;        // one K step of a 64 x 64 tile
+constexpr double kStep128 = 0.70;       // one K step of a 128 x 128 tile
+constexpr double kLaunchFixed = 3.0;    // prologue, epilogue, launch
+constexpr double kReduceFixed = 3.0;    // the reduction's own launch
+constexpr double kHbmBytesPerUs = 4.5e6;
 
 std::mutex g_cu_lock;
 int g_cu_count[kMaxDevices];   // 0 = not queried yet
@@ -141,7 +157,8 @@ int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n =
     p.tiles_m = (int)ceil_div(p.M, tile_m);
     p.tiles_n = (int)ceil_div(p.N, tile_n);
     p.tiles = p.tiles_m * p.tiles_n;
-    p.supergroup = kSupergroup;
+    const int sg = g_supergroup.load(std::memory_order_relaxed);
+    p.supergroup = sg > 0 ? sg : kSupergroup;
     p.grid = gemm355::persistent_grid(p.tiles, cus);
     (void)hipGetLastError(); // clear a stale error so the check below is ours
     hipLaunchKernelGGL(kernel, dim3(p.grid), dim3(gemm355::THREADS), 0, static_cast<hipStream_t>(stream), p);
@@ -165,6 +182,30 @@ void splitk_plan(int M, int N, int K, int cus, int *tiles_m, int *tiles_n, int *
     *splits = std::max(1, (int)ceil_div(nk, per));   // no empty split
 }
 
+// Estimated time of the 64 x 64 instance (persistent, one workgroup per unit).
+double estimate_small(int M, int N, int K, int cus)
+{
+    const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
+    const int64_t grid = gemm355::persistent_grid((int)std::min<int64_t>(tiles, 1 << 30), cus);
+    const double steps = double(ceil_div(tiles, grid)) * double(ceil_div(K, 64));
+    const double operands = 2.0 * (double(M) * K + double(N) * K + double(M) * N);
+    return std::max(steps * kStep64, operands / kHbmBytesPerUs) + kLaunchFixed;
+}
+
+// Estimated time of the 128 x 128 split-K instance (one workgroup per work
+// item and unit), its reduction included when there is more than one split.
+double estimate_split(int M, int N, int K, int cus, int tiles_m, int tiles_n, int splits, int per)
+{
+    const int64_t items = int64_t(tiles_m) * tiles_n * splits;
+    const double steps = double(ceil_div(items, cus)) * per;
+    const double operands = 2.0 * (double(M) * K + double(N) * K + double(M) * N);
+    const double partials = splits > 1 ? 4.0 * double(M) * N * splits : 0.0;
+    double t = std::max(steps * kStep128, (operands + partials) / kHbmBytesPerUs) + kLaunchFixed;
+    if (splits > 1)
+        t += kReduceFixed + (partials + 2.0 * double(M) * N) / kHbmBytesPerUs;
+    return t;
+}
+
 // The BF16 instance for a problem (forced: 0 = by shape, else 1..3) and, for
 // instance 3, the number of K splits. Pure host arithmetic.
 int choose_bf16_instance(int M, int N, int K, int cus, int forced, int *splits)
@@ -174,22 +215,8 @@ int choose_bf16_instance(int M, int N, int K, int cus, int forced, int *splits)
     int instance = forced;
     if (instance == 0) {
         instance = 1;
-        if (ceil_div(M, BM) * ceil_div(N, BN) < kSmallTileThreshold) {
-            // Few output tiles: the time goes into streaming operands. Take
-            // the split when its busiest compute unit moves fewer bytes (a
-            // 64 x 64 tile streams 128 rows over all of K, a split work item
-            // 256 rows over its K range plus a 64 KiB partial tile), except
-            // when the 64 x 64 tiles fill the units in exactly one round:
-            // there both are bound by the copies in flight per unit over the
-            // memory's loaded latency, and the split's partials and second
-            // kernel cost more than its fewer bytes save (measured).
-            const int64_t tiles64 = ceil_div(M, 64) * ceil_div(N, 64);
-            const int64_t bytes64 = ceil_div(tiles64, cus) * 128 * int64_t(K) * 2;
-            const int64_t items = int64_t(tmn) * tnn * *splits;
-            const int64_t bytes_split = ceil_div(items, cus) * (256 * int64_t(per) * 64 * 2 + 65536);
-            const bool one_round = tiles64 >= cus && tiles64 < 2 * int64_t(cus);
-            instance = !one_round && *splits >= 2 && bytes_split < bytes64 ? 3 : 2;
-        }
+        if (2 * ceil_div(M, BM) * ceil_div(N, BN) < cus)
+            instance = estimate_small(M, N, K, cus) <= estimate_split(M, N, K, cus, tmn, tnn, *splits, per) ? 2 : 3;
     }
     if (instance == 1 && K <= 3 * gemm355::bf16::BK)
         instance = 2;   // the 256 x 256 kernel runs its tiles back to back and needs K > 192
@@ -199,7 +226,8 @@ int choose_bf16_instance(int M, int N, int K, int cus, int forced, int *splits)
 }
 
 // Split-K instance: partial tiles into a stream-ordered workspace, then the
-// reduction into C, both on `stream`.
+// reduction into C, both on `stream`; with one split the tiles go straight to
+// C and neither the workspace nor the reduction is used.
 int launch_splitk(const Problem &p, void *stream)
 {
     namespace sk = gemm355::bf16_splitk;
@@ -219,16 +247,20 @@ int launch_splitk(const Problem &p, void *stream)
     if (items > (int64_t(1) << 30))
         return GEMM355_ERR_UNSUPPORTED;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    void *ws = nullptr;
-    rc = stream_workspace(s, size_t(items) * sk::TILE_FLOATS * sizeof(float), &ws);
-    if (rc != GEMM355_OK)
-        return rc;
-    sp.ws = static_cast<float *>(ws);
+    if (sp.splits > 1) {
+        void *ws = nullptr;
+        rc = stream_workspace(s, size_t(items) * sk::TILE_FLOATS * sizeof(float), &ws);
+        if (rc != GEMM355_OK)
+            return rc;
+        sp.ws = static_cast<float *>(ws);
+    }
     (void)hipGetLastError(); // clear a stale error so the check below is ours
     hipLaunchKernelGGL(sk::gemm_bf16_nt_splitk_kernel, dim3((unsigned)items), dim3(gemm355::THREADS), 0, s, sp);
-    const int64_t outs = int64_t(p.M) * (p.N / 8);
-    hipLaunchKernelGGL(sk::splitk_reduce_kernel, dim3((unsigned)ceil_div(outs, sk::REDUCE_THREADS)),
-                       dim3(sk::REDUCE_THREADS), 0, s, sp);
+    if (sp.splits > 1) {   // one split stores C itself
+        const int64_t outs = int64_t(p.M) * (p.N / 8);
+        hipLaunchKernelGGL(sk::splitk_reduce_kernel, dim3((unsigned)ceil_div(outs, sk::REDUCE_THREADS)),
+                           dim3(sk::REDUCE_THREADS), 0, s, sp);
+    }
     return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 
@@ -286,6 +318,14 @@ extern "C" int gemm355_force_instance(int instance)
     if (instance < 0 || instance > 3)
         return GEMM355_ERR_INVALID_ARG;
     g_bf16_instance.store(instance, std::memory_order_relaxed);
+    return GEMM355_OK;
+}
+
+extern "C" int gemm355_force_supergroup(int supergroup)
+{
+    if (supergroup < 0 || supergroup > 4096)
+        return GEMM355_ERR_INVALID_ARG;
+    g_supergroup.store(supergroup, std::memory_order_relaxed);
     return GEMM355_OK;
 }
 

@@ -57,7 +57,7 @@ static_assert(COPIES * (B_STAGES - 1) <= 63, "vmcnt counts at most 63 outstandin
 // Kernel arguments. Work item w = tile * splits + split; tile = tm * tiles_n + tn.
 struct SplitProblem {
     const void *a, *b;
-    float *ws;          // partial tiles, [tiles][splits][TM][TN] FP32, row-major
+    float *ws;          // partial tiles, [tiles][splits][TM][TN] FP32, row-major (unused with one split)
     void *c;
     int M, N, K;
     int tiles_m, tiles_n;
@@ -69,6 +69,7 @@ __device__ inline int swizzle(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline i32x4 rsrc_words(const void *p, unsigned bytes)
 {
@@ -255,16 +256,32 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
             step(ls, Int<1>{}, false);
     }
 
-    // Partial tile: lane (l16, grp) of block (i, j) holds row 64 wm + 16 i +
-    // l16, columns 64 wn + 16 j + 4 grp .. + 3 of the tile.
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws + (size_t)item * TILE_FLOATS, TILE_FLOATS * 4u);
+    // Lane (l16, grp) of block (i, j) holds row 64 wm + 16 i + l16, columns
+    // 64 wn + 16 j + 4 grp .. + 3 of the tile.
+    if (p.splits == 1) {
+        // One split: the tile is final; round to BF16 and store it into C
+        // (8 bytes per lane and block; rows past M and columns past N masked,
+        // N % 8 == 0 so a lane's 4 columns are all inside or all outside).
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 64 * wm + 16 * i + l16, c = 64 * wn + 16 * j + 4 * grp;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw, (r * TN + c) * 4, 0, 0);
-        }
+            for (int j = 0; j < 4; ++j) {
+                const int m = tm * TM + 64 * wm + 16 * i + l16, n = tn * TN + 64 * wn + 16 * j + 4 * grp;
+                const int off = (m < p.M && n < p.N) ? (m * p.N + n) * 2 : OOB;
+                const u32x2 v = {pack_bf16(acc[i][j][0], acc[i][j][1]), pack_bf16(acc[i][j][2], acc[i][j][3])};
+                __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
+            }
+    } else {
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws + (size_t)item * TILE_FLOATS, TILE_FLOATS * 4u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 64 * wm + 16 * i + l16, c = 64 * wn + 16 * j + 4 * grp;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw, (r * TN + c) * 4, 0, 0);
+            }
+    }
     wait_reads();
     wait_all_copies(); // no copy may still be writing LDS when the workgroup ends
 }

@@ -62,14 +62,15 @@ typedef enum gemm355_status {
  * K % 8 == 0 and N % 8 == 0 (whole 16-byte row segments); every operand,
  * padded up to a multiple of 256 rows, spans less than 2^31 bytes.
  * Three kernel instances compute it: 256 x 256 output tiles; or, when the
- * 256 x 256 tiling has fewer than 128 tiles (too few to occupy the compute
- * units: a problem then bound by operand traffic), either 64 x 64 tiles or
- * 128 x 128 tiles whose K range is split over 2 to 8 workgroups (at least 8
- * steps of 64 each) writing FP32 partial tiles that a second kernel on the
- * same stream adds in split order and rounds once to BF16 -- the split when
- * its busiest compute unit moves fewer bytes, unless the 64 x 64 tiles fill
- * the compute units in exactly one round (as for M = 128, N = K = 8192);
- * whenever K <= 192, 64 x 64 tiles. gemm355_bf16_plan reports the choice.
+ * 256 x 256 tiling has fewer tiles than half the compute units, either
+ * 64 x 64 tiles or 128 x 128 tiles whose K range may be split over up to 8
+ * workgroups (at least 8 steps of 64 each) writing FP32 partial tiles that a
+ * second kernel on the same stream adds in split order and rounds once to
+ * BF16 (with one split the tiles are stored directly) -- whichever has the
+ * shorter estimated time (the busiest compute unit's K steps at a measured
+ * cost per step, or the operand and partial traffic at a loaded HBM rate,
+ * plus fixed costs); whenever K <= 192, not 256 x 256 tiles.
+ * gemm355_bf16_plan reports the choice.
  * The split's partials live in one workspace per (device, stream), which only
  * work enqueued on that stream uses; it comes from a memory pool of the
  * library's own, grows by stream-ordered allocation, and is kept until the
@@ -87,13 +88,30 @@ int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, voi
  * A diagnostic for tests and measurements (it is not defined by the pages):
  * instance 0 restores the choice by shape, 1 forces 256 x 256 tiles (except
  * for K <= 192, which always takes the 64 x 64 instance), 2 forces 64 x 64
- * tiles, 3 forces 128 x 128 tiles with split K (one split when K is too
- * short for two), for every later gemm_bf16_nt call in the process. Returns
+ * tiles, 3 forces 128 x 128 tiles with split K (as many splits as give every
+ * compute unit a work item, at most 8, each at least 8 steps of 64; one
+ * split when K is too short for two or the tiles alone fill the units), for
+ * every later gemm_bf16_nt call in the process. Returns
  * GEMM355_OK, or GEMM355_ERR_INVALID_ARG for any other value (the setting is
  * then unchanged). Calls racing with gemm_bf16_nt on other threads see either
  * the old or the new setting. No HIP call is made.
  */
 int gemm355_force_instance(int instance);
+
+/*
+ * gemm355_force_supergroup -- override the band width of the supergroup
+ * visiting order ("NVFP4 GEMM on Blackwell", section "Supergroup Size": the
+ * pages ablate this width per shape) used by the persistent kernels of
+ * gemm_bf16_nt and gemm_nvfp4_nt.
+ *
+ * A diagnostic for measurements: 0 restores the default (8 adjacent N tiles
+ * per band), 1..4096 forces that width for every later launch in the process.
+ * The result of a product does not depend on it (every tile is computed the
+ * same way, only the order changes). Returns GEMM355_OK, or
+ * GEMM355_ERR_INVALID_ARG for any other value (the setting is then
+ * unchanged). No HIP call is made.
+ */
+int gemm355_force_supergroup(int supergroup);
 
 /*
  * gemm355_bf16_plan -- the instance gemm_bf16_nt would run for M x N x K on

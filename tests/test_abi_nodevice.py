@@ -123,11 +123,20 @@ def test_force_instance_accepts_only_known_instances():
         assert lib.gemm355_force_instance(ok) == g.OK
 
 
+def test_force_supergroup_range():
+    lib = g.load()
+    for bad in (-1, 4097):
+        assert lib.gemm355_force_supergroup(bad) == g.ERR_INVALID_ARG
+    for ok in (1, 4, 4096, 0):
+        assert lib.gemm355_force_supergroup(ok) == g.OK
+
+
 def test_bf16_plan_for_the_workload_shapes():
     # 256 compute units: the square workloads take 256 x 256 tiles, the small
     # one 64 x 64 tiles; the skinny one (M = 128) has exactly one round of 256
     # tiles of 64 x 64, where that instance beats splitting K (measured).
     g.force_instance(g.INSTANCE_AUTO)
+    g.force_supergroup(0)
     assert g.bf16_plan(8192, 8192, 8192, 256) == (g.INSTANCE_LARGE, 1)
     assert g.bf16_plan(8000, 8000, 8000, 256) == (g.INSTANCE_LARGE, 1)
     assert g.bf16_plan(4096, 4096, 4096, 256) == (g.INSTANCE_LARGE, 1)
@@ -138,16 +147,27 @@ def test_bf16_plan_for_the_workload_shapes():
     assert g.bf16_plan(512, 4096, 8192, 256) == (g.INSTANCE_SPLITK, 2)
     # short K: nothing to split
     assert g.bf16_plan(128, 8192, 2048, 256) == (g.INSTANCE_SMALL, 1)
+    # mid shapes with a quarter of the units' worth of 256 x 256 tiles: one
+    # round of 128 x 128 tiles, stored directly (measured 27 us against 42 us
+    # for 64 x 64 tiles and 46 us for 256 x 256 ones at 2048^3)
+    assert g.bf16_plan(2048, 2048, 2048, 256) == (g.INSTANCE_SPLITK, 1)
+    assert g.bf16_plan(1024, 4096, 8192, 256) == (g.INSTANCE_SPLITK, 1)
+    # small square problems: 64 x 64 tiles at short K, split K at long K
+    assert g.bf16_plan(1024, 1024, 1024, 256) == (g.INSTANCE_SMALL, 1)
+    assert g.bf16_plan(1024, 1024, 16384, 256) == (g.INSTANCE_SPLITK, 4)
+    # half the units' worth of 256 x 256 tiles or more: that instance
+    assert g.bf16_plan(1024, 8192, 1024, 256) == (g.INSTANCE_LARGE, 1)
+    assert g.bf16_plan(3072, 3072, 3072, 256) == (g.INSTANCE_LARGE, 1)
     # K too short for the 256 x 256 instance's four kinds of step
     assert g.bf16_plan(4096, 4096, 192, 256) == (g.INSTANCE_SMALL, 1)
     assert g.bf16_plan(4096, 4096, 200, 256)[0] == g.INSTANCE_LARGE
     # splitting never makes a split shorter than 8 steps of 64, or empty
-    for M, N, K in [(128, 1032, 4104), (64, 64, 4104), (512, 4096, 8192), (128, 2048, 520)]:
+    for M, N, K in [(128, 1032, 4104), (64, 64, 4104), (512, 4096, 8192), (128, 2048, 520), (2048, 2048, 2048)]:
         inst, splits = g.bf16_plan(M, N, K, 256)
-        if inst == g.INSTANCE_SPLITK:
+        if inst == g.INSTANCE_SPLITK and splits > 1:
             steps = -(-K // 64)
             per = -(-steps // splits)
-            assert 2 <= splits <= 8 and per >= 8 and (splits - 1) * per < steps, (M, N, K, splits)
+            assert splits <= 8 and per >= 8 and (splits - 1) * per < steps, (M, N, K, splits)
 
 
 def test_bf16_plan_follows_the_forced_instance_and_checks_arguments():

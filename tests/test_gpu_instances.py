@@ -1,5 +1,6 @@
 """The three BF16 kernel instances (256 x 256 output tiles, 64 x 64 tiles, and
-128 x 128 tiles with split K and a reduction of FP32 partials), each forced
+128 x 128 tiles with split K and a reduction of FP32 partials, or a direct
+store when there is one split), each forced
 through gemm355_force_instance, against the oracle: ragged shapes element by
 element, exactly summable inputs bitwise, K = 0, and B = I bitwise. The
 automatic choice routes small and skinny problems away from the 256 x 256
@@ -141,6 +142,25 @@ def test_splitk_many_splits_exact_every_element():
     C = run_bf16(A, B, M, N, K)
     want = oracle.bf16_from_double(tolerance.bf16_bits_to_f64(A) @ tolerance.bf16_bits_to_f64(B).T)
     assert np.array_equal(oracle.gemm_bf16_nt(A[:3], B), want[:3])
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 2048), (1992, 2040, 2056)])
+def test_single_split_direct_store_exact_every_element(M, N, K):
+    # A quarter of the units' worth of 256 x 256 tiles: the automatic plan
+    # runs one round of 128 x 128 tiles with one split each, which store C
+    # directly (no partials, no reduction). Ragged M and N at the second shape;
+    # multiples of 1/16 make the answer unique, so every element is compared.
+    need_gpu()
+    g.force_instance(g.INSTANCE_AUTO)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert g.bf16_plan(M, N, K, cus) == (g.INSTANCE_SPLITK, 1)
+    A = syn.bf16_sixteenths(M, K, seed=M + 7)
+    B = syn.bf16_sixteenths(N, K, seed=N + 8)
+    C = run_bf16(A, B, M, N, K)
+    want = oracle.bf16_from_double(tolerance.bf16_bits_to_f64(A) @ tolerance.bf16_bits_to_f64(B).T)
+    assert np.array_equal(oracle.gemm_bf16_nt(A[:2], B), want[:2])
     bad = np.argwhere(C != want)
     assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
 
