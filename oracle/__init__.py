@@ -16,7 +16,9 @@ What is computed (cited passages):
   * output rounding to nearest, ties to even ("Optimized B200 Matrix
     Multiplication", section 5 "The Epilogue");
   * block-scaled FP4: E2M1 values with one FP8 scale per 16 elements
-    ("NVFP4 GEMM on Blackwell", section "NVFP4 Datatype").
+    ("NVFP4 GEMM on Blackwell", section "NVFP4 Datatype");
+  * a fused epilogue, bias and activation applied to the sum before rounding
+    ("NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue Warps").
 """
 from __future__ import annotations
 
@@ -77,6 +79,12 @@ def _bind(lib):
     lib.oracle_gemm_bf16_nt_at.restype = i
     lib.oracle_gemm_nvfp4_nt_at.argtypes = [i, i, i, p, p, p, p, ctypes.c_long, p, p, p, p]
     lib.oracle_gemm_nvfp4_nt_at.restype = i
+    lib.oracle_activate.argtypes = [ctypes.c_double, i]
+    lib.oracle_activate.restype = ctypes.c_double
+    lib.oracle_gemm_bf16_nt_bias_act.argtypes = [i, i, i, p, p, p, i, p]
+    lib.oracle_gemm_bf16_nt_bias_act.restype = i
+    lib.oracle_gemm_bf16_nt_bias_act_at.argtypes = [i, i, i, p, p, p, i, ctypes.c_long, p, p, p, p]
+    lib.oracle_gemm_bf16_nt_bias_act_at.restype = i
     lib.oracle_decode_nvfp4.argtypes = [i, i, p, p, p]
     lib.oracle_decode_nvfp4.restype = i
     lib.oracle_max_threads.argtypes = []
@@ -186,6 +194,57 @@ def gemm_nvfp4_nt(Aq, SFA, Bq, SFB, K: int) -> np.ndarray:
     _check(lib.oracle_gemm_nvfp4_nt(M, N, K, _ptr(Aq), _ptr(SFA), _ptr(Bq), _ptr(SFB), _ptr(C)),
            "gemm_nvfp4_nt")
     return C
+
+
+ACT_NONE, ACT_RELU, ACT_GELU_TANH = 0, 1, 2
+
+
+def activate(z: float, act: int) -> float:
+    """The fused epilogue's activation of one binary64 value."""
+    return _load().oracle_activate(float(z), int(act))
+
+
+def _bias(bias, N):
+    if bias is None:
+        return None
+    bias = _c(bias, np.uint16)
+    if bias.shape != (N,):
+        raise ValueError("bias must hold N = %d BF16 values" % N)
+    return bias
+
+
+def gemm_bf16_nt_bias_act(A: np.ndarray, B: np.ndarray, bias, act: int) -> np.ndarray:
+    """C = bf16(act(A @ B^T + bias)) for BF16 bit arrays; bias (N,) or None."""
+    lib = _load()
+    A = _c(A, np.uint16)
+    B = _c(B, np.uint16)
+    M, K = A.shape
+    N, K2 = B.shape
+    if K != K2:
+        raise ValueError("K mismatch")
+    bias = _bias(bias, N)
+    C = np.empty((M, N), dtype=np.uint16)
+    _check(lib.oracle_gemm_bf16_nt_bias_act(M, N, K, _ptr(A), _ptr(B), _ptr(bias) if bias is not None else None,
+                                            int(act), _ptr(C)), "gemm_bf16_nt_bias_act")
+    return C
+
+
+def gemm_bf16_nt_bias_act_at(A, B, bias, act: int, ms, ns, with_z: bool = False):
+    """Only the elements C[ms[i], ns[i]] (and optionally z before the activation)."""
+    lib = _load()
+    A = _c(A, np.uint16)
+    B = _c(B, np.uint16)
+    M, K = A.shape
+    N = B.shape[0]
+    bias = _bias(bias, N)
+    ms, ns = _idx(ms, ns)
+    out = np.empty(ms.size, dtype=np.uint16)
+    zs = np.empty(ms.size, dtype=np.float64)
+    _check(lib.oracle_gemm_bf16_nt_bias_act_at(M, N, K, _ptr(A), _ptr(B),
+                                               _ptr(bias) if bias is not None else None, int(act), ms.size,
+                                               _ptr(ms), _ptr(ns), _ptr(out), _ptr(zs)),
+           "gemm_bf16_nt_bias_act_at")
+    return (out, zs) if with_z else out
 
 
 def _shape_fp4(Q, SF, rows, K):

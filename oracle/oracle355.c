@@ -38,6 +38,7 @@
  * element is still summed by one thread in ascending k, so the result does
  * not depend on the thread count.
  */
+#define _GNU_SOURCE /* M_PI */
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -228,6 +229,67 @@ int oracle_gemm_nvfp4_nt_at(int M, int N, int K, const uint8_t *Aq, const uint8_
         out_bf16[i] = oracle_bf16_from_double(s);
         if (out_sum)
             out_sum[i] = s;
+    }
+    return ORACLE_OK;
+}
+
+/* ---- fused epilogue -----------------------------------------------------
+ * An element-wise step applied to the sum before the output rounding ("NVFP4
+ * GEMM on Blackwell", "Kernel 1", "Epilogue Warps": the epilogue is where
+ * activation functions and other element-wise operations would be fused).
+ * The pages name no particular operation; the one computed here is the common
+ * linear-layer epilogue, all in binary64:
+ *
+ *     z = sum_k a(m,k) b(n,k) + bias[n]        (bias NULL: no term)
+ *     C[m][n] = bf16_round_nearest_even( act(z) )
+ *
+ * act 0: z; act 1 (ReLU): max(z, 0); act 2 (GELU, tanh form, the published
+ * approximation of Hendrycks and Gimpel): z/2 (1 + tanh(sqrt(2/pi) (z +
+ * 0.044715 z^3))). */
+
+double oracle_activate(double z, int act)
+{
+    if (act == 1)
+        return z > 0.0 ? z : 0.0;
+    if (act == 2)
+        return 0.5 * z * (1.0 + tanh(sqrt(2.0 / M_PI) * (z + 0.044715 * z * z * z)));
+    return z;
+}
+
+static double bias_at(const uint16_t *bias, long n)
+{
+    return bias ? oracle_bf16_to_double(bias[n]) : 0.0;
+}
+
+int oracle_gemm_bf16_nt_bias_act(int M, int N, int K, const uint16_t *A, const uint16_t *B,
+                                 const uint16_t *bias, int act, uint16_t *C)
+{
+    if (M < 0 || N < 0 || K < 0 || act < 0 || act > 2)
+        return ORACLE_BAD_ARGS;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long m = 0; m < M; ++m)
+        for (long n = 0; n < N; ++n)
+            C[m * (long)N + n] =
+                oracle_bf16_from_double(oracle_activate(dot_bf16(A, B, K, m, n) + bias_at(bias, n), act));
+    return ORACLE_OK;
+}
+
+/* Chosen elements only; out_z (may be NULL) gets z before the activation. */
+int oracle_gemm_bf16_nt_bias_act_at(int M, int N, int K, const uint16_t *A, const uint16_t *B,
+                                    const uint16_t *bias, int act, long count, const int32_t *ms,
+                                    const int32_t *ns, uint16_t *out_bf16, double *out_z)
+{
+    if (M < 0 || N < 0 || K < 0 || act < 0 || act > 2 || count < 0)
+        return ORACLE_BAD_ARGS;
+    for (long i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N)
+            return ORACLE_BAD_ARGS;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long i = 0; i < count; ++i) {
+        const double z = dot_bf16(A, B, K, ms[i], ns[i]) + bias_at(bias, ns[i]);
+        out_bf16[i] = oracle_bf16_from_double(oracle_activate(z, act));
+        if (out_z)
+            out_z[i] = z;
     }
     return ORACLE_OK;
 }
