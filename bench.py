@@ -45,25 +45,31 @@ WORKLOADS = {
     "bf16_skinny": ("bf16", 128, 8192, 8192),
     "bf16_256": ("bf16", 256, 256, 256),
     "fp4_8192": ("fp4", 8192, 8192, 8192),
+    # the same product with the fused epilogue: C = gelu(A B^T + bias)
+    "bf16_gelu_8192": ("bf16_gelu", 8192, 8192, 8192),
 }
 CONFIG_INDEX = {"bf16_256": 0, "bf16_4096": 1, "bf16_8192": 2, "bf16_8000": 3, "bf16_skinny": 3,
-                "fp4_8192": 4}
-KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel",
-               "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel",
-               "bf16_splitk": "gemm355::bf16_splitk::gemm_bf16_nt_splitk_kernel",
-               "bf16_splitk_reduce": "gemm355::bf16_splitk::splitk_reduce_kernel"}
+                "fp4_8192": 4, "bf16_gelu_8192": 2}
+# BF16 kernels are templates over the epilogue: -1 plain, 2 bias + tanh-form GELU
+KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel<%d>", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel",
+               "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel<%d>",
+               "bf16_splitk": "gemm355::bf16_splitk::gemm_bf16_nt_splitk_kernel<%d>",
+               "bf16_splitk_reduce": "gemm355::bf16_splitk::splitk_reduce_kernel<%d>"}
+EPILOGUE = {"bf16": -1, "bf16_gelu": 2}
 
 
 def kernels_for(kind: str, M: int, N: int, K: int, compute_units: int = 256) -> list:
-    """The kernels gemm_bf16_nt / gemm_nvfp4_nt launches for this shape, in
-    launch order (the library's own choice, gemm355_bf16_plan)."""
-    if kind != "bf16":
+    """The kernels gemm_bf16_nt / gemm_bf16_nt_bias_act / gemm_nvfp4_nt launch
+    for this shape, in launch order (the library's own choice, gemm355_bf16_plan)."""
+    if kind == "fp4":
         return [KERNEL_NAME[kind]]
     import dense_gemm_14_amd as g
-    instance, _ = g.bf16_plan(M, N, K, compute_units)
+    instance, splits = g.bf16_plan(M, N, K, compute_units)
+    epi = EPILOGUE[kind]
     if instance == 3:
-        return [KERNEL_NAME["bf16_splitk"], KERNEL_NAME["bf16_splitk_reduce"]]
-    return [KERNEL_NAME["bf16_small" if instance == 2 else "bf16"]]
+        names = [KERNEL_NAME["bf16_splitk"] % epi]
+        return names + [KERNEL_NAME["bf16_splitk_reduce"] % epi] if splits > 1 else names
+    return [KERNEL_NAME["bf16_small" if instance == 2 else "bf16"] % epi]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -81,6 +87,8 @@ def kernel_source_hash() -> str:
 def set_bytes(kind, M, N, K):
     if kind == "bf16":
         return 2 * (M * K + N * K + M * N)
+    if kind == "bf16_gelu":
+        return 2 * (M * K + N * K + M * N + N)   # plus the bias
     return M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + 2 * M * N
 
 
@@ -96,10 +104,13 @@ def make_sets(kind, M, N, K, n_sets, cfg):
     sets = []
     for s in range(n_sets):
         seed = syn.seed_for(cfg, s)
-        if kind == "bf16":
+        if kind in ("bf16", "bf16_gelu"):
             A = torch.from_numpy(syn.bf16_uniform(M, K, seed).view(np.int16)).cuda()
             B = torch.from_numpy(syn.bf16_uniform(N, K, seed + 500).view(np.int16)).cuda()
             ops = (A, B)
+            if kind == "bf16_gelu":   # bias on the scale of the sums (sqrt(K / 9) = 30)
+                bias = syn.bf16_uniform(1, N, seed + 900, lo=-32.0, hi=32.0)[0]
+                ops = (A, B, torch.from_numpy(bias.view(np.int16)).cuda())
         else:
             Aq, SFA = syn.fp4_operand(M, K, seed)
             Bq, SFB = syn.fp4_operand(N, K, seed + 500)
@@ -113,6 +124,9 @@ def launcher(kind, M, N, K, stream):
     import dense_gemm_14_amd as g
     if kind == "bf16":
         return lambda ops, C: g.gemm_bf16_nt(M, N, K, ops[0], ops[1], C, stream=stream)
+    if kind == "bf16_gelu":
+        return lambda ops, C: g.gemm_bf16_nt_bias_act(M, N, K, ops[0], ops[1], ops[2], g.ACT_GELU_TANH, C,
+                                                      stream=stream)
     return lambda ops, C: g.gemm_nvfp4_nt(M, N, K, *ops, C, stream=stream)
 
 
@@ -145,6 +159,9 @@ def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
     if kind == "bf16":
         A, B = (h.view(np.uint16) for h in host)
         fn = lambda ms, ns: oracle.gemm_bf16_nt_at(A, B, ms, ns)
+    elif kind == "bf16_gelu":
+        A, B, bias = (h.view(np.uint16) for h in host)
+        fn = lambda ms, ns: oracle.gemm_bf16_nt_bias_act_at(A, B, bias, oracle.ACT_GELU_TANH, ms, ns, with_z=True)
     else:
         Aq, SFA, Bq, SFB = host
         fn = lambda ms, ns: oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns)
@@ -161,6 +178,8 @@ def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
     t0 = time.perf_counter()
     ref = fn(ms, ns)
     dt = time.perf_counter() - t0
+    if kind == "bf16_gelu":
+        ref, z = ref
     # the same sample doubles as a spot check of the GPU output of set 0
     got = C.cpu().numpy().view(np.uint16).reshape(M, N)[ms, ns]
     sigma = 1.0
@@ -168,7 +187,10 @@ def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
         sub = slice(0, min(M, 256))
         sigma = (tolerance.sigma_of(oracle.decode_nvfp4(host[0][sub], host[1][sub], K)) *
                  tolerance.sigma_of(oracle.decode_nvfp4(host[2][sub], host[3][sub], K)))
-    chk = tolerance.check(got, ref, K, sigma)
+    if kind == "bf16_gelu":
+        chk = tolerance.check_fused(got, ref, z, K, oracle.ACT_GELU_TANH)
+    else:
+        chk = tolerance.check(got, ref, K, sigma)
     return {
         "value": 2.0 * n * K / dt / 1e12,
         "unit": "TFLOP/s",
@@ -249,7 +271,7 @@ def main(argv=None):
     run(*sets[0])
     torch.cuda.synchronize()
 
-    dtype = "bf16" if kind == "bf16" else "fp16"  # FP4 operands are decoded to FP16 for the MFMA
+    dtype = "fp16" if kind == "fp4" else "bf16"  # FP4 operands are decoded to FP16 for the MFMA
     traffic = read_traffic(args.workload, flops)
     alg_bytes = algorithmic_bytes(kind, M, N, K)
     ridge = PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
@@ -265,7 +287,9 @@ def main(argv=None):
                      "algorithmic_bytes": alg_bytes, "mean_launch_ms": round(ms_step, 5)})
     out = {
         "metric": "TFLOP/s for BF16 C=A·B^T at M=N=K=8192; % of MI355X dense BF16 peak"
-        if args.workload == "bf16_8192" else "TFLOP/s for %s C=A·B^T at %dx%dx%d" % (kind, M, N, K),
+        if args.workload == "bf16_8192" else
+        "TFLOP/s for bf16 C=gelu_tanh(A·B^T+bias) at %dx%dx%d" % (M, N, K) if kind == "bf16_gelu" else
+        "TFLOP/s for %s C=A·B^T at %dx%dx%d" % (kind, M, N, K),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -275,7 +299,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if kind == "bf16" else "fp4(e2m1+e4m3)->fp16",
+        "dtype": "fp4(e2m1+e4m3)->fp16" if kind == "fp4" else "bf16",
         "data": "synthetic",
         "config": {"workload": "%s_nt_%dx%dx%d" % (kind, M, N, K), "M": M, "N": N, "K": K,
                    "rotation_sets": n_sets, "footprint_MiB": round(n_sets * per_set / 2 ** 20, 1),

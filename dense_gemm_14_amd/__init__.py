@@ -7,6 +7,7 @@ cannot be loaded, every call raises.
 The functions mirror the C entry points declared in ``include/gemm355.h``:
 
     gemm_bf16_nt(M, N, K, A, B, C, stream=None)
+    gemm_bf16_nt_bias_act(M, N, K, A, B, bias, activation, C, stream=None)
     gemm_nvfp4_nt(M, N, K, Aq, SFA, Bq, SFB, C, stream=None)
     force_instance(instance)          # BF16 instance override (diagnostic)
     force_supergroup(width)           # band width of the tile order (diagnostic)
@@ -33,6 +34,10 @@ ERR_INVALID_ARG = 1
 ERR_UNSUPPORTED = 2
 ERR_NO_DEVICE = 3
 ERR_LAUNCH = 4
+
+ACT_NONE = 0         # fused epilogue activations (gemm_bf16_nt_bias_act)
+ACT_RELU = 1
+ACT_GELU_TANH = 2
 
 INSTANCE_AUTO = 0    # gemm_bf16_nt picks the instance by shape
 INSTANCE_LARGE = 1   # 256 x 256 output tiles
@@ -63,6 +68,8 @@ def load() -> ctypes.CDLL:
     p, i = ctypes.c_void_p, ctypes.c_int
     lib.gemm_bf16_nt.argtypes = [i, i, i, p, p, p, p]
     lib.gemm_bf16_nt.restype = i
+    lib.gemm_bf16_nt_bias_act.argtypes = [i, i, i, p, p, p, i, p, p]
+    lib.gemm_bf16_nt_bias_act.restype = i
     lib.gemm_nvfp4_nt.argtypes = [i, i, i, p, p, p, p, p, p]
     lib.gemm_nvfp4_nt.restype = i
     lib.gemm355_status_string.argtypes = [i]
@@ -138,6 +145,20 @@ def gemm_bf16_nt(M: int, N: int, K: int, A, B, C, stream=None) -> None:
     b = _addr(B, N * K * 2 if nz else 0, "B")
     c = _addr(C, M * N * 2 if nz else 0, "C")
     _check(lib.gemm_bf16_nt(M, N, K, a, b, c, _stream(stream)), "gemm_bf16_nt")
+
+
+def gemm_bf16_nt_bias_act(M: int, N: int, K: int, A, B, bias, activation: int, C, stream=None) -> None:
+    """C = act(A @ B^T + bias), bias (N BF16 values, or None) and activation
+    (ACT_NONE, ACT_RELU, ACT_GELU_TANH) applied in the kernels' epilogue."""
+    lib = load()
+    M, N, K = int(M), int(N), int(K)
+    nz = M > 0 and N > 0
+    a = _addr(A, M * K * 2 if nz else 0, "A")
+    b = _addr(B, N * K * 2 if nz else 0, "B")
+    bb = _addr(bias, N * 2 if nz else 0, "bias")
+    c = _addr(C, M * N * 2 if nz else 0, "C")
+    _check(lib.gemm_bf16_nt_bias_act(M, N, K, a, b, bb, int(activation), c, _stream(stream)),
+           "gemm_bf16_nt_bias_act")
 
 
 def gemm_nvfp4_nt(M: int, N: int, K: int, Aq, SFA, Bq, SFB, C, stream=None) -> None:

@@ -25,8 +25,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256;                      // output tile rows (M)
 constexpr int BN = 256;                      // output tile columns (N)
@@ -40,11 +42,57 @@ struct Problem {
     const void *sfa;  // E4M3 scales of A (FP4 only)
     const void *sfb;  // E4M3 scales of B (FP4 only)
     void *c;
+    const void *bias; // fused epilogue only: N BF16 values, or NULL (zeros)
     int M, N, K;
     int tiles_m, tiles_n, tiles;
     int supergroup;
     int grid;
 };
+
+// ---- fused epilogue --------------------------------------------------------
+//
+// An element-wise step applied to the FP32 accumulator before it is rounded
+// to BF16, while it still sits in registers ("NVFP4 GEMM on Blackwell",
+// "Kernel 1", "Epilogue Warps": the epilogue is where activations and other
+// element-wise operations would be fused): z = acc + bias[n] in FP32, then
+// the activation in FP32.
+enum Activation { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2 };
+// Kernel template argument EPI: EPI_PLAIN (no fused epilogue: C = the rounded
+// sum), or the Activation of the fused epilogue (bias added in every case).
+constexpr int EPI_PLAIN = -1;
+
+// BF16 pair (low half = lower column) -> two floats, exactly.
+__device__ inline float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// GELU, tanh form: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), evaluated
+// as z / (1 + exp(-2 u)) with u the tanh argument (the same function:
+// 0.5 (1 + tanh u) = 1 / (1 + exp(-2 u))). exp overflows to +inf for very
+// negative z, giving -0; it underflows to 0 for large z, giving z. The
+// hardware exponential and reciprocal (about 1 ulp each) replace the
+// correctly rounded division, a ten-instruction sequence per element.
+template <int ACT>
+__device__ inline float activate(float z)
+{
+    if constexpr (ACT == ACT_RELU) {
+        return z > 0.0f ? z : 0.0f;
+    } else if constexpr (ACT == ACT_GELU_TANH) {
+        const float u = z * (0.7978845608f + 0.0356774081f * z * z);
+        return z * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+    } else {
+        return z;
+    }
+}
+
+// z = x + bias (bias as two BF16 pairs: columns 0, 1 in w[0], 2, 3 in w[1]),
+// then the activation, for four consecutive columns.
+template <int ACT>
+__device__ inline f32x4 epilogue4(f32x4 x, u32x2 w)
+{
+    return f32x4{activate<ACT>(x[0] + bf16_lo(w[0])), activate<ACT>(x[1] + bf16_hi(w[0])),
+                 activate<ACT>(x[2] + bf16_lo(w[1])), activate<ACT>(x[3] + bf16_hi(w[1]))};
+}
+
 
 // A buffer resource whose range ends at the operand's last byte: loads past it
 // return 0 and stores past it are dropped, which makes row tails (m >= M,

@@ -228,6 +228,7 @@ int choose_bf16_instance(int M, int N, int K, int cus, int forced, int *splits)
 // Split-K instance: partial tiles into a stream-ordered workspace, then the
 // reduction into C, both on `stream`; with one split the tiles go straight to
 // C and neither the workspace nor the reduction is used.
+template <int EPI>
 int launch_splitk(const Problem &p, void *stream)
 {
     namespace sk = gemm355::bf16_splitk;
@@ -239,6 +240,7 @@ int launch_splitk(const Problem &p, void *stream)
     sp.a = p.a;
     sp.b = p.b;
     sp.c = p.c;
+    sp.bias = p.bias;
     sp.M = p.M;
     sp.N = p.N;
     sp.K = p.K;
@@ -255,20 +257,36 @@ int launch_splitk(const Problem &p, void *stream)
         sp.ws = static_cast<float *>(ws);
     }
     (void)hipGetLastError(); // clear a stale error so the check below is ours
-    hipLaunchKernelGGL(sk::gemm_bf16_nt_splitk_kernel, dim3((unsigned)items), dim3(gemm355::THREADS), 0, s, sp);
+    hipLaunchKernelGGL(sk::gemm_bf16_nt_splitk_kernel<EPI>, dim3((unsigned)items), dim3(gemm355::THREADS), 0, s, sp);
     if (sp.splits > 1) {   // one split stores C itself
         const int64_t outs = int64_t(p.M) * (p.N / 8);
-        hipLaunchKernelGGL(sk::splitk_reduce_kernel, dim3((unsigned)ceil_div(outs, sk::REDUCE_THREADS)),
+        hipLaunchKernelGGL(sk::splitk_reduce_kernel<EPI>, dim3((unsigned)ceil_div(outs, sk::REDUCE_THREADS)),
                            dim3(sk::REDUCE_THREADS), 0, s, sp);
     }
     return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 
-} // namespace
+// The chosen instance's kernels with epilogue EPI.
+template <int EPI>
+int launch_instance(int instance, const Problem &p, void *stream)
+{
+    if (instance == 3)
+        return launch_splitk<EPI>(p, stream);
+    if (instance == 2)
+        return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel<EPI>, p, stream, gemm355::bf16_small::TM,
+                      gemm355::bf16_small::TN);
+    return launch(gemm355::bf16::gemm_bf16_nt_kernel<EPI>, p, stream);
+}
 
-extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, void *stream)
+// Shared by gemm_bf16_nt and gemm_bf16_nt_bias_act: validation, instance
+// choice, launch. FUSED selects the kernels with the fused epilogue.
+template <bool FUSED>
+int bf16_product(int M, int N, int K, const void *A, const void *B, const void *bias, int act, void *C,
+                 void *stream)
 {
     if (M < 0 || N < 0 || K < 0)
+        return GEMM355_ERR_INVALID_ARG;
+    if (FUSED && (act < GEMM355_ACT_NONE || act > GEMM355_ACT_GELU_TANH))
         return GEMM355_ERR_INVALID_ARG;
     if (M == 0 || N == 0)
         return GEMM355_OK;
@@ -277,7 +295,9 @@ extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, v
     const size_t c_bytes = size_t(M) * size_t(N) * 2;
     if (K > 0 && (overlaps(C, c_bytes, A, size_t(M) * K * 2) || overlaps(C, c_bytes, B, size_t(N) * K * 2)))
         return GEMM355_ERR_INVALID_ARG;
-    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16))
+    if (FUSED && overlaps(C, c_bytes, bias, size_t(N) * 2))
+        return GEMM355_ERR_INVALID_ARG;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(bias, 16))
         return GEMM355_ERR_UNSUPPORTED;
     if (K % 8 != 0 || N % 8 != 0)
         return GEMM355_ERR_UNSUPPORTED;
@@ -288,6 +308,7 @@ extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, v
     p.a = A;
     p.b = B;
     p.c = C;
+    p.bias = FUSED ? bias : nullptr;
     p.M = M;
     p.N = N;
     p.K = K;
@@ -297,12 +318,26 @@ extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, v
         return rc;
     int splits = 0;
     const int instance = choose_bf16_instance(M, N, K, cus, g_bf16_instance.load(std::memory_order_relaxed), &splits);
-    if (instance == 3)
-        return launch_splitk(p, stream);
-    if (instance == 2)
-        return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel, p, stream, gemm355::bf16_small::TM,
-                      gemm355::bf16_small::TN);
-    return launch(gemm355::bf16::gemm_bf16_nt_kernel, p, stream);
+    if (!FUSED)
+        return launch_instance<gemm355::EPI_PLAIN>(instance, p, stream);
+    if (act == GEMM355_ACT_RELU)
+        return launch_instance<gemm355::ACT_RELU>(instance, p, stream);
+    if (act == GEMM355_ACT_GELU_TANH)
+        return launch_instance<gemm355::ACT_GELU_TANH>(instance, p, stream);
+    return launch_instance<gemm355::ACT_NONE>(instance, p, stream);
+}
+
+} // namespace
+
+extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, void *stream)
+{
+    return bf16_product<false>(M, N, K, A, B, nullptr, GEMM355_ACT_NONE, C, stream);
+}
+
+extern "C" int gemm_bf16_nt_bias_act(int M, int N, int K, const void *A, const void *B, const void *bias,
+                                     int activation, void *C, void *stream)
+{
+    return bf16_product<true>(M, N, K, A, B, bias, activation, C, stream);
 }
 
 extern "C" int gemm355_bf16_plan(int M, int N, int K, int compute_units, int *instance, int *splits)

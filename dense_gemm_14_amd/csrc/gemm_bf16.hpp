@@ -90,7 +90,6 @@ enum StepKind : int { FIRST, MID, TAIL, NEXT0, NEXT1 };
 __device__ inline int swizzle(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resource as four scalar words, for the inline-assembly copies.
 __device__ inline i32x4 rsrc_words(const void *p, unsigned bytes)
@@ -140,10 +139,14 @@ __device__ inline int fresh_lane_id()
     return l;
 }
 
+// EPI: EPI_PLAIN, or the activation of the fused epilogue (bias, then the
+// activation, before rounding).
+template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_kernel(Problem p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    constexpr bool FUSED = EPI != EPI_PLAIN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -179,16 +182,28 @@ void gemm_bf16_nt_kernel(Problem p)
     }
 
     f32x4 acc[8][8];
+    // Fused epilogue: bias[n .. n + 3] (two BF16 pairs) for this lane's
+    // columns n of block column 2 jp + h of tile column ctn; zeros past N and
+    // without a bias (an empty range).
+    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(p.bias, FUSED && p.bias ? (unsigned)p.N * 2u : 0u);
+    auto load_bias = [&](int ctn, int jp, int h, int ln) {
+        const int n = ctn * BN + wn * 128 + 16 * (2 * jp + h) + 4 * (ln >> 4);
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rbias, n < p.N ? n * 2 : OOB, 0, 0));
+    };
     // Epilogue of one pair of blocks. Lane (l16, grp) of block (i, j) holds
     // C[m][n .. n + 3] with m = m0 + 16 i + l16 and n = n0 + 16 j + 4 grp. For
     // x = block (i, 2 jp) and y = block (i, 2 jp + 1), v_permlane16_swap
     // exchanges lane groups so that group 0 holds columns 0..7 of x, group 1
     // columns 0..7 of y, group 2 columns 8..15 of x and group 3 columns 8..15
     // of y: one 16-byte store per lane, 64 contiguous bytes per C row.
-    auto store_pair = [&](int ctm, int ctn, int i, int jp, int ln) {
+    auto store_pair = [&](int ctm, int ctn, int i, int jp, int ln, u32x2 bx, u32x2 by) {
         const int l16 = ln & 15, grp = ln >> 4;
-        const f32x4 &x = acc[i][2 * jp];
-        const f32x4 &y = acc[i][2 * jp + 1];
+        f32x4 x = acc[i][2 * jp];
+        f32x4 y = acc[i][2 * jp + 1];
+        if constexpr (FUSED) {
+            x = epilogue4<EPI>(x, bx);
+            y = epilogue4<EPI>(y, by);
+        }
         const unsigned x0 = pack_bf16(x[0], x[1]), x1 = pack_bf16(x[2], x[3]);
         const unsigned y0 = pack_bf16(y[0], y[1]), y1 = pack_bf16(y[2], y[3]);
         const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
@@ -381,11 +396,30 @@ void gemm_bf16_nt_kernel(Problem p)
         // epilogue; the next tile's first two steps are in LDS or landing
         wait_all_copies();
         const int ln = fresh_lane_id();
+        if constexpr (FUSED) {
+            // by block-column pairs, the bias of the next pair requested
+            // while the current one is stored
+            u32x2 bx = load_bias(tn, 0, 0, ln), by = load_bias(tn, 0, 1, ln);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+            for (int jp = 0; jp < 4; ++jp) {
+                u32x2 nbx = {}, nby = {};
+                if (jp < 3) {
+                    nbx = load_bias(tn, jp + 1, 0, ln);
+                    nby = load_bias(tn, jp + 1, 1, ln);
+                }
 #pragma unroll
-            for (int jp = 0; jp < 4; ++jp)
-                store_pair(tm, tn, i, jp, ln);
+                for (int i = 0; i < 8; ++i)
+                    store_pair(tm, tn, i, jp, ln, bx, by);
+                bx = nbx;
+                by = nby;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp)
+                    store_pair(tm, tn, i, jp, ln, u32x2{}, u32x2{});
+        }
         if (!has_next)
             break;
         // switch to the next tile

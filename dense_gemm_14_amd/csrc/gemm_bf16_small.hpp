@@ -51,7 +51,6 @@ static_assert(COPIES * (STAGES - 1) <= 63, "vmcnt counts at most 63 outstanding 
 __device__ inline int swizzle(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline i32x4 rsrc_words(const void *p, unsigned bytes)
 {
@@ -87,10 +86,14 @@ template <int N>
 __device__ inline void wait_copies_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// EPI: EPI_PLAIN, or the activation of the fused epilogue (bias, then the
+// activation, before rounding).
+template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_small_kernel(Problem p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    constexpr bool FUSED = EPI != EPI_PLAIN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,6 +119,8 @@ void gemm_bf16_nt_small_kernel(Problem p)
     const i32x4 ra = rsrc_words(static_cast<const uint8_t *>(p.a) - SHIFT, (unsigned)p.M * (unsigned)K * 2u + SHIFT);
     const i32x4 rb = rsrc_words(static_cast<const uint8_t *>(p.b) - SHIFT, (unsigned)p.N * (unsigned)K * 2u + SHIFT);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
+    // fused epilogue: bias[n] (zeros past N and without a bias: an empty range)
+    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(p.bias, FUSED && p.bias ? (unsigned)p.N * 2u : 0u);
     const int nk = (K + BK - 1) / BK;
 
     for (int round = 0;; ++round) {
@@ -178,6 +183,17 @@ void gemm_bf16_nt_small_kernel(Problem p)
         wait_reads();
         wait_all_copies();
         lds_barrier();
+        // fused epilogue: bias[n .. n + 3] of this lane's columns in blocks
+        // 0 and 1 (older than every copy of the tile, so landed by the first
+        // step's wait)
+        u32x2 bias_w[2];
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int n = tn * TN + wn * 32 + 16 * j + 4 * grp;
+                bias_w[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rbias, n < p.N ? n * 2 : OOB, 0, 0));
+            }
+        }
         for (int s = 0; s < STAGES - 1; ++s) {
             set_m0(copy_base(s));
             copy(s, Int<0>{});
@@ -240,8 +256,12 @@ void gemm_bf16_nt_small_kernel(Problem p)
         const int n = tn * TN + wn * 32 + 16 * (grp & 1) + 8 * (grp >> 1);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const f32x4 &x = acc[i][0];
-            const f32x4 &y = acc[i][1];
+            f32x4 x = acc[i][0];
+            f32x4 y = acc[i][1];
+            if constexpr (FUSED) {
+                x = epilogue4<EPI>(x, bias_w[0]);
+                y = epilogue4<EPI>(y, bias_w[1]);
+            }
             const unsigned x0 = pack_bf16(x[0], x[1]), x1 = pack_bf16(x[2], x[3]);
             const unsigned y0 = pack_bf16(y[0], y[1]), y1 = pack_bf16(y[2], y[3]);
             const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);

@@ -59,6 +59,7 @@ struct SplitProblem {
     const void *a, *b;
     float *ws;          // partial tiles, [tiles][splits][TM][TN] FP32, row-major (unused with one split)
     void *c;
+    const void *bias;   // fused epilogue only: N BF16 values, or NULL (zeros)
     int M, N, K;
     int tiles_m, tiles_n;
     int splits;
@@ -68,8 +69,6 @@ struct SplitProblem {
 __device__ inline int swizzle(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline i32x4 rsrc_words(const void *p, unsigned bytes)
 {
@@ -115,10 +114,14 @@ __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "m
 // complete in issue order, so a wave copying both operands would wait for its
 // older B copies whenever it waits for A, and B's prefetch depth would shrink
 // to A's. LDS: A ring, then B ring; row r of a unit at byte 128 r.
+// EPI: EPI_PLAIN, or the activation of the fused epilogue, applied here with
+// one split (with several, by the reduction).
+template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_splitk_kernel(SplitProblem p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+    constexpr bool FUSED = EPI != EPI_PLAIN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -188,6 +191,19 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
         else
             wait_copies_le<COPIES * (A_STAGES - 2)>();
     };
+
+    // fused epilogue with one split: bias[n .. n + 3] of this lane's columns
+    // in block column j (requested before any copy, so landed by the first
+    // step's wait; zeros past N and without a bias)
+    u32x2 bias_w[4];
+    if constexpr (FUSED) {
+        const __amdgpu_buffer_rsrc_t rbias = make_rsrc(p.bias, p.bias && p.splits == 1 ? (unsigned)p.N * 2u : 0u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = tn * TN + 64 * wn + 16 * j + 4 * grp;
+            bias_w[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rbias, n < p.N ? n * 2 : OOB, 0, 0));
+        }
+    }
 
     f32x4 acc[4][4];
     bf16x8 fa[2][2][4], fb[2][2][4];   // [buffer][half][block]
@@ -269,7 +285,10 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
             for (int j = 0; j < 4; ++j) {
                 const int m = tm * TM + 64 * wm + 16 * i + l16, n = tn * TN + 64 * wn + 16 * j + 4 * grp;
                 const int off = (m < p.M && n < p.N) ? (m * p.N + n) * 2 : OOB;
-                const u32x2 v = {pack_bf16(acc[i][j][0], acc[i][j][1]), pack_bf16(acc[i][j][2], acc[i][j][3])};
+                f32x4 x = acc[i][j];
+                if constexpr (FUSED)
+                    x = epilogue4<EPI>(x, bias_w[j]);
+                const u32x2 v = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
                 __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
             }
     } else {
@@ -287,7 +306,9 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
 }
 
 // C[m][n .. n + 7] = bf16_rne(sum over splits z = 0, 1, ... of the partials),
-// one thread per 8 consecutive outputs of a row (N % 8 == 0).
+// one thread per 8 consecutive outputs of a row (N % 8 == 0); with the fused
+// epilogue (EPI an activation) applied to the sum before rounding.
+template <int EPI>
 __global__ __launch_bounds__(REDUCE_THREADS) void splitk_reduce_kernel(SplitProblem p)
 {
     const int per_row = p.N / 8;
@@ -302,6 +323,13 @@ __global__ __launch_bounds__(REDUCE_THREADS) void splitk_reduce_kernel(SplitProb
     for (int z = 0; z < p.splits; ++z) {
         lo += *reinterpret_cast<const f32x4 *>(src + (size_t)z * TILE_FLOATS);
         hi += *reinterpret_cast<const f32x4 *>(src + (size_t)z * TILE_FLOATS + 4);
+    }
+    if constexpr (EPI != EPI_PLAIN) {
+        u32x4 b = {};
+        if (p.bias)
+            b = *reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(p.bias) + (size_t)n * 2);
+        lo = epilogue4<EPI>(lo, u32x2{b[0], b[1]});
+        hi = epilogue4<EPI>(hi, u32x2{b[2], b[3]});
     }
     const u32x4 out = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])};
     *reinterpret_cast<u32x4 *>(static_cast<uint8_t *>(p.c) + ((size_t)m * p.N + n) * 2) = out;

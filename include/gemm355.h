@@ -82,6 +82,37 @@ typedef enum gemm355_status {
  */
 int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, void *stream);
 
+/* Activations of gemm_bf16_nt_bias_act's fused epilogue. */
+typedef enum gemm355_activation {
+    GEMM355_ACT_NONE = 0,         /* y = z                                          */
+    GEMM355_ACT_RELU = 1,         /* y = max(z, 0)                                  */
+    GEMM355_ACT_GELU_TANH = 2     /* y = z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) */
+} gemm355_activation;
+
+/*
+ * gemm_bf16_nt_bias_act -- C = act(A * B^T + bias), BF16 in and out, with the
+ * bias and the activation applied in the epilogue while the FP32 sums are
+ * still in registers ("NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue
+ * Warps": the epilogue is where activations and other element-wise operations
+ * would be fused).
+ *
+ *   C[m][n] = bf16_rne(act(z)),  z = fp32(sum_k A[m][k] * B[n][k]) + bias[n]
+ *
+ * with the sum as in gemm_bf16_nt, the bias added in FP32, and the activation
+ * (a gemm355_activation) evaluated in FP32; the GELU's exponential is the
+ * hardware's (relative error about 1e-6), far below the BF16 rounding.
+ *   bias     N BF16 values (one per column of C, e.g. per output feature of a
+ *            linear layer), 16-byte aligned; NULL means zeros.
+ *   activation  GEMM355_ACT_NONE, _RELU or _GELU_TANH.
+ * Everything else (layouts, ownership, edge cases, requirements, instances,
+ * workspace, determinism) is as for gemm_bf16_nt; K == 0 gives act(bias[n]).
+ * Errors: an unknown activation or a bias overlapping C -> INVALID_ARG; a bias
+ * not 16-byte aligned -> UNSUPPORTED. The bias must not be written while the
+ * product runs.
+ */
+int gemm_bf16_nt_bias_act(int M, int N, int K, const void *A, const void *B, const void *bias,
+                          int activation, void *C, void *stream);
+
 /*
  * gemm355_force_instance -- override the choice of gemm_bf16_nt's instance.
  *

@@ -18,7 +18,7 @@ FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced
 def test_library_exports_every_declared_function():
     lib = g.load()
     names = g.declared_functions()
-    assert set(names) >= {"gemm_bf16_nt", "gemm_nvfp4_nt", "gemm355_status_string",
+    assert set(names) >= {"gemm_bf16_nt", "gemm_bf16_nt_bias_act", "gemm_nvfp4_nt", "gemm355_status_string",
                           "gemm355_tile_order", "gemm355_schedule"}
     for n in names:
         assert hasattr(lib, n), n
@@ -57,6 +57,24 @@ def test_bf16_specific_rejections():
     assert _bf16(1 << 16, 8, 1 << 15, b=1 << 40, c=1 << 41) == g.ERR_UNSUPPORTED  # A spans 4 GiB
     # C overlapping A
     assert _bf16(8, 8, 64, a=FAKE, c=FAKE + 64) == g.ERR_INVALID_ARG
+
+
+def _fused(M, N, K, act=0, bias=FAKE + 0x300000, a=FAKE, b=FAKE + 0x100000, c=FAKE + 0x200000):
+    return g.load().gemm_bf16_nt_bias_act(M, N, K, a, b, bias, act, c, None)
+
+
+def test_fused_epilogue_rejections():
+    # the plain product's rules, then the activation and the bias
+    assert _fused(-1, 8, 64) == g.ERR_INVALID_ARG
+    assert _fused(8, 12, 64) == g.ERR_UNSUPPORTED                  # N % 8
+    assert _fused(8, 8, 64, c=None) == g.ERR_INVALID_ARG
+    for bad_act in (-1, 3, 99):
+        assert _fused(8, 8, 64, act=bad_act) == g.ERR_INVALID_ARG
+        assert _fused(0, 8, 64, act=bad_act) == g.ERR_INVALID_ARG   # checked even with nothing to do
+    assert _fused(8, 8, 64, bias=FAKE + 0x300008) == g.ERR_UNSUPPORTED   # bias not 16-byte aligned
+    assert _fused(8, 8, 64, bias=FAKE + 0x200000 + 64) == g.ERR_INVALID_ARG  # bias inside C
+    # empty output with a valid activation: nothing to do
+    assert _fused(0, 8, 64, act=g.ACT_GELU_TANH, a=None, b=None, bias=None, c=None) == g.OK
 
 
 def test_fp4_specific_rejections():

@@ -1,0 +1,134 @@
+"""gemm_bf16_nt_bias_act (bias and activation fused into the epilogue) against
+the oracle, through the C ABI: every BF16 instance forced in turn, each
+activation, ragged shapes element by element, split K with several splits
+(the reduction applies the epilogue), exactly summable inputs bitwise for the
+identity and ReLU, K = 0 (the activation of the bias), no bias, and the
+8192^3 workload on sampled elements.
+
+Reference: "NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue Warps" (the
+epilogue is where activations and element-wise operations would be fused).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_14_amd as g
+import oracle
+import synthetic as syn
+from tests import tolerance
+from tests.gpu_util import GuardedC, need_gpu, sample_positions, to_dev
+
+pytestmark = pytest.mark.gpu
+
+INSTANCES = [g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_SPLITK]
+ACTS = [g.ACT_NONE, g.ACT_RELU, g.ACT_GELU_TANH]
+
+
+@pytest.fixture
+def forced(request):
+    need_gpu()
+    g.force_instance(request.param)
+    yield request.param
+    g.force_instance(g.INSTANCE_AUTO)
+
+
+def run_fused(A, B, bias, act, M, N, K):
+    C = GuardedC(M, N)
+    g.gemm_bf16_nt_bias_act(M, N, K, to_dev(A) if A is not None else None, to_dev(B) if B is not None else None,
+                            to_dev(bias) if bias is not None else None, act, C.view)
+    torch.cuda.synchronize()
+    assert C.guards_intact(), "write outside C"
+    return C.bits()
+
+
+def reference(A, B, bias, act, M, N):
+    ms, ns = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ref, z = oracle.gemm_bf16_nt_bias_act_at(A, B, bias, act, ms.ravel(), ns.ravel(), with_z=True)
+    return ref.reshape(M, N), z.reshape(M, N)
+
+
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("M,N,K", [(300, 264, 520), (65, 72, 64), (257, 520, 1032)])
+def test_fused_matches_oracle(forced, act, M, N, K):
+    # small K keeps z = sum + bias near the activations' bend
+    A = syn.bf16_uniform(M, K, seed=M + 3 * K + act)
+    B = syn.bf16_uniform(N, K, seed=N + 3 * K + 1)
+    bias = syn.bf16_uniform(1, N, seed=N + 17, lo=-2.0, hi=2.0)[0]
+    got = run_fused(A, B, bias, act, M, N, K)
+    ref, z = reference(A, B, bias, act, M, N)
+    res = tolerance.check_fused(got, ref, z, K, act)
+    assert res, res
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_fused_split_reduction(act):
+    # 2 x 9 tiles of 128 x 128 and 65 K steps: eight splits, so the epilogue
+    # runs in the reduction kernel
+    need_gpu()
+    M, N, K = 136, 1032, 4104
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    inst, splits = g.bf16_plan(M, N, K, cus)
+    assert inst == g.INSTANCE_SPLITK and splits > 1
+    A = syn.bf16_uniform(M, K, seed=51)
+    B = syn.bf16_uniform(N, K, seed=52)
+    bias = syn.bf16_uniform(1, N, seed=53, lo=-8.0, hi=8.0)[0]
+    got = run_fused(A, B, bias, act, M, N, K)
+    ref, z = reference(A, B, bias, act, M, N)
+    res = tolerance.check_fused(got, ref, z, K, act)
+    assert res, res
+
+
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("act", [g.ACT_NONE, g.ACT_RELU])
+def test_fused_exact_inputs_bitwise(forced, act):
+    # multiples of 1/16 with K = 264: every partial sum, and the bias added to
+    # it, is exact in FP32, and ReLU is exact, so the result is unique
+    M, N, K = 513, 520, 264
+    A = syn.bf16_sixteenths(M, K, seed=61)
+    B = syn.bf16_sixteenths(N, K, seed=62)
+    bias = syn.bf16_sixteenths(1, N, seed=63, jmax=64)[0]
+    assert np.array_equal(run_fused(A, B, bias, act, M, N, K), oracle.gemm_bf16_nt_bias_act(A, B, bias, act))
+
+
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("act", ACTS)
+def test_fused_empty_sum_is_activation_of_bias(forced, act):
+    M, N = 70, 72
+    bias = syn.bf16_uniform(1, N, seed=71, lo=-4.0, hi=4.0)[0]
+    got = run_fused(None, None, bias, act, M, N, 0)
+    ref = oracle.gemm_bf16_nt_bias_act(np.zeros((M, 0), np.uint16), np.zeros((N, 0), np.uint16), bias, act)
+    z = np.broadcast_to(tolerance.bf16_bits_to_f64(bias), (M, N))
+    res = tolerance.check_fused(got, ref, z, 0, act)
+    assert res, res
+    if act != g.ACT_GELU_TANH:
+        assert np.array_equal(got, ref)
+
+
+def test_fused_without_bias_equals_plain_product():
+    need_gpu()
+    M, N, K = 300, 264, 520
+    A = syn.bf16_uniform(M, K, seed=81)
+    B = syn.bf16_uniform(N, K, seed=82)
+    dA, dB = to_dev(A), to_dev(B)
+    C0, C1 = GuardedC(M, N), GuardedC(M, N)
+    g.gemm_bf16_nt(M, N, K, dA, dB, C0.view)
+    g.gemm_bf16_nt_bias_act(M, N, K, dA, dB, None, g.ACT_NONE, C1.view)
+    torch.cuda.synchronize()
+    # the same sums; only the sign of an exact zero could differ (x + 0 = +0)
+    assert np.array_equal(tolerance.bf16_bits_to_f64(C0.bits()), tolerance.bf16_bits_to_f64(C1.bits()))
+
+
+@pytest.mark.parametrize("act", [g.ACT_RELU, g.ACT_GELU_TANH])
+def test_fused_workload_8192_sampled(act):
+    # the benchmark's fused workload: 256 x 256 tiles, four rounds per unit
+    need_gpu()
+    M = N = K = 8192
+    A = syn.bf16_uniform(M, K, seed=91)
+    B = syn.bf16_uniform(N, K, seed=92)
+    bias = syn.bf16_uniform(1, N, seed=93, lo=-16.0, hi=16.0)[0]
+    got = run_fused(A, B, bias, act, M, N, K)
+    ms, ns = sample_positions(M, N, 2000, seed=94)
+    ref, z = oracle.gemm_bf16_nt_bias_act_at(A, B, bias, act, ms, ns, with_z=True)
+    res = tolerance.check_fused(got[ms, ns], ref, z, K, act)
+    assert res, res
