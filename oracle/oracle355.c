@@ -203,7 +203,7 @@ int oracle_gemm_bf16_nt_at(int M, int N, int K, const uint16_t *A, const uint16_
     for (long i = 0; i < count; ++i)
         if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N)
             return ORACLE_BAD_ARGS;
-#pragma omp parallel for schedule(dynamic, 16)
+#pragma omp parallel for schedule(dynamic, 1)
     for (long i = 0; i < count; ++i) {
         double s = dot_bf16(A, B, K, ms[i], ns[i]);
         out_bf16[i] = oracle_bf16_from_double(s);
@@ -223,7 +223,7 @@ int oracle_gemm_nvfp4_nt_at(int M, int N, int K, const uint8_t *Aq, const uint8_
     for (long i = 0; i < count; ++i)
         if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N)
             return ORACLE_BAD_ARGS;
-#pragma omp parallel for schedule(dynamic, 16)
+#pragma omp parallel for schedule(dynamic, 1)
     for (long i = 0; i < count; ++i) {
         double s = dot_fp4(Aq, SFA, Bq, SFB, K, ms[i], ns[i]);
         out_bf16[i] = oracle_bf16_from_double(s);
@@ -284,7 +284,7 @@ int oracle_gemm_bf16_nt_bias_act_at(int M, int N, int K, const uint16_t *A, cons
     for (long i = 0; i < count; ++i)
         if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N)
             return ORACLE_BAD_ARGS;
-#pragma omp parallel for schedule(dynamic, 16)
+#pragma omp parallel for schedule(dynamic, 1)
     for (long i = 0; i < count; ++i) {
         const double z = dot_bf16(A, B, K, ms[i], ns[i]) + bias_at(bias, ns[i]);
         out_bf16[i] = oracle_bf16_from_double(oracle_activate(z, act));

@@ -51,6 +51,22 @@ def bf16_sixteenths(rows: int, cols: int, seed: int, jmax: int = 16) -> np.ndarr
     return to_bf16_bits(j.astype(np.float32) / 16.0)
 
 
+def bf16_sixteenths_large(rows: int, cols: int, seed: int) -> np.ndarray:
+    """(rows, cols) BF16 bits holding j/16, integer j uniform in [-16, 15], for
+    arrays of billions of elements: byte draws mapped through a 32-entry table
+    of BF16 bit patterns (torch's cast of j/16), in slices, without float
+    temporaries. Products of such values are exact as for ``bf16_sixteenths``."""
+    table = to_bf16_bits(np.arange(-16, 16, dtype=np.float32) / 16.0)
+    g = rng(seed)
+    out = np.empty(rows * cols, dtype=np.uint16)
+    step = 1 << 24
+    for i in range(0, out.size, step):
+        n = min(step, out.size - i)
+        j = np.frombuffer(g.bytes(n), dtype=np.uint8) & 31
+        out[i:i + n] = table[j]
+    return out.reshape(rows, cols)
+
+
 def bf16_identity(n: int) -> np.ndarray:
     return to_bf16_bits(np.eye(n, dtype=np.float32))
 

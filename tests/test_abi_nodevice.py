@@ -77,6 +77,24 @@ def test_fused_epilogue_rejections():
     assert _fused(0, 8, 64, act=g.ACT_GELU_TANH, a=None, b=None, bias=None, c=None) == g.OK
 
 
+def test_extent_limits_are_exact():
+    # Operand extents, padded to whole 256-row tiles, must stay below 2^31
+    # bytes. Just inside, validation passes and the call stops at the missing
+    # device (NO_DEVICE here); at the limit it is UNSUPPORTED. The calls just
+    # inside carry fake addresses, so they run only where there is no device.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("calls with fake device addresses need a host without a GPU")
+    lib = g.load()
+    big = [FAKE, 1 << 40, 1 << 41, 1 << 42, 1 << 43]
+    assert lib.gemm_bf16_nt(3, 16, (1 << 22) - 8, big[0], big[1], big[2], None) == g.ERR_NO_DEVICE
+    assert lib.gemm_bf16_nt(3, 16, 1 << 22, big[0], big[1], big[2], None) == g.ERR_UNSUPPORTED
+    assert lib.gemm_nvfp4_nt(3, 16, (1 << 24) - 64, *big, None) == g.ERR_NO_DEVICE
+    assert lib.gemm_nvfp4_nt(3, 16, 1 << 24, *big, None) == g.ERR_UNSUPPORTED
+    assert lib.gemm_bf16_nt((1 << 27) - 300, 8, 8, big[0], big[1], big[2], None) == g.ERR_NO_DEVICE   # C, A
+    assert lib.gemm_bf16_nt(1 << 27, 8, 8, big[0], big[1], big[2], None) == g.ERR_UNSUPPORTED
+
+
 def test_fp4_specific_rejections():
     assert _fp4(8, 8, 64, sfa=None) == g.ERR_INVALID_ARG
     assert _fp4(8, 8, 32) == g.ERR_UNSUPPORTED                    # K % 64
