@@ -78,12 +78,15 @@ __device__ inline f16x8 decode8(unsigned codes, f16x2 s)
     return r;
 }
 
-// E4M3 scale byte BLK of the dword `sf`, as an FP16 pair (exact).
+// E4M3 scale bytes 0 and 1 of `sf` as FP16 (exact: FP16 holds every E4M3
+// value), one conversion for the two 16-element blocks of a half step.
+__device__ inline f16x2 scales2(unsigned sf) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sf, 1.0f, false); }
+
+// Scale BLK (0 or 1) of such a pair in both halves.
 template <int BLK>
-__device__ inline f16x2 scale2(unsigned sf)
+__device__ inline f16x2 scale2(f16x2 s)
 {
-    const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sf, BLK);
-    return f16x2{s, s};
+    return f16x2{s[BLK], s[BLK]};
 }
 
 // ---- the persistent kernel --------------------------------------------------
@@ -161,20 +164,23 @@ void gemm_nvfp4_nt_kernel(Problem p)
         StageRegs regs[2];
         // load q (0..7) of step kt into register set `set`: codes of row r0,
         // codes of row r0 + 128, scales of r0, scales of r0 + 128, for A (q < 4)
-        // then B. K % 64 == 0, so a step is whole or past K, where it reads zeros.
+        // then B. The per-lane part of the offset is fixed for the tile (rows
+        // past M or N lie beyond the buffer and read zeros); the step's K
+        // offset is uniform and goes in the scalar offset. K % 64 == 0, so a
+        // step is whole or past K; steps past K are requests made ahead for a
+        // step the tile never computes, and read step 0 again instead.
         auto load = [&](int kt, int set, int q) {
-            const int k0 = kt * BK;
-            const bool valid = k0 < K;
+            const int k0 = kt * BK < K ? kt * BK : 0;
             StageRegs &r = regs[set];
             switch (q) {
-            case 0: r.a_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, valid ? a_code_off + k0 / 2 : OOB, 0, 0)); break;
-            case 1: r.a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, valid ? a_code_off + row2_codes + k0 / 2 : OOB, 0, 0)); break;
-            case 2: r.a_sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, valid ? a_sf_off + k0 / 16 : OOB, 0, 0); break;
-            case 3: r.a_sf[1] = __builtin_amdgcn_raw_buffer_load_b32(rsa, valid ? a_sf_off + row2_sf + k0 / 16 : OOB, 0, 0); break;
-            case 4: r.b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, valid ? b_code_off + k0 / 2 : OOB, 0, 0)); break;
-            case 5: r.b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, valid ? b_code_off + row2_codes + k0 / 2 : OOB, 0, 0)); break;
-            case 6: r.b_sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, valid ? b_sf_off + k0 / 16 : OOB, 0, 0); break;
-            default: r.b_sf[1] = __builtin_amdgcn_raw_buffer_load_b32(rsb, valid ? b_sf_off + row2_sf + k0 / 16 : OOB, 0, 0); break;
+            case 0: r.a_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_code_off, k0 / 2, 0)); break;
+            case 1: r.a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_code_off + row2_codes, k0 / 2, 0)); break;
+            case 2: r.a_sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, a_sf_off, k0 / 16, 0); break;
+            case 3: r.a_sf[1] = __builtin_amdgcn_raw_buffer_load_b32(rsa, a_sf_off + row2_sf, k0 / 16, 0); break;
+            case 4: r.b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_code_off, k0 / 2, 0)); break;
+            case 5: r.b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_code_off + row2_codes, k0 / 2, 0)); break;
+            case 6: r.b_sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, b_sf_off, k0 / 16, 0); break;
+            default: r.b_sf[1] = __builtin_amdgcn_raw_buffer_load_b32(rsb, b_sf_off + row2_sf, k0 / 16, 0); break;
             }
         };
         // chunk c (0..15) of register set `set` into `stage`: A for c < 8,
@@ -184,7 +190,7 @@ void gemm_nvfp4_nt_kernel(Problem p)
             constexpr int rr = (c >> 2) & 1, d = c & 3;
             const StageRegs &r = regs[set];
             const unsigned codes = (c < 8 ? r.a_code : r.b_code)[rr][d];
-            const f16x2 s = scale2<d / 2>((c < 8 ? r.a_sf : r.b_sf)[rr] >> sf_shift);
+            const f16x2 s = scale2<d / 2>(scales2((c < 8 ? r.a_sf : r.b_sf)[rr] >> sf_shift));
             *reinterpret_cast<f16x8 *>(stage + (c < 8 ? 0 : TILE_BYTES) + rr * 128 * ROW_BYTES + wpos[d]) = decode8(codes, s);
         };
 
