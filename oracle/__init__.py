@@ -85,6 +85,8 @@ def _bind(lib):
     lib.oracle_gemm_bf16_nt_bias_act.restype = i
     lib.oracle_gemm_bf16_nt_bias_act_at.argtypes = [i, i, i, p, p, p, i, ctypes.c_long, p, p, p, p]
     lib.oracle_gemm_bf16_nt_bias_act_at.restype = i
+    lib.oracle_gemm_nvfp4_nt_bias_act_at.argtypes = [i, i, i, p, p, p, p, p, i, ctypes.c_long, p, p, p, p]
+    lib.oracle_gemm_nvfp4_nt_bias_act_at.restype = i
     lib.oracle_decode_nvfp4.argtypes = [i, i, p, p, p]
     lib.oracle_decode_nvfp4.restype = i
     lib.oracle_max_threads.argtypes = []
@@ -244,6 +246,25 @@ def gemm_bf16_nt_bias_act_at(A, B, bias, act: int, ms, ns, with_z: bool = False)
                                                _ptr(bias) if bias is not None else None, int(act), ms.size,
                                                _ptr(ms), _ptr(ns), _ptr(out), _ptr(zs)),
            "gemm_bf16_nt_bias_act_at")
+    return (out, zs) if with_z else out
+
+
+def gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K: int, bias, act: int, ms, ns, with_z: bool = False):
+    """Elements C[ms[i], ns[i]] of bf16(act(dec(A) @ dec(B)^T + bias))
+    (and optionally z before the activation)."""
+    lib = _load()
+    Aq, SFA, Bq, SFB = (_c(x, np.uint8) for x in (Aq, SFA, Bq, SFB))
+    M, N = Aq.shape[0], Bq.shape[0]
+    _shape_fp4(Aq, SFA, M, K)
+    _shape_fp4(Bq, SFB, N, K)
+    bias = _bias(bias, N)
+    ms, ns = _idx(ms, ns)
+    out = np.empty(ms.size, dtype=np.uint16)
+    zs = np.empty(ms.size, dtype=np.float64)
+    _check(lib.oracle_gemm_nvfp4_nt_bias_act_at(M, N, K, _ptr(Aq), _ptr(SFA), _ptr(Bq), _ptr(SFB),
+                                                _ptr(bias) if bias is not None else None, int(act), ms.size,
+                                                _ptr(ms), _ptr(ns), _ptr(out), _ptr(zs)),
+           "gemm_nvfp4_nt_bias_act_at")
     return (out, zs) if with_z else out
 
 

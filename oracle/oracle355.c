@@ -294,6 +294,29 @@ int oracle_gemm_bf16_nt_bias_act_at(int M, int N, int K, const uint16_t *A, cons
     return ORACLE_OK;
 }
 
+/* The block-scaled FP4 product with the same fused epilogue: z = sum of the
+ * decoded products + bias[n], then the activation, in binary64. Chosen
+ * elements only; out_z (may be NULL) gets z before the activation. */
+int oracle_gemm_nvfp4_nt_bias_act_at(int M, int N, int K, const uint8_t *Aq, const uint8_t *SFA,
+                                     const uint8_t *Bq, const uint8_t *SFB, const uint16_t *bias, int act,
+                                     long count, const int32_t *ms, const int32_t *ns, uint16_t *out_bf16,
+                                     double *out_z)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 16 != 0 || act < 0 || act > 2 || count < 0)
+        return ORACLE_BAD_ARGS;
+    for (long i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N)
+            return ORACLE_BAD_ARGS;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < count; ++i) {
+        const double z = dot_fp4(Aq, SFA, Bq, SFB, K, ms[i], ns[i]) + bias_at(bias, ns[i]);
+        out_bf16[i] = oracle_bf16_from_double(oracle_activate(z, act));
+        if (out_z)
+            out_z[i] = z;
+    }
+    return ORACLE_OK;
+}
+
 /* Decoded FP4 operand as binary64 (rows x K), for cross-checks. */
 int oracle_decode_nvfp4(int rows, int K, const uint8_t *Q, const uint8_t *SF, double *out)
 {

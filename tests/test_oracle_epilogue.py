@@ -144,3 +144,25 @@ def test_fused_bound_accepts_one_ulp_and_rejects_planted_mistakes():
     for wrong in (oracle.ACT_NONE, oracle.ACT_RELU):
         assert not tolerance.check_fused(oracle.gemm_bf16_nt_bias_act(A, B, bias, wrong), ref, z, K,
                                          oracle.ACT_GELU_TANH)
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_fp4_fused_is_activation_of_plain_fp4_sum_plus_bias(act):
+    # the FP4 form: z must be the plain FP4 oracle's binary64 sum plus the
+    # bias of the column (bias from one column to the left fails), and the
+    # output the activation of z evaluated independently (torch for the GELU)
+    M, N, K = 9, 24, 96
+    Aq, SFA = syn.fp4_operand(M, K, seed=131)
+    Bq, SFB = syn.fp4_operand(N, K, seed=132)
+    bias = syn.bf16_uniform(1, N, seed=133, lo=-64.0, hi=64.0)[0]
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    got, z = oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, bias, act, ms, ns, with_z=True)
+    _, s = oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns, with_sum=True)
+    b = tolerance.bf16_bits_to_f64(bias)
+    assert np.array_equal(z, s + b[ns])
+    assert not np.array_equal(z, s + np.roll(b, 1)[ns])
+    y = _gelu_torch(z) if act == oracle.ACT_GELU_TANH else (np.maximum(z, 0.0) if act == oracle.ACT_RELU else z)
+    assert np.array_equal(got, oracle.bf16_from_double(y))
+    if act == oracle.ACT_NONE:
+        assert np.array_equal(oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, None, act, ms, ns),
+                              oracle.gemm_nvfp4_nt(Aq, SFA, Bq, SFB, K).ravel())
