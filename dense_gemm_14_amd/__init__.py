@@ -9,6 +9,7 @@ The functions mirror the C entry points declared in ``include/gemm355.h``:
     gemm_bf16_nt(M, N, K, A, B, C, stream=None)
     gemm_bf16_nt_bias_act(M, N, K, A, B, bias, activation, C, stream=None)
     gemm_nvfp4_nt(M, N, K, Aq, SFA, Bq, SFB, C, stream=None)
+    gemm_nvfp4_nt_bias_act(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, stream=None)
     force_instance(instance)          # BF16 instance override (diagnostic)
     force_supergroup(width)           # band width of the tile order (diagnostic)
     bf16_plan(M, N, K, compute_units)  # (instance, splits) gemm_bf16_nt would run
@@ -72,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.gemm_bf16_nt_bias_act.restype = i
     lib.gemm_nvfp4_nt.argtypes = [i, i, i, p, p, p, p, p, p]
     lib.gemm_nvfp4_nt.restype = i
+    lib.gemm_nvfp4_nt_bias_act.argtypes = [i, i, i, p, p, p, p, p, i, p, p]
+    lib.gemm_nvfp4_nt_bias_act.restype = i
     lib.gemm355_status_string.argtypes = [i]
     lib.gemm355_status_string.restype = ctypes.c_char_p
     lib.gemm355_tile_order.argtypes = [i, i, i, p, p]
@@ -172,6 +175,22 @@ def gemm_nvfp4_nt(M: int, N: int, K: int, Aq, SFA, Bq, SFB, C, stream=None) -> N
     sfb = _addr(SFB, N * K // 16 if nz else 0, "SFB")
     c = _addr(C, M * N * 2 if nz else 0, "C")
     _check(lib.gemm_nvfp4_nt(M, N, K, aq, sfa, bq, sfb, c, _stream(stream)), "gemm_nvfp4_nt")
+
+
+def gemm_nvfp4_nt_bias_act(M: int, N: int, K: int, Aq, SFA, Bq, SFB, bias, activation: int, C,
+                           stream=None) -> None:
+    """C = act(dec(Aq, SFA) @ dec(Bq, SFB)^T + bias) with the fused epilogue."""
+    lib = load()
+    M, N, K = int(M), int(N), int(K)
+    nz = M > 0 and N > 0
+    aq = _addr(Aq, M * K // 2 if nz else 0, "Aq")
+    sfa = _addr(SFA, M * K // 16 if nz else 0, "SFA")
+    bq = _addr(Bq, N * K // 2 if nz else 0, "Bq")
+    sfb = _addr(SFB, N * K // 16 if nz else 0, "SFB")
+    bb = _addr(bias, N * 2 if nz else 0, "bias")
+    c = _addr(C, M * N * 2 if nz else 0, "C")
+    _check(lib.gemm_nvfp4_nt_bias_act(M, N, K, aq, sfa, bq, sfb, bb, int(activation), c, _stream(stream)),
+           "gemm_nvfp4_nt_bias_act")
 
 
 def force_instance(instance: int) -> None:

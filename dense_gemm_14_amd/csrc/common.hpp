@@ -155,9 +155,26 @@ __device__ inline void schedule_reads_with_mma()
 // m = row of the lane. Pairs of 4-column runs are exchanged between the two
 // half-waves (v_permlane32_swap) so every lane stores one 16-byte row segment;
 // a wave's store instruction covers 32 rows x 32 bytes.
-__device__ inline void store_tile(f32x16 (&acc)[4][4], const __amdgpu_buffer_rsrc_t &rc, int M, int N,
-                                  int m0, int n0, int l32, int half)
+//
+// EPI: EPI_PLAIN, or the activation of the fused epilogue, applied with the
+// bias of each column (rbias: N BF16 values; an empty range reads zeros).
+template <int EPI>
+__device__ inline void store_tile(f32x16 (&acc)[4][4], const __amdgpu_buffer_rsrc_t &rc,
+                                  const __amdgpu_buffer_rsrc_t &rbias, int M, int N, int m0, int n0, int l32,
+                                  int half)
 {
+    // fused: bias[n .. n + 3] of this lane's four-column runs, [j][g], columns
+    // n0 + 32 j + 8 g + 4 half
+    u32x2 bias_w[4][4];
+    if constexpr (EPI != EPI_PLAIN) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + 32 * j + 8 * g + 4 * half;
+                bias_w[j][g] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rbias, n < N ? n * 2 : OOB, 0, 0));
+            }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = m0 + i * 32 + l32;
@@ -167,10 +184,16 @@ __device__ inline void store_tile(f32x16 (&acc)[4][4], const __amdgpu_buffer_rsr
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int g0 = 2 * q;
-                unsigned x0 = pack_bf16(acc[i][j][4 * g0 + 0], acc[i][j][4 * g0 + 1]);
-                unsigned x1 = pack_bf16(acc[i][j][4 * g0 + 2], acc[i][j][4 * g0 + 3]);
-                unsigned y0 = pack_bf16(acc[i][j][4 * g0 + 4], acc[i][j][4 * g0 + 5]);
-                unsigned y1 = pack_bf16(acc[i][j][4 * g0 + 6], acc[i][j][4 * g0 + 7]);
+                f32x4 lo = {acc[i][j][4 * g0 + 0], acc[i][j][4 * g0 + 1], acc[i][j][4 * g0 + 2], acc[i][j][4 * g0 + 3]};
+                f32x4 hi = {acc[i][j][4 * g0 + 4], acc[i][j][4 * g0 + 5], acc[i][j][4 * g0 + 6], acc[i][j][4 * g0 + 7]};
+                if constexpr (EPI != EPI_PLAIN) {
+                    lo = epilogue4<EPI>(lo, bias_w[j][g0]);
+                    hi = epilogue4<EPI>(hi, bias_w[j][g0 + 1]);
+                }
+                unsigned x0 = pack_bf16(lo[0], lo[1]);
+                unsigned x1 = pack_bf16(lo[2], lo[3]);
+                unsigned y0 = pack_bf16(hi[0], hi[1]);
+                unsigned y1 = pack_bf16(hi[2], hi[3]);
                 // the lower half-wave keeps group g0 and receives the upper
                 // half's part of it; the upper half-wave ends up with g0 + 1
                 auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);

@@ -364,10 +364,16 @@ extern "C" int gemm355_force_supergroup(int supergroup)
     return GEMM355_OK;
 }
 
-extern "C" int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
-                             const void *SFB, void *C, void *stream)
+namespace {
+
+// Shared by gemm_nvfp4_nt and gemm_nvfp4_nt_bias_act: validation, launch.
+template <bool FUSED>
+int fp4_product(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq, const void *SFB,
+                const void *bias, int act, void *C, void *stream)
 {
     if (M < 0 || N < 0 || K < 0)
+        return GEMM355_ERR_INVALID_ARG;
+    if (FUSED && (act < GEMM355_ACT_NONE || act > GEMM355_ACT_GELU_TANH))
         return GEMM355_ERR_INVALID_ARG;
     if (M == 0 || N == 0)
         return GEMM355_OK;
@@ -377,7 +383,10 @@ extern "C" int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SF
     if (K > 0 && (overlaps(C, c_bytes, Aq, size_t(M) * K / 2) || overlaps(C, c_bytes, Bq, size_t(N) * K / 2) ||
                   overlaps(C, c_bytes, SFA, size_t(M) * K / 16) || overlaps(C, c_bytes, SFB, size_t(N) * K / 16)))
         return GEMM355_ERR_INVALID_ARG;
-    if (!aligned(Aq, 16) || !aligned(Bq, 16) || !aligned(C, 16) || !aligned(SFA, 4) || !aligned(SFB, 4))
+    if (FUSED && overlaps(C, c_bytes, bias, size_t(N) * 2))
+        return GEMM355_ERR_INVALID_ARG;
+    if (!aligned(Aq, 16) || !aligned(Bq, 16) || !aligned(C, 16) || !aligned(SFA, 4) || !aligned(SFB, 4) ||
+        !aligned(bias, 16))
         return GEMM355_ERR_UNSUPPORTED;
     if (K % 64 != 0 || N % 8 != 0)
         return GEMM355_ERR_UNSUPPORTED;
@@ -390,10 +399,31 @@ extern "C" int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SF
     p.sfa = SFA;
     p.sfb = SFB;
     p.c = C;
+    p.bias = FUSED ? bias : nullptr;
     p.M = M;
     p.N = N;
     p.K = K;
-    return launch(gemm355::fp4::gemm_nvfp4_nt_kernel, p, stream);
+    if (!FUSED)
+        return launch(gemm355::fp4::gemm_nvfp4_nt_kernel<gemm355::EPI_PLAIN>, p, stream);
+    if (act == GEMM355_ACT_RELU)
+        return launch(gemm355::fp4::gemm_nvfp4_nt_kernel<gemm355::ACT_RELU>, p, stream);
+    if (act == GEMM355_ACT_GELU_TANH)
+        return launch(gemm355::fp4::gemm_nvfp4_nt_kernel<gemm355::ACT_GELU_TANH>, p, stream);
+    return launch(gemm355::fp4::gemm_nvfp4_nt_kernel<gemm355::ACT_NONE>, p, stream);
+}
+
+} // namespace
+
+extern "C" int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
+                             const void *SFB, void *C, void *stream)
+{
+    return fp4_product<false>(M, N, K, Aq, SFA, Bq, SFB, nullptr, GEMM355_ACT_NONE, C, stream);
+}
+
+extern "C" int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
+                                      const void *SFB, const void *bias, int activation, void *C, void *stream)
+{
+    return fp4_product<true>(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, stream);
 }
 
 extern "C" const char *gemm355_status_string(int status)

@@ -109,6 +109,9 @@ constexpr int CHUNK_EVERY = 3;   // matrix instructions per written chunk
 constexpr int LOADS = 8;         // staging loads per thread and step
 constexpr int LOAD_AT = 2;       // first of them (then one every 4 instructions)
 
+// EPI: EPI_PLAIN, or the activation of the fused epilogue (bias, then the
+// activation, before rounding).
+template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_nvfp4_nt_kernel(Problem p)
 {
@@ -149,6 +152,7 @@ void gemm_nvfp4_nt_kernel(Problem p)
     const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sfa, (unsigned)p.M * ks);
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.sfb, (unsigned)p.N * ks);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
+    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(p.bias, EPI != EPI_PLAIN && p.bias ? (unsigned)p.N * 2u : 0u);
     const int nk = (K + BK - 1) / BK;
 
     for (int round = 0;; ++round) {
@@ -285,7 +289,7 @@ void gemm_nvfp4_nt_kernel(Problem p)
                 step(kt, Int<1>{}, Int<0>{});
         }
 
-        store_tile(acc, rc, p.M, p.N, tm * BM + wm * 128, tn * BN + wn * 128, l32, half);
+        store_tile<EPI>(acc, rc, rbias, p.M, p.N, tm * BM + wm * 128, tn * BN + wn * 128, l32, half);
     }
 }
 

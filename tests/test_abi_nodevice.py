@@ -18,7 +18,8 @@ FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced
 def test_library_exports_every_declared_function():
     lib = g.load()
     names = g.declared_functions()
-    assert set(names) >= {"gemm_bf16_nt", "gemm_bf16_nt_bias_act", "gemm_nvfp4_nt", "gemm355_status_string",
+    assert set(names) >= {"gemm_bf16_nt", "gemm_bf16_nt_bias_act", "gemm_nvfp4_nt", "gemm_nvfp4_nt_bias_act",
+                          "gemm355_status_string",
                           "gemm355_tile_order", "gemm355_schedule"}
     for n in names:
         assert hasattr(lib, n), n
@@ -75,6 +76,20 @@ def test_fused_epilogue_rejections():
     assert _fused(8, 8, 64, bias=FAKE + 0x200000 + 64) == g.ERR_INVALID_ARG  # bias inside C
     # empty output with a valid activation: nothing to do
     assert _fused(0, 8, 64, act=g.ACT_GELU_TANH, a=None, b=None, bias=None, c=None) == g.OK
+
+
+def _fused4(M, N, K, act=0, bias=FAKE + 0x500000, c=FAKE + 0x400000):
+    return g.load().gemm_nvfp4_nt_bias_act(M, N, K, FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000,
+                                           bias, act, c, None)
+
+
+def test_fp4_fused_epilogue_rejections():
+    assert _fused4(8, 8, 32) == g.ERR_UNSUPPORTED                  # K % 64
+    for bad_act in (-1, 3):
+        assert _fused4(8, 8, 64, act=bad_act) == g.ERR_INVALID_ARG
+    assert _fused4(8, 8, 64, bias=FAKE + 0x500004) == g.ERR_UNSUPPORTED
+    assert _fused4(8, 8, 64, bias=FAKE + 0x400000 + 16) == g.ERR_INVALID_ARG   # bias inside C
+    assert _fused4(0, 8, 64, act=g.ACT_RELU, bias=None, c=None) == g.OK
 
 
 def test_extent_limits_are_exact():

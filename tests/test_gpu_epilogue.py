@@ -1,9 +1,9 @@
-"""gemm_bf16_nt_bias_act (bias and activation fused into the epilogue) against
-the oracle, through the C ABI: every BF16 instance forced in turn, each
-activation, ragged shapes element by element, split K with several splits
-(the reduction applies the epilogue), exactly summable inputs bitwise for the
-identity and ReLU, K = 0 (the activation of the bias), no bias, and the
-8192^3 workload on sampled elements.
+"""gemm_bf16_nt_bias_act and gemm_nvfp4_nt_bias_act (bias and activation
+fused into the epilogue) against the oracle, through the C ABI: every BF16
+instance forced in turn, each activation, ragged shapes element by element,
+split K with several splits (the reduction applies the epilogue), exactly
+summable inputs bitwise for the identity and ReLU, K = 0 (the activation of
+the bias), no bias, and the 8192^3 workloads on sampled elements.
 
 Reference: "NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue Warps" (the
 epilogue is where activations and element-wise operations would be fused).
@@ -131,4 +131,84 @@ def test_fused_workload_8192_sampled(act):
     ms, ns = sample_positions(M, N, 2000, seed=94)
     ref, z = oracle.gemm_bf16_nt_bias_act_at(A, B, bias, act, ms, ns, with_z=True)
     res = tolerance.check_fused(got[ms, ns], ref, z, K, act)
+    assert res, res
+
+
+# ---- block-scaled FP4 with the fused epilogue ------------------------------
+
+def run_fused4(ops, bias, act, M, N, K):
+    C = GuardedC(M, N)
+    g.gemm_nvfp4_nt_bias_act(M, N, K, *(to_dev(x) for x in ops), to_dev(bias) if bias is not None else None,
+                             act, C.view)
+    torch.cuda.synchronize()
+    assert C.guards_intact(), "write outside C"
+    return C.bits()
+
+
+def _sigma4(Aq, SFA, Bq, SFB, K):
+    return tolerance.sigma_of(oracle.decode_nvfp4(Aq, SFA, K)) * tolerance.sigma_of(oracle.decode_nvfp4(Bq, SFB, K))
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("M,N,K", [(300, 264, 512), (65, 72, 64), (520, 264, 1024)])
+def test_fp4_fused_matches_oracle(act, M, N, K):
+    need_gpu()
+    Aq, SFA = syn.fp4_operand(M, K, seed=M + K + act)
+    Bq, SFB = syn.fp4_operand(N, K, seed=N + K + 1)
+    sigma = _sigma4(Aq, SFA, Bq, SFB, K)
+    # bias on the scale of the sums, so the activations' bend is exercised
+    bias = syn.bf16_uniform(1, N, seed=N + 5, lo=-sigma * K ** 0.5, hi=sigma * K ** 0.5)[0]
+    got = run_fused4((Aq, SFA, Bq, SFB), bias, act, M, N, K)
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    ref, z = oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, bias, act, ms, ns, with_z=True)
+    res = tolerance.check_fused(got, ref.reshape(M, N), z.reshape(M, N), K, act, sigma)
+    assert res, res
+
+
+@pytest.mark.parametrize("act", [g.ACT_NONE, g.ACT_RELU])
+def test_fp4_fused_exact_inputs_bitwise(act):
+    # unit-exponent scales (1 + m/8, m <= 7) with K = 256: every partial sum
+    # is a multiple of 2^-8 below 2^15, exact in FP32, and so is the bias sum
+    need_gpu()
+    M, N, K = 264, 256, 256
+    Aq = syn.fp4_codes(M, K, seed=141)
+    Bq = syn.fp4_codes(N, K, seed=142)
+    SFA = syn.e4m3_scales(M, K, seed=143, u_lo=0, u_hi=0)
+    SFB = syn.e4m3_scales(N, K, seed=144, u_lo=0, u_hi=0)
+    bias = syn.bf16_sixteenths(1, N, seed=145, jmax=64)[0]
+    got = run_fused4((Aq, SFA, Bq, SFB), bias, act, M, N, K)
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    want = oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, bias, act, ms, ns).reshape(M, N)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_fp4_fused_empty_sum_is_activation_of_bias(act):
+    need_gpu()
+    M, N = 70, 72
+    bias = syn.bf16_uniform(1, N, seed=151, lo=-4.0, hi=4.0)[0]
+    ops = (np.zeros((M, 0), np.uint8), np.zeros((M, 0), np.uint8), np.zeros((N, 0), np.uint8),
+           np.zeros((N, 0), np.uint8))
+    C = GuardedC(M, N)
+    g.gemm_nvfp4_nt_bias_act(M, N, 0, None, None, None, None, to_dev(bias), act, C.view)
+    torch.cuda.synchronize()
+    assert C.guards_intact()
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    ref, z = oracle.gemm_nvfp4_nt_bias_act_at(*ops, 0, bias, act, ms, ns, with_z=True)
+    res = tolerance.check_fused(C.bits(), ref.reshape(M, N), z.reshape(M, N), 0, act)
+    assert res, res
+
+
+def test_fp4_fused_workload_8192_sampled():
+    need_gpu()
+    M = N = K = 8192
+    Aq, SFA = syn.fp4_operand(M, K, seed=161)
+    Bq, SFB = syn.fp4_operand(N, K, seed=162)
+    sub = slice(0, 256)
+    sigma = _sigma4(Aq[sub], SFA[sub], Bq[sub], SFB[sub], K)
+    bias = syn.bf16_uniform(1, N, seed=163, lo=-4096.0, hi=4096.0)[0]
+    got = run_fused4((Aq, SFA, Bq, SFB), bias, g.ACT_GELU_TANH, M, N, K)
+    ms, ns = sample_positions(M, N, 1500, seed=164)
+    ref, z = oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, bias, g.ACT_GELU_TANH, ms, ns, with_z=True)
+    res = tolerance.check_fused(got[ms, ns], ref, z, K, g.ACT_GELU_TANH, sigma)
     assert res, res
