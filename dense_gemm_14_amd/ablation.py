@@ -2,6 +2,7 @@
 
     python -m dense_gemm_14_amd.ablation instances [--csv FILE]
     python -m dense_gemm_14_amd.ablation supergroup [--csv FILE]
+    python -m dense_gemm_14_amd.ablation streams [--csv FILE]
 
 ``instances`` times the three BF16 instances (forced through
 gemm355_force_instance) and the automatic choice on the shape grid
@@ -11,6 +12,11 @@ restricted to shapes with fewer 256 x 256 tiles than 256, plus skinny and mid
 shapes. ``supergroup`` times the band width of the visiting order
 (gemm355_force_supergroup; the page's "Supergroup Size" ablation) on the
 large shapes M, N in {4096, 8192, 16384}, K in {1024, 4096, 16384}.
+``streams`` times independent back-to-back products issued on one stream
+against the same products alternating over two streams, which lets one
+product's workgroups start on units the other's tail leaves idle (the
+question of "Kernel 6", "The Gap Between Grids", without programmatic
+dependent launch).
 
 Every configuration of a shape is timed in three round-robin passes and the
 minimum kept (the first configuration timed on fresh buffers runs slow).
@@ -112,16 +118,52 @@ def supergroup(csv):
                 csv.write("%d,%d,%d,%d,%.2f\n" % (*shp, w, us))
 
 
+STREAM_SHAPES = [(8192, 8192, 8192), (4096, 4096, 4096), (3072, 3072, 3072), (2048, 2048, 2048),
+                 (128, 8192, 8192), (8192, 8192, 1024)]
+
+
+def streams(csv):
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    print("#     M      N      K   one stream   two streams   gain   [us per product, min of 3 passes]")
+    for M, N, K in STREAM_SHAPES:
+        sets = _sets(M, N, K)
+        n = len(sets)
+        reps = 200 if M * N * K < 1e11 else 100
+        best = {}
+        for _ in range(3):
+            for mode in ("one", "two"):
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s0)
+                s1.wait_event(e0)
+                for i in range(reps):
+                    A, B, C = sets[i % n]
+                    g.gemm_bf16_nt(M, N, K, A, B, C, stream=s1 if (mode == "two" and i % 2) else s0)
+                done = torch.cuda.Event()
+                done.record(s1)
+                s0.wait_event(done)
+                e1.record(s0)
+                torch.cuda.synchronize()
+                best[mode] = min(best.get(mode, float("inf")), e0.elapsed_time(e1) / reps * 1e3)
+        print("%7d %6d %6d  %10.1f  %12.1f  %+5.1f%%" % (M, N, K, best["one"], best["two"],
+                                                        100 * (best["one"] / best["two"] - 1)), flush=True)
+        if csv:
+            csv.write("%d,%d,%d,%.2f,%.2f\n" % (M, N, K, best["one"], best["two"]))
+        del sets
+        torch.cuda.empty_cache()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("what", choices=["instances", "supergroup"])
+    ap.add_argument("what", choices=["instances", "supergroup", "streams"])
     ap.add_argument("--csv", default=None, help="also write M,N,K,config,us rows here")
     args = ap.parse_args(argv)
     if not torch.cuda.is_available():
         sys.exit("the ablation needs a GPU")
     csv = open(args.csv, "w") if args.csv else None
     try:
-        (instances if args.what == "instances" else supergroup)(csv)
+        {"instances": instances, "supergroup": supergroup, "streams": streams}[args.what](csv)
     finally:
         if csv:
             csv.close()
