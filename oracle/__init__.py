@@ -87,6 +87,12 @@ def _bind(lib):
     lib.oracle_gemm_bf16_nt_bias_act_at.restype = i
     lib.oracle_gemm_nvfp4_nt_bias_act_at.argtypes = [i, i, i, p, p, p, p, p, i, ctypes.c_long, p, p, p, p]
     lib.oracle_gemm_nvfp4_nt_bias_act_at.restype = i
+    lib.oracle_e8m0_to_double.argtypes = [ctypes.c_uint]
+    lib.oracle_e8m0_to_double.restype = ctypes.c_double
+    lib.oracle_gemm_mxfp4_nt.argtypes = [i, i, i, p, p, p, p, p]
+    lib.oracle_gemm_mxfp4_nt.restype = i
+    lib.oracle_gemm_mxfp4_nt_at.argtypes = [i, i, i, p, p, p, p, ctypes.c_long, p, p, p, p]
+    lib.oracle_gemm_mxfp4_nt_at.restype = i
     lib.oracle_decode_nvfp4.argtypes = [i, i, p, p, p]
     lib.oracle_decode_nvfp4.restype = i
     lib.oracle_max_threads.argtypes = []
@@ -266,6 +272,44 @@ def gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K: int, bias, act: int, ms, ns, 
                                                 _ptr(ms), _ptr(ns), _ptr(out), _ptr(zs)),
            "gemm_nvfp4_nt_bias_act_at")
     return (out, zs) if with_z else out
+
+
+def e8m0_to_double(byte: int) -> float:
+    return _load().oracle_e8m0_to_double(int(byte))
+
+
+def _shape_mx(Q, S, rows, K):
+    if K % 32:
+        raise ValueError("K must be a multiple of 32 for one scale per 32 elements")
+    if Q.shape != (rows, K // 2) or S.shape != (rows, K // 32):
+        raise ValueError("MXFP4 operand shapes do not match K=%d: codes %s, scales %s" % (K, Q.shape, S.shape))
+
+
+def gemm_mxfp4_nt(Aq, SA, Bq, SB, K: int) -> np.ndarray:
+    """C = bf16(dec(A) @ dec(B)^T) for E2M1 codes with one E8M0 scale per 32
+    elements: Aq (M, K/2), SA (M, K/32), Bq (N, K/2), SB (N, K/32), uint8."""
+    lib = _load()
+    Aq, SA, Bq, SB = (_c(x, np.uint8) for x in (Aq, SA, Bq, SB))
+    M, N = Aq.shape[0], Bq.shape[0]
+    _shape_mx(Aq, SA, M, K)
+    _shape_mx(Bq, SB, N, K)
+    C = np.empty((M, N), dtype=np.uint16)
+    _check(lib.oracle_gemm_mxfp4_nt(M, N, K, _ptr(Aq), _ptr(SA), _ptr(Bq), _ptr(SB), _ptr(C)), "gemm_mxfp4_nt")
+    return C
+
+
+def gemm_mxfp4_nt_at(Aq, SA, Bq, SB, K: int, ms, ns, with_sum: bool = False):
+    lib = _load()
+    Aq, SA, Bq, SB = (_c(x, np.uint8) for x in (Aq, SA, Bq, SB))
+    M, N = Aq.shape[0], Bq.shape[0]
+    _shape_mx(Aq, SA, M, K)
+    _shape_mx(Bq, SB, N, K)
+    ms, ns = _idx(ms, ns)
+    out = np.empty(ms.size, dtype=np.uint16)
+    sums = np.empty(ms.size, dtype=np.float64)
+    _check(lib.oracle_gemm_mxfp4_nt_at(M, N, K, _ptr(Aq), _ptr(SA), _ptr(Bq), _ptr(SB), ms.size, _ptr(ms), _ptr(ns),
+                                       _ptr(out), _ptr(sums)), "gemm_mxfp4_nt_at")
+    return (out, sums) if with_sum else out
 
 
 def _shape_fp4(Q, SF, rows, K):

@@ -119,6 +119,17 @@ double oracle_e4m3_to_double(unsigned byte)
     return s ? -mag : mag;
 }
 
+/* E8M0 (the shared scale of the microscaling formats, a reading outside the
+ * pages -- see the MX product below): the byte is a biased exponent alone,
+ * value 2^(byte - 127); 0xFF is NaN. */
+double oracle_e8m0_to_double(unsigned byte)
+{
+    byte &= 255u;
+    if (byte == 255u)
+        return NAN;
+    return ldexp(1.0, (int)byte - 127);
+}
+
 /* Array forms of the two BF16 codecs (same scalar routines, element by element). */
 void oracle_bf16_to_double_n(const uint16_t *bits, double *out, long n)
 {
@@ -148,6 +159,15 @@ static double fp4_elem(const uint8_t *Q, const uint8_t *SF, long K, long row, lo
     return oracle_e2m1_to_double(code) * oracle_e4m3_to_double(SF[row * (K / 16) + k / 16]);
 }
 
+/* Microscaled FP4 element: the same E2M1 codes and nibble order, one E8M0
+ * scale per 32 consecutive elements of a row (K/32 bytes per row). */
+static double mx_elem(const uint8_t *Q, const uint8_t *S, long K, long row, long k)
+{
+    uint8_t byte = Q[row * (K / 2) + k / 2];
+    unsigned code = (k & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u);
+    return oracle_e2m1_to_double(code) * oracle_e8m0_to_double(S[row * (K / 32) + k / 32]);
+}
+
 static double dot_bf16(const uint16_t *A, const uint16_t *B, long K, long m, long n)
 {
     double s = 0.0;
@@ -162,6 +182,15 @@ static double dot_fp4(const uint8_t *Aq, const uint8_t *SFA, const uint8_t *Bq,
     double s = 0.0;
     for (long k = 0; k < K; ++k)
         s += fp4_elem(Aq, SFA, K, m, k) * fp4_elem(Bq, SFB, K, n, k);
+    return s;
+}
+
+static double dot_mx(const uint8_t *Aq, const uint8_t *SA, const uint8_t *Bq, const uint8_t *SB, long K,
+                     long m, long n)
+{
+    double s = 0.0;
+    for (long k = 0; k < K; ++k)
+        s += mx_elem(Aq, SA, K, m, k) * mx_elem(Bq, SB, K, n, k);
     return s;
 }
 
@@ -313,6 +342,46 @@ int oracle_gemm_nvfp4_nt_bias_act_at(int M, int N, int K, const uint8_t *Aq, con
         out_bf16[i] = oracle_bf16_from_double(oracle_activate(z, act));
         if (out_z)
             out_z[i] = z;
+    }
+    return ORACLE_OK;
+}
+
+/* ---- microscaled FP4 (MXFP4) ---------------------------------------------
+ * Not a format of the pages, which define the FP4 variant with an E4M3 scale
+ * per 16 elements; this is the format the gfx950 matrix cores scale in
+ * hardware (the microscaling convention: E2M1 elements, one power-of-two E8M0
+ * scale per 32 elements). The product is the plain definition as for the
+ * other formats:
+ *     C[m][n] = bf16_round_nearest_even( sum_k a(m,k) b(n,k) ),
+ *     a(m,k) = e2m1(code(m,k)) * 2^(SA[m][k/32] - 127),
+ * K % 32 == 0, every product exact in binary64. */
+int oracle_gemm_mxfp4_nt(int M, int N, int K, const uint8_t *Aq, const uint8_t *SA, const uint8_t *Bq,
+                         const uint8_t *SB, uint16_t *C)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0)
+        return ORACLE_BAD_ARGS;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long m = 0; m < M; ++m)
+        for (long n = 0; n < N; ++n)
+            C[m * (long)N + n] = oracle_bf16_from_double(dot_mx(Aq, SA, Bq, SB, K, m, n));
+    return ORACLE_OK;
+}
+
+int oracle_gemm_mxfp4_nt_at(int M, int N, int K, const uint8_t *Aq, const uint8_t *SA, const uint8_t *Bq,
+                            const uint8_t *SB, long count, const int32_t *ms, const int32_t *ns,
+                            uint16_t *out_bf16, double *out_sum)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || count < 0)
+        return ORACLE_BAD_ARGS;
+    for (long i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N)
+            return ORACLE_BAD_ARGS;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < count; ++i) {
+        double s = dot_mx(Aq, SA, Bq, SB, K, ms[i], ns[i]);
+        out_bf16[i] = oracle_bf16_from_double(s);
+        if (out_sum)
+            out_sum[i] = s;
     }
     return ORACLE_OK;
 }

@@ -17,6 +17,8 @@ Workload recipes
   * FP4 scales: one byte per 16 consecutive K of a row, ``((u + 7) << 3) | m``
     with integer u uniform in [-4, 4] and m uniform in 0..7, i.e. the E4M3
     value 2^u * (1 + m/8).
+  * MXFP4 (microscaled FP4): the same codes; one E8M0 byte per 32
+    consecutive K of a row, 127 + u with integer u uniform in [-4, 4].
   * Rotation sets: seed = 1000 * config_index + set_index.
 """
 from __future__ import annotations
@@ -104,6 +106,20 @@ def e4m3_scales(rows: int, K: int, seed: int, u_lo: int = -4, u_hi: int = 4,
 def fp4_operand(rows: int, K: int, seed: int):
     """(codes, scales) for one block-scaled FP4 operand of the workload recipe."""
     return fp4_codes(rows, K, seed), e4m3_scales(rows, K, seed + 7919)
+
+
+def e8m0_scales(rows: int, K: int, seed: int, u_lo: int = -4, u_hi: int = 4) -> np.ndarray:
+    """(rows, K/32) E8M0 bytes 127 + u with integer u uniform in [u_lo, u_hi],
+    i.e. the power-of-two scale 2^u of each 32-element block."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    return (127 + rng(seed).integers(u_lo, u_hi + 1, size=(rows, K // 32))).astype(np.uint8)
+
+
+def mxfp4_operand(rows: int, K: int, seed: int):
+    """(codes, scales) for one microscaled FP4 operand: the FP4 workload's codes
+    with an E8M0 scale 2^u, u uniform in [-4, 4], per 32 elements."""
+    return fp4_codes(rows, K, seed), e8m0_scales(rows, K, seed + 7919)
 
 
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:
