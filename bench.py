@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 LLC_BYTES = 256 << 20                  # MI355X Infinity Cache (last-level cache)
-PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # published dense MFMA peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp4": 10100.0}  # published dense MFMA peaks
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {
@@ -47,11 +47,14 @@ WORKLOADS = {
     "fp4_8192": ("fp4", 8192, 8192, 8192),
     # the same product with the fused epilogue: C = gelu(A B^T + bias)
     "bf16_gelu_8192": ("bf16_gelu", 8192, 8192, 8192),
+    # microscaled FP4 (E2M1 codes, E8M0 scale per 32) on the scaled matrix instructions
+    "mx_8192": ("mx", 8192, 8192, 8192),
 }
 CONFIG_INDEX = {"bf16_256": 0, "bf16_4096": 1, "bf16_8192": 2, "bf16_8000": 3, "bf16_skinny": 3,
-                "fp4_8192": 4, "bf16_gelu_8192": 2}
+                "fp4_8192": 4, "bf16_gelu_8192": 2, "mx_8192": 4}
 # BF16 kernels are templates over the epilogue: -1 plain, 2 bias + tanh-form GELU
 KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel<%d>", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel",
+               "mx": "gemm355::mx::gemm_mxfp4_nt_kernel<-1>",
                "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel<%d>",
                "bf16_splitk": "gemm355::bf16_splitk::gemm_bf16_nt_splitk_kernel<%d>",
                "bf16_splitk_reduce": "gemm355::bf16_splitk::splitk_reduce_kernel<%d>"}
@@ -61,7 +64,7 @@ EPILOGUE = {"bf16": -1, "bf16_gelu": 2}
 def kernels_for(kind: str, M: int, N: int, K: int, compute_units: int = 256) -> list:
     """The kernels gemm_bf16_nt / gemm_bf16_nt_bias_act / gemm_nvfp4_nt launch
     for this shape, in launch order (the library's own choice, gemm355_bf16_plan)."""
-    if kind == "fp4":
+    if kind in ("fp4", "mx"):
         return [KERNEL_NAME[kind]]
     import dense_gemm_14_amd as g
     instance, splits = g.bf16_plan(M, N, K, compute_units)
@@ -89,6 +92,8 @@ def set_bytes(kind, M, N, K):
         return 2 * (M * K + N * K + M * N)
     if kind == "bf16_gelu":
         return 2 * (M * K + N * K + M * N + N)   # plus the bias
+    if kind == "mx":
+        return M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + 2 * M * N
     return M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + 2 * M * N
 
 
@@ -112,8 +117,9 @@ def make_sets(kind, M, N, K, n_sets, cfg):
                 bias = syn.bf16_uniform(1, N, seed + 900, lo=-32.0, hi=32.0)[0]
                 ops = (A, B, torch.from_numpy(bias.view(np.int16)).cuda())
         else:
-            Aq, SFA = syn.fp4_operand(M, K, seed)
-            Bq, SFB = syn.fp4_operand(N, K, seed + 500)
+            operand = syn.mxfp4_operand if kind == "mx" else syn.fp4_operand
+            Aq, SFA = operand(M, K, seed)
+            Bq, SFB = operand(N, K, seed + 500)
             ops = tuple(torch.from_numpy(x).cuda() for x in (Aq, SFA, Bq, SFB))
         C = torch.empty(M * N, dtype=torch.int16, device="cuda")
         sets.append((ops, C))
@@ -127,6 +133,8 @@ def launcher(kind, M, N, K, stream):
     if kind == "bf16_gelu":
         return lambda ops, C: g.gemm_bf16_nt_bias_act(M, N, K, ops[0], ops[1], ops[2], g.ACT_GELU_TANH, C,
                                                       stream=stream)
+    if kind == "mx":
+        return lambda ops, C: g.gemm_mxfp4_nt(M, N, K, *ops, C, stream=stream)
     return lambda ops, C: g.gemm_nvfp4_nt(M, N, K, *ops, C, stream=stream)
 
 
@@ -162,6 +170,9 @@ def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
     elif kind == "bf16_gelu":
         A, B, bias = (h.view(np.uint16) for h in host)
         fn = lambda ms, ns: oracle.gemm_bf16_nt_bias_act_at(A, B, bias, oracle.ACT_GELU_TANH, ms, ns, with_z=True)
+    elif kind == "mx":
+        Aq, SA, Bq, SB = host
+        fn = lambda ms, ns: oracle.gemm_mxfp4_nt_at(Aq, SA, Bq, SB, K, ms, ns)
     else:
         Aq, SFA, Bq, SFB = host
         fn = lambda ms, ns: oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns)
@@ -187,6 +198,14 @@ def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
         sub = slice(0, min(M, 256))
         sigma = (tolerance.sigma_of(oracle.decode_nvfp4(host[0][sub], host[1][sub], K)) *
                  tolerance.sigma_of(oracle.decode_nvfp4(host[2][sub], host[3][sub], K)))
+    if kind == "mx":
+        # decoded rows from the oracle's per-code and per-scale values
+        e2 = np.array([oracle.e2m1_to_double(c) for c in range(16)])
+        e8 = np.array([oracle.e8m0_to_double(b) if b != 0xFF else np.nan for b in range(256)])
+        def dec(Q, S):
+            Q, S = Q[:256], S[:256]
+            return e2[np.stack([Q & 15, Q >> 4], -1).reshape(Q.shape[0], -1)] * np.repeat(e8[S], 32, axis=1)
+        sigma = tolerance.sigma_of(dec(host[0], host[1])) * tolerance.sigma_of(dec(host[2], host[3]))
     if kind == "bf16_gelu":
         chk = tolerance.check_fused(got, ref, z, K, oracle.ACT_GELU_TANH)
     else:
@@ -271,7 +290,8 @@ def main(argv=None):
     run(*sets[0])
     torch.cuda.synchronize()
 
-    dtype = "fp16" if kind == "fp4" else "bf16"  # FP4 operands are decoded to FP16 for the MFMA
+    # NVFP4 operands are decoded to FP16 for the MFMA; MX operands enter it as FP4
+    dtype = {"fp4": "fp16", "mx": "fp4"}.get(kind, "bf16")
     traffic = read_traffic(args.workload, flops)
     alg_bytes = algorithmic_bytes(kind, M, N, K)
     ridge = PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
@@ -299,7 +319,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4(e2m1+e4m3)->fp16" if kind == "fp4" else "bf16",
+        "dtype": {"fp4": "fp4(e2m1+e4m3)->fp16", "mx": "fp4(e2m1+e8m0)"}.get(kind, "bf16"),
         "data": "synthetic",
         "config": {"workload": "%s_nt_%dx%dx%d" % (kind, M, N, K), "M": M, "N": N, "K": K,
                    "rotation_sets": n_sets, "footprint_MiB": round(n_sets * per_set / 2 ** 20, 1),

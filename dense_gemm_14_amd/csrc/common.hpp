@@ -158,17 +158,18 @@ __device__ inline void schedule_reads_with_mma()
 //
 // EPI: EPI_PLAIN, or the activation of the fused epilogue, applied with the
 // bias of each column (rbias: N BF16 values; an empty range reads zeros).
-template <int EPI>
-__device__ inline void store_tile(f32x16 (&acc)[4][4], const __amdgpu_buffer_rsrc_t &rc,
+// BI x BJ blocks of 32 x 32 (the wave's tile is 32 BI x 32 BJ).
+template <int EPI, int BI, int BJ>
+__device__ inline void store_tile(f32x16 (&acc)[BI][BJ], const __amdgpu_buffer_rsrc_t &rc,
                                   const __amdgpu_buffer_rsrc_t &rbias, int M, int N, int m0, int n0, int l32,
                                   int half)
 {
     // fused: bias[n .. n + 3] of this lane's four-column runs, [j][g], columns
     // n0 + 32 j + 8 g + 4 half
-    u32x2 bias_w[4][4];
+    u32x2 bias_w[BJ][4];
     if constexpr (EPI != EPI_PLAIN) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < BJ; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + 32 * j + 8 * g + 4 * half;
@@ -176,10 +177,10 @@ __device__ inline void store_tile(f32x16 (&acc)[4][4], const __amdgpu_buffer_rsr
             }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < BI; ++i) {
         const int m = m0 + i * 32 + l32;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < BJ; ++j) {
             const int nb = n0 + j * 32;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {

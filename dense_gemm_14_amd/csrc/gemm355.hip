@@ -13,6 +13,7 @@
 #include "gemm_bf16.hpp"
 #include "gemm_bf16_small.hpp"
 #include "gemm_bf16_splitk.hpp"
+#include "gemm_mxfp4.hpp"
 #include "gemm_fp4.hpp"
 #include "schedule.hpp"
 
@@ -424,6 +425,39 @@ extern "C" int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const
                                       const void *SFB, const void *bias, int activation, void *C, void *stream)
 {
     return fp4_product<true>(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, stream);
+}
+
+extern "C" int gemm_mxfp4_nt(int M, int N, int K, const void *Aq, const void *SA, const void *Bq, const void *SB,
+                             void *C, void *stream)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM355_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return GEMM355_OK;
+    if (!C || (K > 0 && (!Aq || !SA || !Bq || !SB)))
+        return GEMM355_ERR_INVALID_ARG;
+    const size_t c_bytes = size_t(M) * size_t(N) * 2;
+    if (K > 0 && (overlaps(C, c_bytes, Aq, size_t(M) * K / 2) || overlaps(C, c_bytes, Bq, size_t(N) * K / 2) ||
+                  overlaps(C, c_bytes, SA, size_t(M) * K / 32) || overlaps(C, c_bytes, SB, size_t(N) * K / 32)))
+        return GEMM355_ERR_INVALID_ARG;
+    if (!aligned(Aq, 16) || !aligned(Bq, 16) || !aligned(C, 16) || !aligned(SA, 16) || !aligned(SB, 16))
+        return GEMM355_ERR_UNSUPPORTED;
+    if (K % 512 != 0 || N % 8 != 0)
+        return GEMM355_ERR_UNSUPPORTED;
+    if (!extent_ok(M, int64_t(K) / 2) || !extent_ok(N, int64_t(K) / 2) || !extent_ok(M, int64_t(N) * 2))
+        return GEMM355_ERR_UNSUPPORTED;
+
+    Problem p = {};
+    p.a = Aq;
+    p.b = Bq;
+    p.sfa = SA;
+    p.sfb = SB;
+    p.c = C;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    return launch(gemm355::mx::gemm_mxfp4_nt_kernel<gemm355::EPI_PLAIN>, p, stream, gemm355::mx::TM,
+                  gemm355::mx::TN);
 }
 
 extern "C" const char *gemm355_status_string(int status)

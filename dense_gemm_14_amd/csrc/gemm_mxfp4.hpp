@@ -1,0 +1,354 @@
+// gemm_mxfp4.hpp -- microscaled FP4 NT GEMM for gfx950 on the matrix cores'
+// own block scaling: E2M1 codes (two per byte, even k in the low nibble) with
+// one E8M0 (power-of-two) scale per 32 consecutive K elements of a row, fed
+// undecoded to v_mfma_scale_f32_32x32x64_f8f6f4, which multiplies 64 K of a
+// 32 x 32 block at four times the BF16 rate and applies each lane's scale to
+// the 32 elements it holds.
+//
+// The format is not the pages' (their FP4 variant scales every 16 elements by
+// an E4M3 value, "NVFP4 GEMM on Blackwell", section "NVFP4 Datatype", which
+// has mantissa bits the hardware scaling cannot apply); it is the one whose
+// scales the matrix cores take as operands, the MI355X counterpart of the
+// page's block-scaled MMA with scales applied inside the instruction.
+//
+// Work decomposition
+//   * Output tile 256 x 256 per workgroup, 4 waves in 2 x 2, each wave 128 x
+//     128 = 4 x 4 blocks of 32 x 32 (256 accumulation registers per lane).
+//   * K advances 128 per step: 64 bytes of codes per row (the LDS row) and 4
+//     scale bytes. A stage holds the A and B code tiles (16 KiB each) and
+//     their scale rows (1 KiB each, row-major); four stages (136 KiB) form a
+//     ring that runs on across the workgroup's tiles, so the next tile's first
+//     steps are copied while the current one finishes. Code rows are 64 bytes:
+//     logical 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3), so
+//     the 16 rows a fragment read serves per cycle at one chunk cover the 16
+//     bank groups of 256 bytes.
+//   * Copies are LDS-DMA only (no registers carry operands): per step and
+//     wave, four 1 KiB code copies of A (rows 64 w .. 64 w + 63, 16 rows
+//     each), four of B, and one 256-byte scale copy of each. Step k + 3 is
+//     requested during step k, after the barrier that frees step k - 1's
+//     stage, one copy every three matrix instructions (issued together they
+//     stall the wave for most of a step).
+//   * Per step each wave issues 32 matrix instructions (2 sub-steps of K 64 x
+//     4 x 4 blocks). Fragment reads (16 bytes per lane: row l % 32 of a block,
+//     the 32 K of sub-step kk that belong to lane half l / 32) of sub-step 1
+//     are issued during sub-step 0, those of the next step's sub-step 0 (and
+//     its scales) during sub-step 1.
+//   * A lane's scale for sub-step kk is byte 2 kk + l / 32 of its row's 4;
+//     each row's scale dword is shifted right by 8 (l / 32) once per step, so
+//     that byte 2 kk is the lane's scale in both halves and the instruction's
+//     byte select stays a constant.
+#pragma once
+
+#include "common.hpp"
+
+#include <utility>
+
+namespace gemm355 {
+namespace mx {
+
+constexpr int TM = 256;                          // output tile rows
+constexpr int TN = 256;                          // output tile columns
+constexpr int BK = 128;                          // K elements per step
+constexpr int ROW_BYTES = BK / 2;                // 64 bytes of codes per row and step
+constexpr int CODE_UNIT = TM * ROW_BYTES;        // 16 KiB
+constexpr int SCALE_ROW = BK / 32;               // 4 scale bytes per row and step
+constexpr int A_CODES = 0, B_CODES = CODE_UNIT;
+constexpr int STAGE_BYTES = 2 * CODE_UNIT;       // A then B codes of one step
+constexpr int STAGES = 4;
+// Scales travel in blocks of four steps: 16 bytes per row (one 16-byte lane
+// of a copy; a copy per step of 4 bytes per row touches a cache line per row
+// and costs as much as all the code copies). Two blocks form their own ring.
+constexpr int SCALE_STEPS = 4;
+constexpr int SCALE_BLOCK_ROW = SCALE_STEPS * SCALE_ROW;   // 16 bytes
+constexpr int SCALE_BLOCK = 2 * TM * SCALE_BLOCK_ROW;     // A then B: 8 KiB
+constexpr int SCALES_BASE = STAGES * STAGE_BYTES;
+constexpr int LDS_BYTES = SCALES_BASE + 2 * SCALE_BLOCK;
+constexpr int COPIES = 8;                        // code copies per wave and step (4 + 4)
+constexpr int SCALE_COPIES = 2;                  // per wave and scale block (A, B)
+constexpr int EPILOGUE_STORES = 32;              // 16-byte stores per wave per tile (128 x 128 BF16)
+
+static_assert(LDS_BYTES <= 163840, "LDS ring exceeds the 160 KiB of a gfx950 workgroup");
+static_assert(TM == 256 && TN == 256 && THREADS == 256, "the copy map assumes 256 x 256 tiles and 4 waves");
+// in flight at most: the copies of three steps ahead and one epilogue
+static_assert((STAGES - 1) * COPIES + SCALE_COPIES + EPILOGUE_STORES <= 63,
+              "vmcnt counts at most 63 outstanding operations");
+
+// Physical 16-byte chunk position of logical chunk c (0..3) in tile row r.
+__device__ inline int swizzle(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline i32x4 rsrc_words(const void *p, unsigned bytes)
+{
+    const unsigned long long a = reinterpret_cast<unsigned long long>(p);
+    return i32x4{(int)(unsigned)a, (int)(unsigned)(a >> 32), (int)bytes, (int)RSRC_WORD3};
+}
+
+// Resources start SHIFT bytes before their operand (and span SHIFT bytes
+// more) so that per-lane offsets less an instruction offset stay non-negative;
+// OOB_SHIFTED lies past every range and stays below 2^32 after any
+// instruction and scalar offset is added (operand extents, and so scalar K
+// offsets, are below 2^31).
+constexpr int SHIFT = 3072;
+constexpr unsigned OOB_SHIFTED = 0x80000000u;
+
+// m0 = LDS base of the following copies; one wait state before LDS-DMA.
+__device__ inline void set_m0(unsigned lds_addr) { asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" ::"s"(lds_addr) : "memory", "m0"); }
+
+// 1 KiB copy: lane i's 16 bytes at buffer offset voff + soff + IMM land at
+// LDS byte m0 + IMM + 16 i. Rows past the operand have voff past its range;
+// the scalar K offset soff (at most the row length) keeps them there.
+template <int IMM>
+__device__ inline void copy_1k(const i32x4 &rsrc, unsigned voff, int soff)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds" ::"v"(voff), "s"(rsrc), "s"(soff), "n"(IMM) : "memory");
+}
+
+__device__ inline void wait_all_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ inline void wait_copies_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Kernel arguments: Problem with a, b the codes and sfa, sfb the E8M0 scales.
+// EPI: EPI_PLAIN, or the activation of the fused epilogue.
+template <int EPI>
+__global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
+void gemm_mxfp4_nt_kernel(Problem p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1;   // 128-row half of the tile (A rows)
+    const int wn = wave >> 1;  // 128-column half (B rows)
+    const int l32 = lane & 31;
+    const int half = lane >> 5;
+    const int K = p.K;
+    const unsigned kb = (unsigned)K / 2;       // code bytes per row
+    const unsigned sb = (unsigned)K / 32;      // scale bytes per row
+    const int nk = (K + BK - 1) / BK;
+
+    const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
+    const i32x4 ra = rsrc_words(static_cast<const uint8_t *>(p.a) - SHIFT, (unsigned)p.M * kb + SHIFT);
+    const i32x4 rb = rsrc_words(static_cast<const uint8_t *>(p.b) - SHIFT, (unsigned)p.N * kb + SHIFT);
+    const i32x4 rsa = rsrc_words(static_cast<const uint8_t *>(p.sfa) - SHIFT, (unsigned)p.M * sb + SHIFT);
+    const i32x4 rsb = rsrc_words(static_cast<const uint8_t *>(p.sfb) - SHIFT, (unsigned)p.N * sb + SHIFT);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
+    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(p.bias, EPI != EPI_PLAIN && p.bias ? (unsigned)p.N * 2u : 0u);
+
+    // Copy map. Code copy t (0..3) of an operand: tile rows 64 wave + 16 t +
+    // lane / 4, lane position lane % 4 of the row, which fetches logical chunk
+    // (lane % 4) ^ swizzle; scale copy: tile row 64 wave + lane, its 16 bytes
+    // of a block of four steps.
+    // Per-lane offsets are set per tile (rows past M or N lie past the buffer
+    // and read zeros; a round without a tile reads zeros throughout); the
+    // step's K offset is the scalar offset.
+    const int copy_row = lane >> 2;
+    const int srow = 64 * wave + lane;
+    int chunk_b[4];   // byte offset (within the step's 64) of each code copy's chunk
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        chunk_b[t] = 16 * swizzle(64 * wave + 16 * t + copy_row, lane & 3);
+
+    // Per-lane copy offsets of the current tile (rows past M or N lie past
+    // the buffer and read zeros); the step's K offset is the scalar offset,
+    // and steps past K (requested ahead of the tile's end) read zeros.
+    unsigned a_off[4], b_off[4], sa_off, sb_off;
+    auto set_tile = [&](int tm, int tn) {
+        const int am = tm * TM, bn = tn * TN;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int row = 64 * wave + 16 * t + copy_row;
+            a_off[t] = (unsigned)(am + row) * kb + (unsigned)chunk_b[t] + SHIFT - 1024u * t;
+            b_off[t] = (unsigned)(bn + row) * kb + (unsigned)chunk_b[t] + SHIFT - 1024u * t;
+        }
+        sa_off = (unsigned)(am + srow) * sb + SHIFT;
+        sb_off = (unsigned)(bn + srow) * sb + SHIFT;
+    };
+    // Copy q (0..7) of K step k of the current tile into stage `stage`:
+    // q 0..3 A codes, 4..7 B codes, each group after one m0 write.
+    auto copy_one = [&](int k, int stage, int q) {
+        const unsigned base = lds_base + (unsigned)(stage * STAGE_BYTES);
+        const bool in = k < nk;
+        const int ko = in ? k * ROW_BYTES : 0;
+        switch (q) {
+        case 0: set_m0(__builtin_amdgcn_readfirstlane(base + A_CODES + 4096 * wave));
+                copy_1k<0>(ra, in ? a_off[0] : OOB_SHIFTED, ko); break;
+        case 1: copy_1k<1024>(ra, in ? a_off[1] : OOB_SHIFTED, ko); break;
+        case 2: copy_1k<2048>(ra, in ? a_off[2] : OOB_SHIFTED, ko); break;
+        case 3: copy_1k<3072>(ra, in ? a_off[3] : OOB_SHIFTED, ko); break;
+        case 4: set_m0(__builtin_amdgcn_readfirstlane(base + B_CODES + 4096 * wave));
+                copy_1k<0>(rb, in ? b_off[0] : OOB_SHIFTED, ko); break;
+        case 5: copy_1k<1024>(rb, in ? b_off[1] : OOB_SHIFTED, ko); break;
+        case 6: copy_1k<2048>(rb, in ? b_off[2] : OOB_SHIFTED, ko); break;
+        default: copy_1k<3072>(rb, in ? b_off[3] : OOB_SHIFTED, ko); break;
+        }
+    };
+    // Scale block b (steps 4 b .. 4 b + 3) of the current tile into scale
+    // slot b % 2: A rows, then B rows 4 KiB on (K % 512 == 0: every block is
+    // whole; blocks past K read zeros).
+    auto copy_scales = [&](int b) {
+        const unsigned base = lds_base + (unsigned)(SCALES_BASE + (b & 1) * SCALE_BLOCK);
+        const bool in = b * SCALE_STEPS < nk;
+        const int so = in ? b * SCALE_BLOCK_ROW : 0;
+        set_m0(__builtin_amdgcn_readfirstlane(base + 1024 * wave));
+        copy_1k<0>(rsa, in ? sa_off : OOB_SHIFTED, so);
+        set_m0(__builtin_amdgcn_readfirstlane(base + TM * SCALE_BLOCK_ROW + 1024 * wave));
+        copy_1k<0>(rsb, in ? sb_off : OOB_SHIFTED, so);
+    };
+    auto copy_step = [&](int k, int stage) {
+#pragma unroll
+        for (int q = 0; q < COPIES; ++q)
+            copy_one(k, stage, q);
+    };
+
+    // Fragments: [buffer][block] 16 bytes (the instruction reads the low four
+    // dwords of an eight-dword FP4 operand); scales [buffer][block] as two
+    // dwords, pre-shifted for the lane's half. A and B rows of a lane have the
+    // same swizzle (they differ by multiples of 32), so one set of chunk
+    // offsets serves both.
+    i32x4 fa[2][4], fb[2][4];
+    unsigned sa[2][4], sbv[2][4];
+    const int a_row0 = 128 * wm + l32, b_row0 = 128 * wn + l32;   // block 0 rows; block i is 32 i rows on
+    int kofs[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        kofs[kk] = swizzle(l32, 2 * kk + half) << 4;
+    int a_frag = A_CODES + a_row0 * ROW_BYTES, b_frag = B_CODES + b_row0 * ROW_BYTES;
+    int a_sc = SCALES_BASE + a_row0 * SCALE_BLOCK_ROW, b_sc = SCALES_BASE + TM * SCALE_BLOCK_ROW + b_row0 * SCALE_BLOCK_ROW;
+    // fragment read r (0..7) of sub-step kk: A block r for r < 4, else B block r - 4
+    auto read_frag = [&](int stage, int kk, int buf, int r) {
+        const uint8_t *st = lds + stage * STAGE_BYTES;
+        if (r < 4)
+            fa[buf][r] = *reinterpret_cast<const i32x4 *>(st + a_frag + r * 32 * ROW_BYTES + kofs[kk]);
+        else
+            fb[buf][r - 4] = *reinterpret_cast<const i32x4 *>(st + b_frag + (r - 4) * 32 * ROW_BYTES + kofs[kk]);
+    };
+    auto read_frags = [&](int stage, int kk, int buf) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            read_frag(stage, kk, buf, r);
+    };
+    // scales of K step k: dword k % 4 of the rows' 16 bytes in slot (k / 4) % 2
+    const unsigned sh = 8u * (unsigned)half;
+    auto read_scales = [&](int k, int buf) {
+        const uint8_t *st = lds + ((k >> 2) & 1) * SCALE_BLOCK + (k & 3) * SCALE_ROW;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sa[buf][i] = *reinterpret_cast<const unsigned *>(st + a_sc + 32 * i * SCALE_BLOCK_ROW) >> sh;
+            sbv[buf][i] = *reinterpret_cast<const unsigned *>(st + b_sc + 32 * i * SCALE_BLOCK_ROW) >> sh;
+        }
+    };
+
+    f32x16 acc[4][4];
+    // Matrix instructions of sub-step kk on fragment buffer fbuf and scale
+    // buffer sbuf (format 4 = E2M1 for both operands; byte select 2 kk). B rows are the first operand, so each 32 x 32 result
+    // arrives as in the FP4 kernel: lane (l32, half) of block (i, j) holds
+    // C[m][n + 8 g + 4 half + e] in element 4 g + e, m = row l32 of block i.
+    // matrix instruction t (0..15) of sub-step kk: block (t / 4, t % 4)
+    auto mma1 = [&](int fbuf, int sbuf, int kk, int t) {
+        const int i = t >> 2, j = t & 3;
+        const i32x8 x = __builtin_shufflevector(fb[fbuf][j], fb[fbuf][j], 0, 1, 2, 3, -1, -1, -1, -1);
+        const i32x8 y = __builtin_shufflevector(fa[fbuf][i], fa[fbuf][i], 0, 1, 2, 3, -1, -1, -1, -1);
+        if (kk == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc[i][j], 4, 4, 0, (int)sbv[sbuf][j], 0,
+                                                                    (int)sa[sbuf][i]);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc[i][j], 4, 4, 2, (int)sbv[sbuf][j], 2,
+                                                                    (int)sa[sbuf][i]);
+    };
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = f32x16{};
+    };
+
+    for (int round = 0;; ++round) {
+        const int pos = schedule_position(blockIdx.x, round, p.grid);
+        if (pos >= p.tiles)
+            break;
+        int tm, tn;
+        supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
+        set_tile(tm, tn);
+        zero_acc();
+
+        if (nk > 0) {
+            // the previous tile's copies and reads are done before the ring
+            // is refilled with steps 0 .. STAGES - 2
+            wait_reads();
+            wait_all_copies();
+            lds_barrier();
+            copy_scales(0);
+#pragma unroll
+            for (int s = 0; s < STAGES - 1; ++s)
+                copy_step(s, s);
+            wait_copies_le<COPIES * (STAGES - 2)>();
+            lds_barrier();
+            read_frags(0, 0, 0);
+            read_scales(0, 0);
+
+            // K step k on stage k % STAGES; scale buffer k % 2
+            auto step = [&](int k, auto sbuf_c) {
+                constexpr int sbuf = decltype(sbuf_c)::value;
+                const int stage = k & (STAGES - 1);
+                const int next_stage = (k + 1) & (STAGES - 1);
+                const int copy_stage = (k + STAGES - 1) & (STAGES - 1);
+                // LDS address bases, hidden from the optimiser at every step so
+                // that each stage's addresses are formed where they are used
+                asm volatile("" : "+v"(kofs[0]), "+v"(kofs[1]), "+v"(a_frag), "+v"(b_frag), "+v"(a_sc), "+v"(b_sc));
+                // this wave's reads of step k - 1 and k and its copies of step
+                // k + 1 (and every older scale block) are done: only step
+                // k + 2's code copies may still be in flight, plus a scale
+                // block issued after them, which makes this wait stricter
+                wait_reads();
+                wait_copies_le<COPIES * (STAGES - 3)>();
+                // after the barrier every wave is done with step k - 1's stage
+                lds_barrier();
+                // sub-steps 0 and 1, order fixed: fragment read r of sub-step 1
+                // after matrix instruction 2 r of sub-step 0; those of step
+                // k + 1's sub-step 0 likewise during sub-step 1, then its
+                // scales; the copies of step k + STAGES - 1 into step k - 1's
+                // stage one every three matrix instructions
+                SCHED_FENCE();
+                static_for<32>([&](auto tc) {
+                    constexpr int t = decltype(tc)::value;
+                    constexpr int kk = t >> 4, u = t & 15;
+                    mma1(kk, sbuf, kk, u);
+                    if constexpr (u % 2 == 0) {
+                        if constexpr (kk == 0)
+                            read_frag(stage, 1, 1, u / 2);
+                        else
+                            read_frag(next_stage, 0, 0, u / 2);
+                    }
+                    if constexpr (t % 3 == 2 && t / 3 < COPIES)
+                        copy_one(k + STAGES - 1, copy_stage, t / 3);
+                    if constexpr (t == 31)
+                        read_scales(k + 1, sbuf ^ 1);
+                    SCHED_VALU_ONLY();
+                });
+                // the next scale block during the first step of a block: its
+                // slot held block k / 4 - 1, whose steps every wave finished
+                // before this step's barrier
+                if ((k & 3) == 0)
+                    copy_scales((k >> 2) + 1);
+            };
+            int k = 0;
+            for (; k + 1 < nk; k += 2) {
+                step(k, Int<0>{});
+                step(k + 1, Int<1>{});
+            }
+            if (k < nk)
+                step(k, Int<0>{});
+        }
+        store_tile<EPI>(acc, rc, rbias, p.M, p.N, tm * TM + 128 * wm, tn * TN + 128 * wn, l32, half);
+    }
+    wait_reads();
+    wait_all_copies(); // no copy may still be writing LDS when the workgroup ends
+}
+
+} // namespace mx
+} // namespace gemm355

@@ -196,6 +196,31 @@ int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const void *SFA,
                            const void *SFB, const void *bias, int activation, void *C, void *stream);
 
 /* Human-readable text for a status code (static storage; never NULL). */
+/*
+ * gemm_mxfp4_nt -- C = A * B^T for microscaled FP4 operands (E2M1 codes with
+ * one E8M0 power-of-two scale per 32 elements), on the gfx950 matrix cores'
+ * own block scaling (v_mfma_scale_f32_32x32x64_f8f6f4, four times the BF16
+ * rate). Not a format of the pages: their FP4 variant scales every 16
+ * elements by an E4M3 value ("NVFP4 GEMM on Blackwell", "NVFP4 Datatype"),
+ * whose mantissa the hardware scaling cannot apply; this is the block-scaled
+ * matrix product with scales applied inside the instruction, in the format
+ * the hardware takes.
+ *
+ *   a(m,k) = e2m1(code(m,k)) * 2^(SA[m][k/32] - 127),  likewise b(n,k)
+ *   C[m][n] = bf16_rne(fp32(sum_k a(m,k) * b(n,k)))
+ *
+ *   Aq   M x K/2 bytes, row-major: two codes per byte, even k in the low nibble
+ *   SA   M x K/32 E8M0 bytes, row-major (0xFF, NaN, is not supported)
+ *   Bq, SB  the same with N rows;  C  M x N BF16, row-major.
+ * Products of two scaled E2M1 values are exact; sums are FP32 (order
+ * unspecified). Ownership, streams and edge cases as for gemm_nvfp4_nt.
+ * Requirements, else GEMM355_ERR_UNSUPPORTED: K % 512 == 0 (scales travel
+ * 16 bytes per row at a time), N % 8 == 0; Aq, Bq, SA, SB, C 16-byte aligned;
+ * extents as for the other products. 256 x 256 output tiles.
+ */
+int gemm_mxfp4_nt(int M, int N, int K, const void *Aq, const void *SA, const void *Bq, const void *SB, void *C,
+                  void *stream);
+
 const char *gemm355_status_string(int status);
 
 /*

@@ -19,7 +19,7 @@ def test_library_exports_every_declared_function():
     lib = g.load()
     names = g.declared_functions()
     assert set(names) >= {"gemm_bf16_nt", "gemm_bf16_nt_bias_act", "gemm_nvfp4_nt", "gemm_nvfp4_nt_bias_act",
-                          "gemm355_status_string",
+                          "gemm_mxfp4_nt", "gemm355_status_string",
                           "gemm355_tile_order", "gemm355_schedule"}
     for n in names:
         assert hasattr(lib, n), n
@@ -39,16 +39,20 @@ def _fp4(M, N, K, aq=FAKE, sfa=FAKE + 0x100000, bq=FAKE + 0x200000, sfb=FAKE + 0
     return g.load().gemm_nvfp4_nt(M, N, K, aq, sfa, bq, sfb, c, None)
 
 
-@pytest.mark.parametrize("fn", [_bf16, _fp4])
-def test_rejections_happen_before_any_device_call(fn):
-    assert fn(-1, 8, 64) == g.ERR_INVALID_ARG
-    assert fn(8, -8, 64) == g.ERR_INVALID_ARG
-    assert fn(8, 8, -64) == g.ERR_INVALID_ARG
+def _mx(M, N, K, aq=FAKE, sa=FAKE + 0x100000, bq=FAKE + 0x200000, sb=FAKE + 0x300000, c=FAKE + 0x400000):
+    return g.load().gemm_mxfp4_nt(M, N, K, aq, sa, bq, sb, c, None)
+
+
+@pytest.mark.parametrize("fn,K", [(_bf16, 64), (_fp4, 64), (_mx, 512)])
+def test_rejections_happen_before_any_device_call(fn, K):
+    assert fn(-1, 8, K) == g.ERR_INVALID_ARG
+    assert fn(8, -8, K) == g.ERR_INVALID_ARG
+    assert fn(8, 8, -K) == g.ERR_INVALID_ARG
     # empty output: nothing to do, even with NULL pointers
-    assert fn(0, 8, 64, None, None, None) == g.OK if fn is _bf16 else fn(0, 8, 64, None, None, None, None, None) == g.OK
-    assert fn(8, 8, 64, c=None) == g.ERR_INVALID_ARG
-    assert fn(8, 12, 64) == g.ERR_UNSUPPORTED          # N % 8
-    assert fn(8, 8, 64, c=FAKE + 0x900008) == g.ERR_UNSUPPORTED  # C not 16-byte aligned
+    assert fn(0, 8, K, None, None, None) == g.OK if fn is _bf16 else fn(0, 8, K, None, None, None, None, None) == g.OK
+    assert fn(8, 8, K, c=None) == g.ERR_INVALID_ARG
+    assert fn(8, 12, K) == g.ERR_UNSUPPORTED          # N % 8
+    assert fn(8, 8, K, c=FAKE + 0x900008) == g.ERR_UNSUPPORTED  # C not 16-byte aligned
 
 
 def test_bf16_specific_rejections():
@@ -115,6 +119,25 @@ def test_fp4_specific_rejections():
     assert _fp4(8, 8, 32) == g.ERR_UNSUPPORTED                    # K % 64
     assert _fp4(8, 8, 64, sfb=FAKE + 0x300002) == g.ERR_UNSUPPORTED  # scales need 4-byte alignment
     assert _fp4(8, 8, 64, aq=FAKE + 8) == g.ERR_UNSUPPORTED
+
+
+def test_mx_specific_rejections():
+    assert _mx(8, 8, 512, sa=None) == g.ERR_INVALID_ARG
+    assert _mx(8, 8, 512, bq=None) == g.ERR_INVALID_ARG
+    for K in (32, 256, 768):                                     # K % 512 (scales move 16 bytes per row)
+        assert _mx(8, 8, K) == g.ERR_UNSUPPORTED
+    assert _mx(8, 8, 512, sb=FAKE + 0x300004) == g.ERR_UNSUPPORTED   # scales need 16-byte alignment
+    assert _mx(8, 8, 512, aq=FAKE + 8) == g.ERR_UNSUPPORTED
+    assert _mx(8, 8, 512, aq=FAKE, c=FAKE + 512) == g.ERR_INVALID_ARG   # C overlaps the A codes
+    import torch
+    if torch.cuda.is_available():
+        return
+    lib = g.load()
+    big = [FAKE, 1 << 40, 1 << 41, 1 << 42, 1 << 43]
+    # codes of 256 padded rows: K / 2 bytes each, below 2^31 in all
+    assert lib.gemm_mxfp4_nt(3, 16, (1 << 24) - 512, *big, None) == g.ERR_NO_DEVICE
+    assert lib.gemm_mxfp4_nt(3, 16, 1 << 24, *big, None) == g.ERR_UNSUPPORTED
+    assert _mx(8, 8, 0, None, None, None, None) == g.ERR_NO_DEVICE   # K = 0: zeros, no operand read
 
 
 def test_binding_checks_tensor_sizes_before_calling():

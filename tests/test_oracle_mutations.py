@@ -26,8 +26,14 @@ MUTATIONS = {
     "e2m1_bias": ("(int)e - 1);", "(int)e - 2);"),
     "e2m1_subnormal": ("? 0.5 * (double)m", "? 1.0 * (double)m"),
     "e4m3_bias": ("(int)e - 7);", "(int)e - 8);"),
-    "nibble_order": ("(k & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u)",
-                     "(k & 1) ? (unsigned)(byte & 15u) : (unsigned)(byte >> 4)"),
+    "nibble_order": ("(k & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u);\n    return oracle_e2m1_to_double(code) * oracle_e4m3",
+                     "(k & 1) ? (unsigned)(byte & 15u) : (unsigned)(byte >> 4);\n    return oracle_e2m1_to_double(code) * oracle_e4m3"),
+    # (the nibble order of the microscaled product has no mutant: swapping it
+    # relabels k and k ^ 1 in both operands alike, and both lie in one scale
+    # block, so every product is unchanged)
+    "mx_scale_row": ("S[row * (K / 32) + k / 32]", "S[(row / 2) * (K / 32) + k / 32]"),
+    "mx_scale_block_64": ("S[row * (K / 32) + k / 32]", "S[row * (K / 32) + (k / 64) * 2]"),
+    "e8m0_bias": ("ldexp(1.0, (int)byte - 127)", "ldexp(1.0, (int)byte - 128)"),
     "scale_block_32": ("SF[row * (K / 16) + k / 16]", "SF[row * (K / 16) + k / 32]"),
     "scale_row": ("SF[row * (K / 16) + k / 16]", "SF[(row / 2) * (K / 16) + k / 16]"),
     "ties_away": ("if (frac > 0.5)", "if (frac >= 0.5)"),
@@ -77,6 +83,20 @@ def _pins_pass() -> bool:
     dec = oracle.decode_nvfp4(Q, SF, 32)
     ref = exact.fp4_fractions(Q, SF, 32)
     checks.append(all(dec[r, k] == float(ref[r, k]) for r in range(2) for k in range(32)))
+    # microscaled FP4: E8M0 values, and A against an identity B coded as
+    # 1.0 (code 2) with unit scales, whose product is A decoded by hand
+    checks.append(all(oracle.e8m0_to_double(b) == 2.0 ** (b - 127) for b in range(255)))
+    K = 128
+    Q, S = syn.mxfp4_operand(3, K, seed=11)
+    codes = np.zeros((K, K), np.uint8)
+    codes[np.arange(K), np.arange(K)] = 2
+    got = oracle.gemm_mxfp4_nt(Q, S, syn.pack_nibbles(codes), np.full((K, K // 32), 127, np.uint8), K)
+    nib = lambda r, k: (int(Q[r, k // 2]) >> (4 * (k & 1))) & 15
+    want = [[exact.rne_bf16(exact.e2m1_fraction(nib(r, k)) * Fraction(2) ** (int(S[r, k // 32]) - 127))
+             for k in range(K)] for r in range(3)]
+    # compared as values: code 8 is -0
+    checks.append(all(exact.rne_bf16(Fraction(oracle.bf16_to_double(np.array([got[r, k]]))[0].item())) == want[r][k]
+                      for r in range(3) for k in range(K)))
     return all(checks)
 
 
