@@ -427,10 +427,15 @@ extern "C" int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const
     return fp4_product<true>(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, stream);
 }
 
-extern "C" int gemm_mxfp4_nt(int M, int N, int K, const void *Aq, const void *SA, const void *Bq, const void *SB,
-                             void *C, void *stream)
+namespace {
+
+template <bool FUSED>
+int mx_product(int M, int N, int K, const void *Aq, const void *SA, const void *Bq, const void *SB, const void *bias,
+               int act, void *C, void *stream)
 {
     if (M < 0 || N < 0 || K < 0)
+        return GEMM355_ERR_INVALID_ARG;
+    if (FUSED && (act < GEMM355_ACT_NONE || act > GEMM355_ACT_GELU_TANH))
         return GEMM355_ERR_INVALID_ARG;
     if (M == 0 || N == 0)
         return GEMM355_OK;
@@ -440,7 +445,10 @@ extern "C" int gemm_mxfp4_nt(int M, int N, int K, const void *Aq, const void *SA
     if (K > 0 && (overlaps(C, c_bytes, Aq, size_t(M) * K / 2) || overlaps(C, c_bytes, Bq, size_t(N) * K / 2) ||
                   overlaps(C, c_bytes, SA, size_t(M) * K / 32) || overlaps(C, c_bytes, SB, size_t(N) * K / 32)))
         return GEMM355_ERR_INVALID_ARG;
-    if (!aligned(Aq, 16) || !aligned(Bq, 16) || !aligned(C, 16) || !aligned(SA, 16) || !aligned(SB, 16))
+    if (FUSED && overlaps(C, c_bytes, bias, size_t(N) * 2))
+        return GEMM355_ERR_INVALID_ARG;
+    if (!aligned(Aq, 16) || !aligned(Bq, 16) || !aligned(C, 16) || !aligned(SA, 16) || !aligned(SB, 16) ||
+        !aligned(bias, 16))
         return GEMM355_ERR_UNSUPPORTED;
     if (K % 512 != 0 || N % 8 != 0)
         return GEMM355_ERR_UNSUPPORTED;
@@ -453,11 +461,32 @@ extern "C" int gemm_mxfp4_nt(int M, int N, int K, const void *Aq, const void *SA
     p.sfa = SA;
     p.sfb = SB;
     p.c = C;
+    p.bias = FUSED ? bias : nullptr;
     p.M = M;
     p.N = N;
     p.K = K;
-    return launch(gemm355::mx::gemm_mxfp4_nt_kernel<gemm355::EPI_PLAIN>, p, stream, gemm355::mx::TM,
-                  gemm355::mx::TN);
+    using namespace gemm355;
+    if (!FUSED)
+        return launch(mx::gemm_mxfp4_nt_kernel<EPI_PLAIN>, p, stream, mx::TM, mx::TN);
+    if (act == GEMM355_ACT_RELU)
+        return launch(mx::gemm_mxfp4_nt_kernel<ACT_RELU>, p, stream, mx::TM, mx::TN);
+    if (act == GEMM355_ACT_GELU_TANH)
+        return launch(mx::gemm_mxfp4_nt_kernel<ACT_GELU_TANH>, p, stream, mx::TM, mx::TN);
+    return launch(mx::gemm_mxfp4_nt_kernel<ACT_NONE>, p, stream, mx::TM, mx::TN);
+}
+
+} // namespace
+
+extern "C" int gemm_mxfp4_nt(int M, int N, int K, const void *Aq, const void *SA, const void *Bq, const void *SB,
+                             void *C, void *stream)
+{
+    return mx_product<false>(M, N, K, Aq, SA, Bq, SB, nullptr, GEMM355_ACT_NONE, C, stream);
+}
+
+extern "C" int gemm_mxfp4_nt_bias_act(int M, int N, int K, const void *Aq, const void *SA, const void *Bq,
+                                      const void *SB, const void *bias, int activation, void *C, void *stream)
+{
+    return mx_product<true>(M, N, K, Aq, SA, Bq, SB, bias, activation, C, stream);
 }
 
 extern "C" const char *gemm355_status_string(int status)

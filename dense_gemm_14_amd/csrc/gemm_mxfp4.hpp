@@ -15,16 +15,17 @@
 //   * Output tile 256 x 256 per workgroup, 4 waves in 2 x 2, each wave 128 x
 //     128 = 4 x 4 blocks of 32 x 32 (256 accumulation registers per lane).
 //   * K advances 128 per step: 64 bytes of codes per row (the LDS row) and 4
-//     scale bytes. A stage holds the A and B code tiles (16 KiB each) and
-//     their scale rows (1 KiB each, row-major); four stages (136 KiB) form a
-//     ring that runs on across the workgroup's tiles, so the next tile's first
-//     steps are copied while the current one finishes. Code rows are 64 bytes:
+//     scale bytes. A stage holds the A and B code tiles (16 KiB each); four
+//     stages (128 KiB) form a ring. Scales come in blocks of four steps (16
+//     bytes per row, 8 KiB per block for A and B) in a ring of two blocks
+//     beside it (144 KiB in all). Code rows are 64 bytes:
 //     logical 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3), so
 //     the 16 rows a fragment read serves per cycle at one chunk cover the 16
 //     bank groups of 256 bytes.
 //   * Copies are LDS-DMA only (no registers carry operands): per step and
 //     wave, four 1 KiB code copies of A (rows 64 w .. 64 w + 63, 16 rows
-//     each), four of B, and one 256-byte scale copy of each. Step k + 3 is
+//     each) and four of B; per block of four steps one 1 KiB scale copy of
+//     each (64 rows, 16 bytes each). Step k + 3 is
 //     requested during step k, after the barrier that frees step k - 1's
 //     stage, one copy every three matrix instructions (issued together they
 //     stall the wave for most of a step).
@@ -336,13 +337,11 @@ void gemm_mxfp4_nt_kernel(Problem p)
                 if ((k & 3) == 0)
                     copy_scales((k >> 2) + 1);
             };
-            int k = 0;
-            for (; k + 1 < nk; k += 2) {
+            // nk is a multiple of 4 (K % 512 == 0): steps go in pairs
+            for (int k = 0; k < nk; k += 2) {
                 step(k, Int<0>{});
                 step(k + 1, Int<1>{});
             }
-            if (k < nk)
-                step(k, Int<0>{});
         }
         store_tile<EPI>(acc, rc, rbias, p.M, p.N, tm * TM + 128 * wm, tn * TN + 128 * wn, l32, half);
     }

@@ -195,7 +195,6 @@ int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SFA, const vo
 int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
                            const void *SFB, const void *bias, int activation, void *C, void *stream);
 
-/* Human-readable text for a status code (static storage; never NULL). */
 /*
  * gemm_mxfp4_nt -- C = A * B^T for microscaled FP4 operands (E2M1 codes with
  * one E8M0 power-of-two scale per 32 elements), on the gfx950 matrix cores'
@@ -221,6 +220,21 @@ int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const void *SFA,
 int gemm_mxfp4_nt(int M, int N, int K, const void *Aq, const void *SA, const void *Bq, const void *SB, void *C,
                   void *stream);
 
+/*
+ * gemm_mxfp4_nt_bias_act -- the microscaled FP4 product with the fused
+ * epilogue of gemm_bf16_nt_bias_act ("NVFP4 GEMM on Blackwell", "Kernel 1",
+ * "Epilogue Warps"):
+ *
+ *   C[m][n] = bf16_rne(act(fp32(sum_k a(m,k) * b(n,k)) + bias[n]))
+ *
+ * with a, b, layouts and requirements as for gemm_mxfp4_nt and bias,
+ * activation and their errors as for gemm_bf16_nt_bias_act (bias: N BF16
+ * values, 16-byte aligned, or NULL; K == 0 gives act(bias[n])).
+ */
+int gemm_mxfp4_nt_bias_act(int M, int N, int K, const void *Aq, const void *SA, const void *Bq, const void *SB,
+                           const void *bias, int activation, void *C, void *stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
 const char *gemm355_status_string(int status);
 
 /*

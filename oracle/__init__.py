@@ -93,6 +93,8 @@ def _bind(lib):
     lib.oracle_gemm_mxfp4_nt.restype = i
     lib.oracle_gemm_mxfp4_nt_at.argtypes = [i, i, i, p, p, p, p, ctypes.c_long, p, p, p, p]
     lib.oracle_gemm_mxfp4_nt_at.restype = i
+    lib.oracle_gemm_mxfp4_nt_bias_act_at.argtypes = [i, i, i, p, p, p, p, p, i, ctypes.c_long, p, p, p, p]
+    lib.oracle_gemm_mxfp4_nt_bias_act_at.restype = i
     lib.oracle_decode_nvfp4.argtypes = [i, i, p, p, p]
     lib.oracle_decode_nvfp4.restype = i
     lib.oracle_max_threads.argtypes = []
@@ -310,6 +312,25 @@ def gemm_mxfp4_nt_at(Aq, SA, Bq, SB, K: int, ms, ns, with_sum: bool = False):
     _check(lib.oracle_gemm_mxfp4_nt_at(M, N, K, _ptr(Aq), _ptr(SA), _ptr(Bq), _ptr(SB), ms.size, _ptr(ms), _ptr(ns),
                                        _ptr(out), _ptr(sums)), "gemm_mxfp4_nt_at")
     return (out, sums) if with_sum else out
+
+
+def gemm_mxfp4_nt_bias_act_at(Aq, SA, Bq, SB, K: int, bias, act: int, ms, ns, with_z: bool = False):
+    """Elements C[ms[i], ns[i]] of bf16(act(dec(A) @ dec(B)^T + bias)) for
+    microscaled FP4 operands (and optionally z before the activation)."""
+    lib = _load()
+    Aq, SA, Bq, SB = (_c(x, np.uint8) for x in (Aq, SA, Bq, SB))
+    M, N = Aq.shape[0], Bq.shape[0]
+    _shape_mx(Aq, SA, M, K)
+    _shape_mx(Bq, SB, N, K)
+    bias = _bias(bias, N)
+    ms, ns = _idx(ms, ns)
+    out = np.empty(ms.size, dtype=np.uint16)
+    zs = np.empty(ms.size, dtype=np.float64)
+    _check(lib.oracle_gemm_mxfp4_nt_bias_act_at(M, N, K, _ptr(Aq), _ptr(SA), _ptr(Bq), _ptr(SB),
+                                                _ptr(bias) if bias is not None else None, int(act), ms.size,
+                                                _ptr(ms), _ptr(ns), _ptr(out), _ptr(zs)),
+           "gemm_mxfp4_nt_bias_act_at")
+    return (out, zs) if with_z else out
 
 
 def _shape_fp4(Q, SF, rows, K):

@@ -386,6 +386,28 @@ int oracle_gemm_mxfp4_nt_at(int M, int N, int K, const uint8_t *Aq, const uint8_
     return ORACLE_OK;
 }
 
+/* The microscaled FP4 product with the fused epilogue (bias per column, then
+ * the activation, in binary64), as for the other formats. Chosen elements
+ * only; out_z (may be NULL) gets z before the activation. */
+int oracle_gemm_mxfp4_nt_bias_act_at(int M, int N, int K, const uint8_t *Aq, const uint8_t *SA, const uint8_t *Bq,
+                                     const uint8_t *SB, const uint16_t *bias, int act, long count,
+                                     const int32_t *ms, const int32_t *ns, uint16_t *out_bf16, double *out_z)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || act < 0 || act > 2 || count < 0)
+        return ORACLE_BAD_ARGS;
+    for (long i = 0; i < count; ++i)
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N)
+            return ORACLE_BAD_ARGS;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < count; ++i) {
+        const double z = dot_mx(Aq, SA, Bq, SB, K, ms[i], ns[i]) + bias_at(bias, ns[i]);
+        out_bf16[i] = oracle_bf16_from_double(oracle_activate(z, act));
+        if (out_z)
+            out_z[i] = z;
+    }
+    return ORACLE_OK;
+}
+
 /* Decoded FP4 operand as binary64 (rows x K), for cross-checks. */
 int oracle_decode_nvfp4(int rows, int K, const uint8_t *Q, const uint8_t *SF, double *out)
 {

@@ -96,6 +96,21 @@ def test_fp4_fused_epilogue_rejections():
     assert _fused4(0, 8, 64, act=g.ACT_RELU, bias=None, c=None) == g.OK
 
 
+def _fused_mx(M, N, K, act=0, bias=FAKE + 0x500000, c=FAKE + 0x400000):
+    return g.load().gemm_mxfp4_nt_bias_act(M, N, K, FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000,
+                                           bias, act, c, None)
+
+
+def test_mx_fused_epilogue_rejections():
+    assert _fused_mx(8, 8, 256) == g.ERR_UNSUPPORTED                # K % 512
+    for bad_act in (-1, 3):
+        assert _fused_mx(8, 8, 512, act=bad_act) == g.ERR_INVALID_ARG
+    assert _fused_mx(8, 8, 512, bias=FAKE + 0x500004) == g.ERR_UNSUPPORTED   # bias 16-byte aligned
+    assert _fused_mx(8, 8, 512, bias=FAKE + 0x400000 + 16) == g.ERR_INVALID_ARG   # bias inside C
+    assert _fused_mx(8, 12, 512) == g.ERR_UNSUPPORTED               # N % 8
+    assert _fused_mx(0, 8, 512, act=g.ACT_GELU_TANH, bias=None, c=None) == g.OK
+
+
 def test_extent_limits_are_exact():
     # Operand extents, padded to whole 256-row tiles, must stay below 2^31
     # bytes. Just inside, validation passes and the call stops at the missing

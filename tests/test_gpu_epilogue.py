@@ -212,3 +212,87 @@ def test_fp4_fused_workload_8192_sampled():
     ref, z = oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, bias, g.ACT_GELU_TANH, ms, ns, with_z=True)
     res = tolerance.check_fused(got[ms, ns], ref, z, K, g.ACT_GELU_TANH, sigma)
     assert res, res
+
+
+# ---- microscaled FP4 with the fused epilogue -------------------------------
+
+def run_fused_mx(ops, bias, act, M, N, K):
+    C = GuardedC(M, N)
+    g.gemm_mxfp4_nt_bias_act(M, N, K, *(to_dev(x) for x in ops), to_dev(bias) if bias is not None else None,
+                             act, C.view)
+    torch.cuda.synchronize()
+    assert C.guards_intact(), "write outside C"
+    return C.bits()
+
+
+_E2M1 = np.array([oracle.e2m1_to_double(c) for c in range(16)])
+
+
+def _sigma_mx(Q, S):
+    Q, S = Q[:512], S[:512]
+    codes = np.stack([Q & 15, Q >> 4], -1).reshape(Q.shape[0], -1)
+    scale = np.repeat(np.array([oracle.e8m0_to_double(b) for b in range(255)])[S], 32, axis=1)
+    return tolerance.sigma_of(_E2M1[codes] * scale)
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("M,N,K", [(300, 264, 512), (65, 72, 1024), (520, 264, 1536)])
+def test_mx_fused_matches_oracle(act, M, N, K):
+    need_gpu()
+    Aq, SA = syn.mxfp4_operand(M, K, seed=M + K + act)
+    Bq, SB = syn.mxfp4_operand(N, K, seed=N + K + 1)
+    sigma = _sigma_mx(Aq, SA) * _sigma_mx(Bq, SB)
+    bias = syn.bf16_uniform(1, N, seed=N + 5, lo=-sigma * K ** 0.5, hi=sigma * K ** 0.5)[0]
+    got = run_fused_mx((Aq, SA, Bq, SB), bias, act, M, N, K)
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    ref, z = oracle.gemm_mxfp4_nt_bias_act_at(Aq, SA, Bq, SB, K, bias, act, ms, ns, with_z=True)
+    res = tolerance.check_fused(got, ref.reshape(M, N), z.reshape(M, N), K, act, sigma)
+    assert res, res
+
+
+@pytest.mark.parametrize("act", [g.ACT_NONE, g.ACT_RELU])
+def test_mx_fused_exact_inputs_bitwise(act):
+    # unit scales with K = 512: every partial sum is a multiple of 2^-2 below
+    # 2^15, exact in FP32, and so is the bias sum (multiples of 1/16)
+    need_gpu()
+    M, N, K = 264, 256, 512
+    Aq, Bq = syn.fp4_codes(M, K, seed=241), syn.fp4_codes(N, K, seed=242)
+    SA = syn.e8m0_scales(M, K, seed=243, u_lo=0, u_hi=0)
+    SB = syn.e8m0_scales(N, K, seed=244, u_lo=0, u_hi=0)
+    bias = syn.bf16_sixteenths(1, N, seed=245, jmax=64)[0]
+    got = run_fused_mx((Aq, SA, Bq, SB), bias, act, M, N, K)
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    want = oracle.gemm_mxfp4_nt_bias_act_at(Aq, SA, Bq, SB, K, bias, act, ms, ns).reshape(M, N)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_mx_fused_empty_sum_is_activation_of_bias(act):
+    need_gpu()
+    M, N = 70, 72
+    bias = syn.bf16_uniform(1, N, seed=251, lo=-4.0, hi=4.0)[0]
+    C = GuardedC(M, N)
+    g.gemm_mxfp4_nt_bias_act(M, N, 0, None, None, None, None, to_dev(bias), act, C.view)
+    torch.cuda.synchronize()
+    assert C.guards_intact()
+    ops = (np.zeros((M, 0), np.uint8), np.zeros((M, 0), np.uint8), np.zeros((N, 0), np.uint8),
+           np.zeros((N, 0), np.uint8))
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    ref, z = oracle.gemm_mxfp4_nt_bias_act_at(*ops, 0, bias, act, ms, ns, with_z=True)
+    res = tolerance.check_fused(C.bits(), ref.reshape(M, N), z.reshape(M, N), 0, act)
+    assert res, res
+
+
+def test_mx_fused_workload_8192_sampled():
+    need_gpu()
+    M = N = K = 8192
+    print("mx fused workload", M, N, K, flush=True)
+    Aq, SA = syn.mxfp4_operand(M, K, seed=261)
+    Bq, SB = syn.mxfp4_operand(N, K, seed=262)
+    sigma = _sigma_mx(Aq, SA) * _sigma_mx(Bq, SB)
+    bias = syn.bf16_uniform(1, N, seed=263, lo=-4096.0, hi=4096.0)[0]
+    got = run_fused_mx((Aq, SA, Bq, SB), bias, g.ACT_GELU_TANH, M, N, K)
+    ms, ns = sample_positions(M, N, 1500, seed=264)
+    ref, z = oracle.gemm_mxfp4_nt_bias_act_at(Aq, SA, Bq, SB, K, bias, g.ACT_GELU_TANH, ms, ns, with_z=True)
+    res = tolerance.check_fused(got[ms, ns], ref, z, K, g.ACT_GELU_TANH, sigma)
+    assert res, res

@@ -166,3 +166,25 @@ def test_fp4_fused_is_activation_of_plain_fp4_sum_plus_bias(act):
     if act == oracle.ACT_NONE:
         assert np.array_equal(oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, None, act, ms, ns),
                               oracle.gemm_nvfp4_nt(Aq, SFA, Bq, SFB, K).ravel())
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_mx_fused_is_activation_of_plain_mx_sum_plus_bias(act):
+    # the microscaled form: z must be the plain microscaled oracle's binary64
+    # sum plus the column's bias (a bias one column to the left fails), and
+    # the output the activation of z evaluated independently (torch: GELU)
+    M, N, K = 9, 24, 128
+    Aq, SA = syn.mxfp4_operand(M, K, seed=231)
+    Bq, SB = syn.mxfp4_operand(N, K, seed=232)
+    bias = syn.bf16_uniform(1, N, seed=233, lo=-64.0, hi=64.0)[0]
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    got, z = oracle.gemm_mxfp4_nt_bias_act_at(Aq, SA, Bq, SB, K, bias, act, ms, ns, with_z=True)
+    _, s = oracle.gemm_mxfp4_nt_at(Aq, SA, Bq, SB, K, ms, ns, with_sum=True)
+    b = tolerance.bf16_bits_to_f64(bias)
+    assert np.array_equal(z, s + b[ns])
+    assert not np.array_equal(z, s + np.roll(b, 1)[ns])
+    y = _gelu_torch(z) if act == oracle.ACT_GELU_TANH else (np.maximum(z, 0.0) if act == oracle.ACT_RELU else z)
+    assert np.array_equal(got, oracle.bf16_from_double(y))
+    if act == oracle.ACT_NONE:
+        assert np.array_equal(oracle.gemm_mxfp4_nt_bias_act_at(Aq, SA, Bq, SB, K, None, act, ms, ns),
+                              oracle.gemm_mxfp4_nt(Aq, SA, Bq, SB, K).ravel())
