@@ -149,7 +149,7 @@ bool extent_ok(int64_t rows, int64_t row_bytes)
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <class Kernel>
-int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n = BN)
+int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n = BN, int threads = gemm355::THREADS)
 {
     int cus = 0;
     const int rc = compute_units(&cus);
@@ -162,7 +162,7 @@ int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n =
     p.supergroup = sg > 0 ? sg : kSupergroup;
     p.grid = gemm355::persistent_grid(p.tiles, cus);
     (void)hipGetLastError(); // clear a stale error so the check below is ours
-    hipLaunchKernelGGL(kernel, dim3(p.grid), dim3(gemm355::THREADS), 0, static_cast<hipStream_t>(stream), p);
+    hipLaunchKernelGGL(kernel, dim3(p.grid), dim3(threads), 0, static_cast<hipStream_t>(stream), p);
     return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 
@@ -467,12 +467,12 @@ int mx_product(int M, int N, int K, const void *Aq, const void *SA, const void *
     p.K = K;
     using namespace gemm355;
     if (!FUSED)
-        return launch(mx::gemm_mxfp4_nt_kernel<EPI_PLAIN>, p, stream, mx::TM, mx::TN);
+        return launch(mx::gemm_mxfp4_nt_kernel<EPI_PLAIN>, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
     if (act == GEMM355_ACT_RELU)
-        return launch(mx::gemm_mxfp4_nt_kernel<ACT_RELU>, p, stream, mx::TM, mx::TN);
+        return launch(mx::gemm_mxfp4_nt_kernel<ACT_RELU>, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
     if (act == GEMM355_ACT_GELU_TANH)
-        return launch(mx::gemm_mxfp4_nt_kernel<ACT_GELU_TANH>, p, stream, mx::TM, mx::TN);
-    return launch(mx::gemm_mxfp4_nt_kernel<ACT_NONE>, p, stream, mx::TM, mx::TN);
+        return launch(mx::gemm_mxfp4_nt_kernel<ACT_GELU_TANH>, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
+    return launch(mx::gemm_mxfp4_nt_kernel<ACT_NONE>, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
 }
 
 } // namespace

@@ -12,8 +12,10 @@
 // page's block-scaled MMA with scales applied inside the instruction.
 //
 // Work decomposition
-//   * Output tile 256 x 256 per workgroup, 4 waves in 2 x 2, each wave 128 x
-//     128 = 4 x 4 blocks of 32 x 32 (256 accumulation registers per lane).
+//   * Output tile 256 x 256 per workgroup, 8 waves in 2 x 4, each wave 128 x
+//     64 = 4 x 2 blocks of 32 x 32 (128 accumulation registers per lane), two
+//     waves per SIMD, so that one wave's matrix instructions run while the
+//     other is held issuing copies or waiting on fragment reads.
 //   * K advances 128 per step: 64 bytes of codes per row (the LDS row) and 4
 //     scale bytes. A stage holds the A and B code tiles (16 KiB each); four
 //     stages (128 KiB) form a ring. Scales come in blocks of four steps (16
@@ -23,14 +25,14 @@
 //     the 16 rows a fragment read serves per cycle at one chunk cover the 16
 //     bank groups of 256 bytes.
 //   * Copies are LDS-DMA only (no registers carry operands): per step and
-//     wave, four 1 KiB code copies of A (rows 64 w .. 64 w + 63, 16 rows
-//     each) and four of B; per block of four steps one 1 KiB scale copy of
-//     each (64 rows, 16 bytes each). Step k + 3 is
+//     wave, two 1 KiB code copies of A (rows 32 w .. 32 w + 31, 16 rows
+//     each) and two of B; per block of four steps one 1 KiB scale copy (64
+//     rows of A for waves 0..3, of B for waves 4..7, 16 bytes each). Step k + 3 is
 //     requested during step k, after the barrier that frees step k - 1's
-//     stage, one copy every three matrix instructions (issued together they
-//     stall the wave for most of a step).
-//   * Per step each wave issues 32 matrix instructions (2 sub-steps of K 64 x
-//     4 x 4 blocks). Fragment reads (16 bytes per lane: row l % 32 of a block,
+//     stage, one copy every four matrix instructions (issued together they
+//     stall the wave).
+//   * Per step each wave issues 16 matrix instructions (2 sub-steps of K 64 x
+//     4 x 2 blocks). Fragment reads (16 bytes per lane: row l % 32 of a block,
 //     the 32 K of sub-step kk that belong to lane half l / 32) of sub-step 1
 //     are issued during sub-step 0, those of the next step's sub-step 0 (and
 //     its scales) during sub-step 1.
@@ -64,12 +66,13 @@ constexpr int SCALE_BLOCK_ROW = SCALE_STEPS * SCALE_ROW;   // 16 bytes
 constexpr int SCALE_BLOCK = 2 * TM * SCALE_BLOCK_ROW;     // A then B: 8 KiB
 constexpr int SCALES_BASE = STAGES * STAGE_BYTES;
 constexpr int LDS_BYTES = SCALES_BASE + 2 * SCALE_BLOCK;
-constexpr int COPIES = 8;                        // code copies per wave and step (4 + 4)
-constexpr int SCALE_COPIES = 2;                  // per wave and scale block (A, B)
-constexpr int EPILOGUE_STORES = 32;              // 16-byte stores per wave per tile (128 x 128 BF16)
+constexpr int THREADS_MX = 512;                  // 8 waves, two per SIMD
+constexpr int COPIES = 4;                        // code copies per wave and step (2 + 2)
+constexpr int SCALE_COPIES = 1;                  // per wave and scale block (A or B)
+constexpr int EPILOGUE_STORES = 16;              // 16-byte stores per wave per tile (128 x 64 BF16)
 
 static_assert(LDS_BYTES <= 163840, "LDS ring exceeds the 160 KiB of a gfx950 workgroup");
-static_assert(TM == 256 && TN == 256 && THREADS == 256, "the copy map assumes 256 x 256 tiles and 4 waves");
+static_assert(TM == 256 && TN == 256 && THREADS_MX == 512, "the copy map assumes 256 x 256 tiles and 8 waves");
 // in flight at most: the copies of three steps ahead and one epilogue
 static_assert((STAGES - 1) * COPIES + SCALE_COPIES + EPILOGUE_STORES <= 63,
               "vmcnt counts at most 63 outstanding operations");
@@ -114,16 +117,16 @@ __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "m
 // Kernel arguments: Problem with a, b the codes and sfa, sfb the E8M0 scales.
 // EPI: EPI_PLAIN, or the activation of the fused epilogue.
 template <int EPI>
-__global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(THREADS_MX, THREADS_MX), amdgpu_waves_per_eu(2, 2)))
 void gemm_mxfp4_nt_kernel(Problem p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0 .. 7; waves w and w + 4 share a SIMD
     const int wm = wave & 1;   // 128-row half of the tile (A rows)
-    const int wn = wave >> 1;  // 128-column half (B rows)
+    const int wn = wave >> 1;  // 64-column quarter (B rows)
     const int l32 = lane & 31;
     const int half = lane >> 5;
     const int K = p.K;
@@ -139,65 +142,62 @@ void gemm_mxfp4_nt_kernel(Problem p)
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c, (unsigned)p.M * (unsigned)p.N * 2u);
     const __amdgpu_buffer_rsrc_t rbias = make_rsrc(p.bias, EPI != EPI_PLAIN && p.bias ? (unsigned)p.N * 2u : 0u);
 
-    // Copy map. Code copy t (0..3) of an operand: tile rows 64 wave + 16 t +
+    // Copy map. Code copy t (0, 1) of an operand: tile rows 32 wave + 16 t +
     // lane / 4, lane position lane % 4 of the row, which fetches logical chunk
-    // (lane % 4) ^ swizzle; scale copy: tile row 64 wave + lane, its 16 bytes
-    // of a block of four steps.
+    // (lane % 4) ^ swizzle; scale copy: waves 0..3 copy A rows, 4..7 B rows,
+    // tile row 64 (wave % 4) + lane, its 16 bytes of a block of four steps.
     // Per-lane offsets are set per tile (rows past M or N lie past the buffer
     // and read zeros; a round without a tile reads zeros throughout); the
     // step's K offset is the scalar offset.
     const int copy_row = lane >> 2;
-    const int srow = 64 * wave + lane;
-    int chunk_b[4];   // byte offset (within the step's 64) of each code copy's chunk
+    const int swave = wave & 3;
+    const bool scales_of_b = wave >= 4;
+    const int srow = 64 * swave + lane;
+    const i32x4 rs = scales_of_b ? rsb : rsa;
+    int chunk_b[2];   // byte offset (within the step's 64) of each code copy's chunk
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        chunk_b[t] = 16 * swizzle(64 * wave + 16 * t + copy_row, lane & 3);
+    for (int t = 0; t < 2; ++t)
+        chunk_b[t] = 16 * swizzle(32 * wave + 16 * t + copy_row, lane & 3);
 
     // Per-lane copy offsets of the current tile (rows past M or N lie past
     // the buffer and read zeros); the step's K offset is the scalar offset,
     // and steps past K (requested ahead of the tile's end) read zeros.
-    unsigned a_off[4], b_off[4], sa_off, sb_off;
+    unsigned a_off[2], b_off[2], s_off;
     auto set_tile = [&](int tm, int tn) {
         const int am = tm * TM, bn = tn * TN;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int row = 64 * wave + 16 * t + copy_row;
+        for (int t = 0; t < 2; ++t) {
+            const int row = 32 * wave + 16 * t + copy_row;
             a_off[t] = (unsigned)(am + row) * kb + (unsigned)chunk_b[t] + SHIFT - 1024u * t;
             b_off[t] = (unsigned)(bn + row) * kb + (unsigned)chunk_b[t] + SHIFT - 1024u * t;
         }
-        sa_off = (unsigned)(am + srow) * sb + SHIFT;
-        sb_off = (unsigned)(bn + srow) * sb + SHIFT;
+        s_off = (unsigned)((scales_of_b ? bn : am) + srow) * sb + SHIFT;
     };
-    // Copy q (0..7) of K step k of the current tile into stage `stage`:
-    // q 0..3 A codes, 4..7 B codes, each group after one m0 write.
+    // Copy q (0..3) of K step k of the current tile into stage `stage`:
+    // q 0, 1 A codes, 2, 3 B codes, each pair after one m0 write.
     auto copy_one = [&](int k, int stage, int q) {
         const unsigned base = lds_base + (unsigned)(stage * STAGE_BYTES);
         const bool in = k < nk;
         const int ko = in ? k * ROW_BYTES : 0;
         switch (q) {
-        case 0: set_m0(__builtin_amdgcn_readfirstlane(base + A_CODES + 4096 * wave));
+        case 0: set_m0(__builtin_amdgcn_readfirstlane(base + A_CODES + 2048 * wave));
                 copy_1k<0>(ra, in ? a_off[0] : OOB_SHIFTED, ko); break;
         case 1: copy_1k<1024>(ra, in ? a_off[1] : OOB_SHIFTED, ko); break;
-        case 2: copy_1k<2048>(ra, in ? a_off[2] : OOB_SHIFTED, ko); break;
-        case 3: copy_1k<3072>(ra, in ? a_off[3] : OOB_SHIFTED, ko); break;
-        case 4: set_m0(__builtin_amdgcn_readfirstlane(base + B_CODES + 4096 * wave));
+        case 2: set_m0(__builtin_amdgcn_readfirstlane(base + B_CODES + 2048 * wave));
                 copy_1k<0>(rb, in ? b_off[0] : OOB_SHIFTED, ko); break;
-        case 5: copy_1k<1024>(rb, in ? b_off[1] : OOB_SHIFTED, ko); break;
-        case 6: copy_1k<2048>(rb, in ? b_off[2] : OOB_SHIFTED, ko); break;
-        default: copy_1k<3072>(rb, in ? b_off[3] : OOB_SHIFTED, ko); break;
+        default: copy_1k<1024>(rb, in ? b_off[1] : OOB_SHIFTED, ko); break;
         }
     };
     // Scale block b (steps 4 b .. 4 b + 3) of the current tile into scale
     // slot b % 2: A rows, then B rows 4 KiB on (K % 512 == 0: every block is
-    // whole; blocks past K read zeros).
+    // whole; blocks past K read zeros). One copy per wave.
     auto copy_scales = [&](int b) {
-        const unsigned base = lds_base + (unsigned)(SCALES_BASE + (b & 1) * SCALE_BLOCK);
+        const unsigned base = lds_base + (unsigned)(SCALES_BASE + (b & 1) * SCALE_BLOCK) +
+                              (scales_of_b ? TM * SCALE_BLOCK_ROW : 0) + 1024u * swave;
         const bool in = b * SCALE_STEPS < nk;
         const int so = in ? b * SCALE_BLOCK_ROW : 0;
-        set_m0(__builtin_amdgcn_readfirstlane(base + 1024 * wave));
-        copy_1k<0>(rsa, in ? sa_off : OOB_SHIFTED, so);
-        set_m0(__builtin_amdgcn_readfirstlane(base + TM * SCALE_BLOCK_ROW + 1024 * wave));
-        copy_1k<0>(rsb, in ? sb_off : OOB_SHIFTED, so);
+        set_m0(__builtin_amdgcn_readfirstlane(base));
+        copy_1k<0>(rs, in ? s_off : OOB_SHIFTED, so);
     };
     auto copy_step = [&](int k, int stage) {
 #pragma unroll
@@ -210,16 +210,16 @@ void gemm_mxfp4_nt_kernel(Problem p)
     // dwords, pre-shifted for the lane's half. A and B rows of a lane have the
     // same swizzle (they differ by multiples of 32), so one set of chunk
     // offsets serves both.
-    i32x4 fa[2][4], fb[2][4];
-    unsigned sa[2][4], sbv[2][4];
-    const int a_row0 = 128 * wm + l32, b_row0 = 128 * wn + l32;   // block 0 rows; block i is 32 i rows on
+    i32x4 fa[2][4], fb[2][2];
+    unsigned sa[2][4], sbv[2][2];
+    const int a_row0 = 128 * wm + l32, b_row0 = 64 * wn + l32;   // block 0 rows; block i is 32 i rows on
     int kofs[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
         kofs[kk] = swizzle(l32, 2 * kk + half) << 4;
     int a_frag = A_CODES + a_row0 * ROW_BYTES, b_frag = B_CODES + b_row0 * ROW_BYTES;
     int a_sc = SCALES_BASE + a_row0 * SCALE_BLOCK_ROW, b_sc = SCALES_BASE + TM * SCALE_BLOCK_ROW + b_row0 * SCALE_BLOCK_ROW;
-    // fragment read r (0..7) of sub-step kk: A block r for r < 4, else B block r - 4
+    // fragment read r (0..5) of sub-step kk: A block r for r < 4, else B block r - 4
     auto read_frag = [&](int stage, int kk, int buf, int r) {
         const uint8_t *st = lds + stage * STAGE_BYTES;
         if (r < 4)
@@ -229,7 +229,7 @@ void gemm_mxfp4_nt_kernel(Problem p)
     };
     auto read_frags = [&](int stage, int kk, int buf) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
+        for (int r = 0; r < 6; ++r)
             read_frag(stage, kk, buf, r);
     };
     // scales of K step k: dword k % 4 of the rows' 16 bytes in slot (k / 4) % 2
@@ -237,20 +237,21 @@ void gemm_mxfp4_nt_kernel(Problem p)
     auto read_scales = [&](int k, int buf) {
         const uint8_t *st = lds + ((k >> 2) & 1) * SCALE_BLOCK + (k & 3) * SCALE_ROW;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
             sa[buf][i] = *reinterpret_cast<const unsigned *>(st + a_sc + 32 * i * SCALE_BLOCK_ROW) >> sh;
-            sbv[buf][i] = *reinterpret_cast<const unsigned *>(st + b_sc + 32 * i * SCALE_BLOCK_ROW) >> sh;
-        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            sbv[buf][j] = *reinterpret_cast<const unsigned *>(st + b_sc + 32 * j * SCALE_BLOCK_ROW) >> sh;
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
     // Matrix instructions of sub-step kk on fragment buffer fbuf and scale
     // buffer sbuf (format 4 = E2M1 for both operands; byte select 2 kk). B rows are the first operand, so each 32 x 32 result
     // arrives as in the FP4 kernel: lane (l32, half) of block (i, j) holds
     // C[m][n + 8 g + 4 half + e] in element 4 g + e, m = row l32 of block i.
-    // matrix instruction t (0..15) of sub-step kk: block (t / 4, t % 4)
+    // matrix instruction t (0..7) of sub-step kk: block (t / 2, t % 2)
     auto mma1 = [&](int fbuf, int sbuf, int kk, int t) {
-        const int i = t >> 2, j = t & 3;
+        const int i = t >> 1, j = t & 1;
         const i32x8 x = __builtin_shufflevector(fb[fbuf][j], fb[fbuf][j], 0, 1, 2, 3, -1, -1, -1, -1);
         const i32x8 y = __builtin_shufflevector(fa[fbuf][i], fa[fbuf][i], 0, 1, 2, 3, -1, -1, -1, -1);
         if (kk == 0)
@@ -264,7 +265,7 @@ void gemm_mxfp4_nt_kernel(Problem p)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
                 acc[i][j] = f32x16{};
     };
 
@@ -315,19 +316,19 @@ void gemm_mxfp4_nt_kernel(Problem p)
                 // scales; the copies of step k + STAGES - 1 into step k - 1's
                 // stage one every three matrix instructions
                 SCHED_FENCE();
-                static_for<32>([&](auto tc) {
+                static_for<16>([&](auto tc) {
                     constexpr int t = decltype(tc)::value;
-                    constexpr int kk = t >> 4, u = t & 15;
+                    constexpr int kk = t >> 3, u = t & 7;
                     mma1(kk, sbuf, kk, u);
-                    if constexpr (u % 2 == 0) {
+                    if constexpr (u < 6) {
                         if constexpr (kk == 0)
-                            read_frag(stage, 1, 1, u / 2);
+                            read_frag(stage, 1, 1, u);
                         else
-                            read_frag(next_stage, 0, 0, u / 2);
+                            read_frag(next_stage, 0, 0, u);
                     }
-                    if constexpr (t % 3 == 2 && t / 3 < COPIES)
-                        copy_one(k + STAGES - 1, copy_stage, t / 3);
-                    if constexpr (t == 31)
+                    if constexpr (t % 4 == 1)
+                        copy_one(k + STAGES - 1, copy_stage, t / 4);
+                    if constexpr (t == 15)
                         read_scales(k + 1, sbuf ^ 1);
                     SCHED_VALU_ONLY();
                 });
@@ -343,7 +344,7 @@ void gemm_mxfp4_nt_kernel(Problem p)
                 step(k + 1, Int<1>{});
             }
         }
-        store_tile<EPI>(acc, rc, rbias, p.M, p.N, tm * TM + 128 * wm, tn * TN + 128 * wn, l32, half);
+        store_tile<EPI>(acc, rc, rbias, p.M, p.N, tm * TM + 128 * wm, tn * TN + 64 * wn, l32, half);
     }
     wait_reads();
     wait_all_copies(); // no copy may still be writing LDS when the workgroup ends
