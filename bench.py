@@ -19,6 +19,11 @@ launch stream time them. One JSON line goes to stdout:
   cpu_baseline  the plain CPU oracle timed on a bounded sample of the same
              workload's output elements on this host's cores.
 
+Other workloads (--workload): bf16_4096, bf16_8000, bf16_skinny (128 x 8192 x
+8192, HBM roofline), bf16_256, fp4_8192 (E2M1 + E4M3 per 16, decoded to FP16),
+bf16_gelu_8192 (bias + GELU fused), mx_8192 (E2M1 + E8M0 per 32 on the scaled
+FP4 matrix instructions, against the FP4 peak).
+
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations

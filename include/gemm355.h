@@ -8,7 +8,10 @@
  * GB300 for HGEMM" (opening paragraph): BF16 inputs and output, FP32
  * accumulation. The block-scaled variant takes its operand format from
  * "NVFP4 GEMM on Blackwell", section "NVFP4 Datatype": E2M1 codes with one FP8
- * scale per 16 consecutive elements.
+ * scale per 16 consecutive elements. A microscaled variant (one power-of-two
+ * E8M0 scale per 32 elements) runs on the matrix cores' own block scaling.
+ * Each product also comes with a fused epilogue (bias per output column, then
+ * identity, ReLU or tanh GELU).
  *
  * Conventions shared by every entry point
  *  - All array pointers are DEVICE pointers owned by the caller. The library
