@@ -18,7 +18,10 @@
 //     other is held issuing copies or waiting on fragment reads.
 //   * K advances 128 per step: 64 bytes of codes per row (the LDS row) and 4
 //     scale bytes. A stage holds the A and B code tiles (16 KiB each); four
-//     stages (128 KiB) form a ring. Scales come in blocks of four steps (16
+//     stages (128 KiB) form a ring that runs on across the workgroup's tiles:
+//     a tile's last three steps copy the next tile's first three, so neither
+//     its epilogue stores nor a refill of the ring stall the next tile. Scales
+//     come in blocks of four steps (16
 //     bytes per row, 8 KiB per block for A and B) in a ring of two blocks
 //     beside it (144 KiB in all). Code rows are 64 bytes:
 //     logical 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3), so
@@ -162,42 +165,53 @@ void gemm_mxfp4_nt_kernel(Problem p)
     // Per-lane copy offsets of the current tile (rows past M or N lie past
     // the buffer and read zeros); the step's K offset is the scalar offset,
     // and steps past K (requested ahead of the tile's end) read zeros.
-    unsigned a_off[2], b_off[2], s_off;
-    auto set_tile = [&](int tm, int tn) {
+    // Offsets of the current tile and of the workgroup's next one: the last
+    // three steps of a tile copy the next tile's first three (K % 512 == 0
+    // makes every tile's step count a multiple of the four stages, so they
+    // land in the stages the next tile reads them from), and its first scale
+    // block. Without a next tile they read zeros.
+    unsigned a_off[2], b_off[2], s_off, na_off[2], nb_off[2], ns_off;
+    bool has_next = false;
+    auto offsets = [&](int tm, int tn, unsigned (&ao)[2], unsigned (&bo)[2], unsigned &so) {
         const int am = tm * TM, bn = tn * TN;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int row = 32 * wave + 16 * t + copy_row;
-            a_off[t] = (unsigned)(am + row) * kb + (unsigned)chunk_b[t] + SHIFT - 1024u * t;
-            b_off[t] = (unsigned)(bn + row) * kb + (unsigned)chunk_b[t] + SHIFT - 1024u * t;
+            ao[t] = (unsigned)(am + row) * kb + (unsigned)chunk_b[t] + SHIFT - 1024u * t;
+            bo[t] = (unsigned)(bn + row) * kb + (unsigned)chunk_b[t] + SHIFT - 1024u * t;
         }
-        s_off = (unsigned)((scales_of_b ? bn : am) + srow) * sb + SHIFT;
+        so = (unsigned)((scales_of_b ? bn : am) + srow) * sb + SHIFT;
     };
-    // Copy q (0..3) of K step k of the current tile into stage `stage`:
-    // q 0, 1 A codes, 2, 3 B codes, each pair after one m0 write.
+    // Copy q (0..3) of K step k into stage `stage`: step k of the current
+    // tile, or for k >= nk step k - nk of the next; q 0, 1 A codes, 2, 3 B
+    // codes, each pair after one m0 write.
     auto copy_one = [&](int k, int stage, int q) {
         const unsigned base = lds_base + (unsigned)(stage * STAGE_BYTES);
-        const bool in = k < nk;
-        const int ko = in ? k * ROW_BYTES : 0;
+        const bool nxt = k >= nk;
+        const bool in = !nxt || has_next;
+        const int ko = in ? (nxt ? k - nk : k) * ROW_BYTES : 0;
         switch (q) {
         case 0: set_m0(__builtin_amdgcn_readfirstlane(base + A_CODES + 2048 * wave));
-                copy_1k<0>(ra, in ? a_off[0] : OOB_SHIFTED, ko); break;
-        case 1: copy_1k<1024>(ra, in ? a_off[1] : OOB_SHIFTED, ko); break;
+                copy_1k<0>(ra, in ? (nxt ? na_off[0] : a_off[0]) : OOB_SHIFTED, ko); break;
+        case 1: copy_1k<1024>(ra, in ? (nxt ? na_off[1] : a_off[1]) : OOB_SHIFTED, ko); break;
         case 2: set_m0(__builtin_amdgcn_readfirstlane(base + B_CODES + 2048 * wave));
-                copy_1k<0>(rb, in ? b_off[0] : OOB_SHIFTED, ko); break;
-        default: copy_1k<1024>(rb, in ? b_off[1] : OOB_SHIFTED, ko); break;
+                copy_1k<0>(rb, in ? (nxt ? nb_off[0] : b_off[0]) : OOB_SHIFTED, ko); break;
+        default: copy_1k<1024>(rb, in ? (nxt ? nb_off[1] : b_off[1]) : OOB_SHIFTED, ko); break;
         }
     };
-    // Scale block b (steps 4 b .. 4 b + 3) of the current tile into scale
-    // slot b % 2: A rows, then B rows 4 KiB on (K % 512 == 0: every block is
-    // whole; blocks past K read zeros). One copy per wave.
+    // Scale block b (steps 4 b .. 4 b + 3; b = nk / 4 is the next tile's
+    // block 0) into slot (gb0 + b) % 2, gb0 = blocks of the workgroup's
+    // earlier tiles: A rows, then B rows 4 KiB on (K % 512 == 0: every block
+    // is whole). One copy per wave.
+    int gb0 = 0;
     auto copy_scales = [&](int b) {
-        const unsigned base = lds_base + (unsigned)(SCALES_BASE + (b & 1) * SCALE_BLOCK) +
+        const unsigned base = lds_base + (unsigned)(SCALES_BASE + ((gb0 + b) & 1) * SCALE_BLOCK) +
                               (scales_of_b ? TM * SCALE_BLOCK_ROW : 0) + 1024u * swave;
-        const bool in = b * SCALE_STEPS < nk;
-        const int so = in ? b * SCALE_BLOCK_ROW : 0;
+        const bool nxt = b * SCALE_STEPS >= nk;
+        const bool in = !nxt || has_next;
+        const int so = in ? (nxt ? b - nk / SCALE_STEPS : b) * SCALE_BLOCK_ROW : 0;
         set_m0(__builtin_amdgcn_readfirstlane(base));
-        copy_1k<0>(rs, in ? s_off : OOB_SHIFTED, so);
+        copy_1k<0>(rs, in ? (nxt ? ns_off : s_off) : OOB_SHIFTED, so);
     };
     auto copy_step = [&](int k, int stage) {
 #pragma unroll
@@ -232,10 +246,10 @@ void gemm_mxfp4_nt_kernel(Problem p)
         for (int r = 0; r < 6; ++r)
             read_frag(stage, kk, buf, r);
     };
-    // scales of K step k: dword k % 4 of the rows' 16 bytes in slot (k / 4) % 2
+    // scales of K step k: dword k % 4 of the rows' 16 bytes in slot (gb0 + k / 4) % 2
     const unsigned sh = 8u * (unsigned)half;
     auto read_scales = [&](int k, int buf) {
-        const uint8_t *st = lds + ((k >> 2) & 1) * SCALE_BLOCK + (k & 3) * SCALE_ROW;
+        const uint8_t *st = lds + ((gb0 + (k >> 2)) & 1) * SCALE_BLOCK + (k & 3) * SCALE_ROW;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             sa[buf][i] = *reinterpret_cast<const unsigned *>(st + a_sc + 32 * i * SCALE_BLOCK_ROW) >> sh;
@@ -269,29 +283,34 @@ void gemm_mxfp4_nt_kernel(Problem p)
                 acc[i][j] = f32x16{};
     };
 
-    for (int round = 0;; ++round) {
-        const int pos = schedule_position(blockIdx.x, round, p.grid);
-        if (pos >= p.tiles)
-            break;
-        int tm, tn;
-        supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
-        set_tile(tm, tn);
+    int tm = 0, tn = 0;
+    if (schedule_position(blockIdx.x, 0, p.grid) < p.tiles)
+        supergroup_tile(schedule_position(blockIdx.x, 0, p.grid), p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
+    bool first = true;
+    for (int round = 0; schedule_position(blockIdx.x, round, p.grid) < p.tiles; ++round) {
+        const int npos = schedule_position(blockIdx.x, round + 1, p.grid);
+        has_next = npos < p.tiles;
+        int ntm = 0, ntn = 0;
+        if (has_next)
+            supergroup_tile(npos, p.tiles_m, p.tiles_n, p.supergroup, ntm, ntn);
+        offsets(tm, tn, a_off, b_off, s_off);
+        offsets(ntm, ntn, na_off, nb_off, ns_off);
         zero_acc();
 
         if (nk > 0) {
-            // the previous tile's copies and reads are done before the ring
-            // is refilled with steps 0 .. STAGES - 2
-            wait_reads();
-            wait_all_copies();
-            lds_barrier();
-            copy_scales(0);
+            if (first) {
+                // fill the ring with steps 0 .. STAGES - 2 and scale block 0
+                copy_scales(0);
 #pragma unroll
-            for (int s = 0; s < STAGES - 1; ++s)
-                copy_step(s, s);
-            wait_copies_le<COPIES * (STAGES - 2)>();
-            lds_barrier();
-            read_frags(0, 0, 0);
-            read_scales(0, 0);
+                for (int s = 0; s < STAGES - 1; ++s)
+                    copy_step(s, s);
+                wait_copies_le<COPIES * (STAGES - 2)>();
+                lds_barrier();
+                read_frags(0, 0, 0);
+                read_scales(0, 0);
+            }
+            // (otherwise the previous tile's last steps copied steps 0 .. 2
+            // and read step 0's fragments and scales)
 
             // K step k on stage k % STAGES; scale buffer k % 2
             auto step = [&](int k, auto sbuf_c) {
@@ -305,9 +324,14 @@ void gemm_mxfp4_nt_kernel(Problem p)
                 // this wave's reads of step k - 1 and k and its copies of step
                 // k + 1 (and every older scale block) are done: only step
                 // k + 2's code copies may still be in flight, plus a scale
-                // block issued after them, which makes this wait stricter
+                // block issued after them (which makes this wait stricter),
+                // and at step 0 after a previous tile that tile's epilogue
+                // stores, issued after them
                 wait_reads();
-                wait_copies_le<COPIES * (STAGES - 3)>();
+                if (k == 0 && !first)
+                    wait_copies_le<COPIES * (STAGES - 3) + EPILOGUE_STORES>();
+                else
+                    wait_copies_le<COPIES * (STAGES - 3)>();
                 // after the barrier every wave is done with step k - 1's stage
                 lds_barrier();
                 // sub-steps 0 and 1, order fixed: fragment read r of sub-step 1
@@ -345,6 +369,10 @@ void gemm_mxfp4_nt_kernel(Problem p)
             }
         }
         store_tile<EPI>(acc, rc, rbias, p.M, p.N, tm * TM + 128 * wm, tn * TN + 64 * wn, l32, half);
+        gb0 += nk / SCALE_STEPS;
+        tm = ntm;
+        tn = ntn;
+        first = false;
     }
     wait_reads();
     wait_all_copies(); // no copy may still be writing LDS when the workgroup ends
