@@ -6,7 +6,8 @@ rows past M or N into zeros). These tests sit just inside that limit:
 
   * K at the limit with M = 3, N = 16: the offsets the kernels form for the
     padded rows 3 .. 255 reach 2^31 - 4 KiB and must all fall outside A's
-    range; every BF16 instance forced in turn, and the FP4 kernel;
+    range; every BF16 instance forced in turn, the FP4 kernel, and the
+    microscaled FP4 kernel at K = 2^24 - 512;
   * C (and A) at the limit with M = 2^27 - 300, N = K = 8: the store offsets
     reach 2^31 - 8 KiB; sampled rows, including the last tile's, compared
     bitwise (K = 8 sixteenths: the sums are exact).
@@ -25,6 +26,7 @@ pytestmark = pytest.mark.gpu
 
 K_BF16 = (1 << 22) - 8       # 256 padded rows x K x 2 bytes = 2^31 - 4096
 K_FP4 = (1 << 24) - 64       # 256 padded rows x K / 2 bytes = 2^31 - 8192
+K_MX = (1 << 24) - 512       # the same for the microscaled product (K % 512 == 0)
 
 
 @pytest.mark.parametrize("instance", [g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_SPLITK, g.INSTANCE_AUTO])
@@ -60,6 +62,30 @@ def test_fp4_k_at_extent_limit():
              tolerance.sigma_of(oracle.decode_nvfp4(Bq[:, :1 << 16], SFB[:, :1 << 13], 1 << 17)))
     ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
     want = oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns).reshape(M, N)   # threads over elements
+    res = tolerance.check(C.bits(), want, K, sigma)
+    assert res, res
+
+
+def test_mx_k_at_extent_limit():
+    need_gpu()
+    M, N, K = 3, 16, K_MX
+    print("mx K limit", M, N, K, flush=True)
+    Aq, SA = syn.mxfp4_operand(M, K, seed=113)
+    Bq, SB = syn.mxfp4_operand(N, K, seed=114)
+    C = GuardedC(M, N)
+    g.gemm_mxfp4_nt(M, N, K, *(to_dev(x) for x in (Aq, SA, Bq, SB)), C.view)
+    torch.cuda.synchronize()
+    assert C.guards_intact(), "write outside C"
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    want = oracle.gemm_mxfp4_nt_at(Aq, SA, Bq, SB, K, ms, ns).reshape(M, N)
+    # sigma from the first 2^17 elements of each row, decoded from the
+    # oracle's per-code and per-scale values
+    e2 = np.array([oracle.e2m1_to_double(c) for c in range(16)])
+    e8 = np.array([oracle.e8m0_to_double(b) if b != 0xFF else np.nan for b in range(256)])
+    def dec(Q, S):
+        Q, S = Q[:, :1 << 16], S[:, :1 << 12]
+        return e2[np.stack([Q & 15, Q >> 4], -1).reshape(Q.shape[0], -1)] * np.repeat(e8[S], 32, axis=1)
+    sigma = tolerance.sigma_of(dec(Aq, SA)) * tolerance.sigma_of(dec(Bq, SB))
     res = tolerance.check(C.bits(), want, K, sigma)
     assert res, res
 
