@@ -146,3 +146,23 @@ def test_mx_workload_exactly_summable_every_element():
     assert np.array_equal(oracle.gemm_mxfp4_nt_at(Aq, SA, Bq, SB, K, ms, ns), want[ms, ns])
     bad = np.argwhere(C != want)
     assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+
+
+def test_multi_round_ragged_tiles_exact_every_element():
+    # 17 x 17 = 289 tiles of 256 x 256 on a grid of at most 256 workgroups:
+    # some workgroups take a second (ragged) tile, whose first steps the ring
+    # fetched during the first tile's last ones, others stop after one.
+    # Unit scales and K = 1024: every partial sum is a multiple of 2^-2 below
+    # 2^16, exact in FP32, so every element is compared bitwise.
+    need_gpu()
+    M, N, K = 4100, 4104, 1024
+    print("mx multi-round ragged", M, N, K, flush=True)
+    Aq, Bq = syn.fp4_codes(M, K, seed=191), syn.fp4_codes(N, K, seed=192)
+    SA = syn.e8m0_scales(M, K, seed=193, u_lo=0, u_hi=0)
+    SB = syn.e8m0_scales(N, K, seed=194, u_lo=0, u_hi=0)
+    C = run_mx(Aq, SA, Bq, SB, M, N, K)
+    want = oracle.bf16_from_double(decode(Aq, SA) @ decode(Bq, SB).T)
+    ms, ns = sample_positions(M, N, 300, seed=195)
+    assert np.array_equal(oracle.gemm_mxfp4_nt_at(Aq, SA, Bq, SB, K, ms, ns), want[ms, ns])
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
