@@ -32,8 +32,8 @@
 //     each) and two of B; per block of four steps one 1 KiB scale copy (64
 //     rows of A for waves 0..3, of B for waves 4..7, 16 bytes each). Step k + 3 is
 //     requested during step k, after the barrier that frees step k - 1's
-//     stage, one copy every four matrix instructions (issued together they
-//     stall the wave).
+//     stage, one copy every two matrix instructions over the first half of
+//     the step (issued together they stall the wave).
 //   * Per step each wave issues 16 matrix instructions (2 sub-steps of K 64 x
 //     4 x 2 blocks). Fragment reads (16 bytes per lane: row l % 32 of a block,
 //     the 32 K of sub-step kk that belong to lane half l / 32) of sub-step 1
@@ -338,7 +338,7 @@ void gemm_mxfp4_nt_kernel(Problem p)
                 // after matrix instruction 2 r of sub-step 0; those of step
                 // k + 1's sub-step 0 likewise during sub-step 1, then its
                 // scales; the copies of step k + STAGES - 1 into step k - 1's
-                // stage one every three matrix instructions
+                // stage one every two matrix instructions, first half only
                 SCHED_FENCE();
                 static_for<16>([&](auto tc) {
                     constexpr int t = decltype(tc)::value;
@@ -350,8 +350,8 @@ void gemm_mxfp4_nt_kernel(Problem p)
                         else
                             read_frag(next_stage, 0, 0, u);
                     }
-                    if constexpr (t % 4 == 1)
-                        copy_one(k + STAGES - 1, copy_stage, t / 4);
+                    if constexpr (t % 2 == 1 && t < 2 * COPIES)
+                        copy_one(k + STAGES - 1, copy_stage, t / 2);
                     if constexpr (t == 15)
                         read_scales(k + 1, sbuf ^ 1);
                     SCHED_VALU_ONLY();
