@@ -148,6 +148,9 @@ bool extent_ok(int64_t rows, int64_t row_bytes)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// One launch of a persistent kernel on `stream`: tile counts for tile_m x
+// tile_n output tiles, the supergroup width, a grid of at most one workgroup
+// per compute unit, `threads` work-items per workgroup.
 template <class Kernel>
 int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n = BN, int threads = gemm355::THREADS)
 {

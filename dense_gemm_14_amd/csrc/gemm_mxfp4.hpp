@@ -73,11 +73,14 @@ constexpr int THREADS_MX = 512;                  // 8 waves, two per SIMD
 constexpr int COPIES = 4;                        // code copies per wave and step (2 + 2)
 constexpr int SCALE_COPIES = 1;                  // per wave and scale block (A or B)
 constexpr int EPILOGUE_STORES = 16;              // 16-byte stores per wave per tile (128 x 64 BF16)
+constexpr int EPILOGUE_LOADS = 8;                // fused epilogue: bias loads per wave (2 x 4 column runs)
 
 static_assert(LDS_BYTES <= 163840, "LDS ring exceeds the 160 KiB of a gfx950 workgroup");
 static_assert(TM == 256 && TN == 256 && THREADS_MX == 512, "the copy map assumes 256 x 256 tiles and 8 waves");
-// in flight at most: the copies of three steps ahead and one epilogue
-static_assert((STAGES - 1) * COPIES + SCALE_COPIES + EPILOGUE_STORES <= 63,
+// in flight at most: the copies of three steps ahead, a scale block and one
+// epilogue's loads and stores (at a tile boundary fewer: the next tile's
+// steps 1 and 2 and the epilogue)
+static_assert((STAGES - 1) * COPIES + SCALE_COPIES + EPILOGUE_LOADS + EPILOGUE_STORES <= 63,
               "vmcnt counts at most 63 outstanding operations");
 
 // Physical 16-byte chunk position of logical chunk c (0..3) in tile row r.
