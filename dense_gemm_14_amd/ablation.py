@@ -3,6 +3,7 @@
     python -m dense_gemm_14_amd.ablation instances [--csv FILE]
     python -m dense_gemm_14_amd.ablation supergroup [--csv FILE]
     python -m dense_gemm_14_amd.ablation streams [--csv FILE]
+    python -m dense_gemm_14_amd.ablation mx_supergroup [--csv FILE]
 
 ``instances`` times the three BF16 instances (forced through
 gemm355_force_instance) and the automatic choice on the shape grid
@@ -16,7 +17,9 @@ large shapes M, N in {4096, 8192, 16384}, K in {1024, 4096, 16384}.
 against the same products alternating over two streams, which lets one
 product's workgroups start on units the other's tail leaves idle (the
 question of "Kernel 6", "The Gap Between Grids", without programmatic
-dependent launch).
+dependent launch). ``mx_supergroup`` times the band width for the
+microscaled FP4 product (gemm_mxfp4_nt; same 256 x 256 tiles, a quarter of
+the operand bytes per tile) at 8192^3 and 16384 x 16384 x 8192.
 
 Every configuration of a shape is timed in three round-robin passes and the
 minimum kept (the first configuration timed on fresh buffers runs slow).
@@ -154,16 +157,63 @@ def streams(csv):
         torch.cuda.empty_cache()
 
 
+def _mx_sets(M, N, K):
+    import synthetic as syn
+    per = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + 2 * M * N
+    n = max(2, -(-(600 << 20) // per))
+    sets = []
+    for s in range(n):
+        Aq, SA = syn.mxfp4_operand(M, K, 10 + s)
+        Bq, SB = syn.mxfp4_operand(N, K, 20 + s)
+        sets.append([torch.from_numpy(x).cuda() for x in (Aq, SA, Bq, SB)] +
+                    [torch.empty(M * N, dtype=torch.int16, device="cuda")])
+    return sets
+
+
+def mx_supergroup(csv):
+    widths = [2, 4, 8, 16, 32]
+    print("#     M      N      K  " + " ".join("%8s" % ("w=%d" % w) for w in widths) + "   best  best/w8   [us]")
+    for M, N, K in [(8192, 8192, 8192), (16384, 16384, 8192)]:
+        sets = _mx_sets(M, N, K)
+        n = len(sets)
+        best = {}
+        try:
+            for _ in range(3):
+                for w in widths:
+                    g.force_supergroup(w)
+                    for i in range(4):
+                        g.gemm_mxfp4_nt(M, N, K, *sets[i % n])
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    reps = 100 if M * N < 1e8 else 30
+                    e0.record()
+                    for i in range(reps):
+                        g.gemm_mxfp4_nt(M, N, K, *sets[i % n])
+                    e1.record()
+                    torch.cuda.synchronize()
+                    best[w] = min(best.get(w, float("inf")), e0.elapsed_time(e1) / reps * 1e3)
+        finally:
+            g.force_supergroup(0)
+        b = min(best, key=best.get)
+        print("%7d %6d %6d  " % (M, N, K) + " ".join("%8.1f" % best[w] for w in widths) +
+              "  %5d  %7.3f" % (b, best[b] / best[8]), flush=True)
+        if csv:
+            for w, us in best.items():
+                csv.write("%d,%d,%d,%d,%.2f\n" % (M, N, K, w, us))
+        del sets
+        torch.cuda.empty_cache()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("what", choices=["instances", "supergroup", "streams"])
+    ap.add_argument("what", choices=["instances", "supergroup", "streams", "mx_supergroup"])
     ap.add_argument("--csv", default=None, help="also write M,N,K,config,us rows here")
     args = ap.parse_args(argv)
     if not torch.cuda.is_available():
         sys.exit("the ablation needs a GPU")
     csv = open(args.csv, "w") if args.csv else None
     try:
-        {"instances": instances, "supergroup": supergroup, "streams": streams}[args.what](csv)
+        {"instances": instances, "supergroup": supergroup, "streams": streams,
+         "mx_supergroup": mx_supergroup}[args.what](csv)
     finally:
         if csv:
             csv.close()
