@@ -81,3 +81,17 @@ def test_sampled_elements_match_whole_product():
     whole = oracle.gemm_mxfp4_nt(Aq, SA, Bq, SB, K)
     ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
     assert np.array_equal(oracle.gemm_mxfp4_nt_at(Aq, SA, Bq, SB, K, ms, ns).reshape(M, N), whole)
+
+
+def test_mx_fused_oracle_rejects_bad_arguments():
+    # K not a multiple of 32, an unknown activation, an index out of range
+    Aq, SA = syn.mxfp4_operand(2, 64, seed=301)
+    Bq, SB = syn.mxfp4_operand(3, 64, seed=302)
+    ms, ns = np.array([0, 1]), np.array([2, 0])
+    for act in (-1, 3):
+        with pytest.raises(ValueError):
+            oracle.gemm_mxfp4_nt_bias_act_at(Aq, SA, Bq, SB, 64, None, act, ms, ns)
+    with pytest.raises(ValueError):
+        oracle.gemm_mxfp4_nt_bias_act_at(Aq, SA, Bq, SB, 64, None, oracle.ACT_NONE, np.array([2]), np.array([0]))
+    with pytest.raises(ValueError):
+        oracle.gemm_mxfp4_nt_bias_act_at(Aq[:, :8], SA[:, :1], Bq[:, :8], SB[:, :1], 16, None, oracle.ACT_NONE, ms, ns)
