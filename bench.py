@@ -8,16 +8,30 @@ measurement method of "NVFP4 GEMM on Blackwell", section "Benchmarking":
 separate warm-up and timed iterations, buffer rotation, uniform data).
 
 A step is one call of the library's entry point on one input set that is
-already resident in device memory. W warm-up steps run first, then exactly K
-timed steps bracketed by device synchronisation; HIP events recorded on the
-launch stream time them. One JSON line goes to stdout:
+already resident in device memory. W warm-up steps run first; if they took
+less than --warm-seconds of wall time, more untimed steps follow until they
+have (the board's clock and power settle within about a second of sustained
+load; the extra steps are reported in their own field and `warmup` stays W).
+Then exactly K timed steps run, bracketed by device synchronisation; HIP
+events recorded on the launch stream time them. A second pass times each of
+--launch-samples launches with its own event pair, for the spread. The GPU
+clock and socket power are sampled (amdsmi gpu_metrics) during both passes.
+One JSON line goes to stdout:
   value      TFLOP/s over the K timed steps (2 M N K per step);
   roofline   the kernel's achieved TFLOP/s (algorithmic FLOPs per launch over
-             the mean launch duration) against the dense peak of its operand
-             type, plus HBM traffic per launch from the committed rocprofv3
-             counter summary when it was taken from the current kernel source;
+             the mean launch duration of the timed steps) against the dense
+             peak of its operand type, plus the L2-egress traffic per launch
+             (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy) from the
+             committed rocprofv3 counter summary when it was taken from the
+             current kernel source;
+  launch_ms  mean, p10, p50, p90, min, max of the per-launch pass;
+  clock      mean GPU clock (MHz, over the XCDs) and socket power (W) sampled
+             during the timed steps and during the per-launch pass;
   cpu_baseline  the plain CPU oracle timed on a bounded sample of the same
              workload's output elements on this host's cores.
+
+--parity-full compares every element of set 0's C with the oracle (minutes of
+CPU time at 8192^3) and adds the result to the line.
 
 Other workloads (--workload): bf16_4096, bf16_8000, bf16_skinny (128 x 8192 x
 8192, HBM roofline), bf16_256, fp4_8192 (E2M1 + E4M3 per 16, decoded to FP16),
@@ -39,7 +53,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 LLC_BYTES = 256 << 20                  # MI355X Infinity Cache (last-level cache)
-PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp4": 10100.0}  # published dense MFMA peaks
+# Dense matrix-core peaks of MI355X (the datasheet's 2.5 PFLOP/s BF16/FP16 and
+# 10.1 PFLOP/s FP4, exactly: 256 CUs x 2.4 GHz x 4096 BF16 FLOP per clock, and
+# four times that for FP4)
+PEAK_TFLOPS = {"bf16": 2516.58, "fp16": 2516.58, "fp4": 10066.33}
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {
@@ -143,8 +160,12 @@ def launcher(kind, M, N, K, stream):
     return lambda ops, C: g.gemm_nvfp4_nt(M, N, K, *ops, C, stream=stream)
 
 
-def read_traffic(workload: str, launches_flops: float):
-    """HBM bytes per launch from the committed counter summary, if current."""
+def read_traffic(workload: str):
+    """L2-egress bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by a
+    plain copy of known size) from the committed counter summary, or None when
+    it was taken from other kernel sources. These counters count the bytes L2
+    requests from the fabric, which include hits in the 256 MiB last-level
+    cache, so they bound the HBM bytes from above."""
     path = os.path.join(PROFILE_DIR, "traffic_%s.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -156,9 +177,159 @@ def read_traffic(workload: str, launches_flops: float):
     if fields.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields["l2_egress_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+class ClockSampler:
+    """Samples the GPU clock (mean over the XCDs' current gfx clocks) and the
+    socket power from the driver's gpu_metrics table in a background thread,
+    through the amdsmi Python module (read-only queries; no HIP calls)."""
+
+    def __init__(self, period_s: float = 0.005):
+        import threading
+        self.period = period_s
+        self.samples = []   # (time.perf_counter(), mhz, watts)
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._handle = self._match(amdsmi, handles)
+            self._amdsmi = amdsmi
+        except Exception as e:   # no driver access: the line then says why
+            self.error = "%s: %s" % (type(e).__name__, e)
+
+    @staticmethod
+    def _match(amdsmi, handles):
+        """The handle of torch's device 0 (by PCI bus), else the only one."""
+        import torch
+        if len(handles) == 1:
+            return handles[0]
+        props = torch.cuda.get_device_properties(0)
+        bus = getattr(props, "pci_bus_id", None)
+        for h in handles:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+            if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                return h
+        return handles[0]
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = m.get("current_gfxclks")
+        vals = [c for c in clks if isinstance(c, (int, float)) and 0 < c < 10000] if isinstance(clks, list) else []
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [m["current_gfxclk"]]
+        mhz = sum(vals) / len(vals) if vals else None
+        w = m.get("current_socket_power")
+        if not isinstance(w, (int, float)) or not 0 < w < 10000:
+            w = m.get("average_socket_power")
+        watts = w if isinstance(w, (int, float)) and 0 < w < 10000 else None
+        return mhz, watts
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                mhz, watts = self._read()
+                self.samples.append((time.perf_counter(), mhz, watts))
+            except Exception as e:
+                self.error = "%s: %s" % (type(e).__name__, e)
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self._handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def window(self, t0: float, t1: float):
+        """Mean, min and max clock and mean power of the samples in [t0, t1]."""
+        s = [x for x in self.samples if t0 <= x[0] <= t1]
+        mhz = [x[1] for x in s if x[1] is not None]
+        w = [x[2] for x in s if x[2] is not None]
+        # the driver refreshes the table at a coarse interval: count the
+        # distinct readings so a stale window shows as one
+        out = {"samples": len(s), "distinct": len(set((x[1], x[2]) for x in s))}
+        if mhz:
+            out.update({"gfx_mhz_mean": round(sum(mhz) / len(mhz), 1), "gfx_mhz_min": round(min(mhz), 1),
+                        "gfx_mhz_max": round(max(mhz), 1)})
+        if w:
+            out["socket_w_mean"] = round(sum(w) / len(w), 1)
+        return out
+
+
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"n": int(a.size), "mean": round(float(a.mean()), 5),
+            **{"p%d" % q: round(float(np.percentile(a, q)), 5) for q in (10, 50, 90)},
+            "min": round(float(a.min()), 5), "max": round(float(a.max()), 5)}
+
+
+def host_operands(kind, ops):
+    """Set 0's operands as numpy arrays of raw bits (BF16 as uint16)."""
+    import numpy as np
+    host = [o.cpu().numpy() for o in ops]
+    if kind in ("bf16", "bf16_gelu"):
+        host = [h.view(np.uint16) for h in host]
+    return host
+
+
+def parity_sigma(kind, host, K):
+    """sigma_A * sigma_B of the decoded operands (from their first 256 rows)
+    for the FP4 bound; 1 for BF16 inputs in [-1, 1]."""
+    import numpy as np
+    import oracle
+    from tests import tolerance
+    if kind == "fp4":
+        sub = slice(0, 256)
+        return (tolerance.sigma_of(oracle.decode_nvfp4(host[0][sub], host[1][sub], K)) *
+                tolerance.sigma_of(oracle.decode_nvfp4(host[2][sub], host[3][sub], K)))
+    if kind == "mx":
+        e2 = np.array([oracle.e2m1_to_double(c) for c in range(16)])
+        e8 = np.array([oracle.e8m0_to_double(b) if b != 0xFF else np.nan for b in range(256)])
+
+        def dec(Q, S):
+            Q, S = Q[:256], S[:256]
+            return e2[np.stack([Q & 15, Q >> 4], -1).reshape(Q.shape[0], -1)] * np.repeat(e8[S], 32, axis=1)
+        return tolerance.sigma_of(dec(host[0], host[1])) * tolerance.sigma_of(dec(host[2], host[3]))
+    return 1.0
+
+
+def parity_full(kind, M, N, K, sets):
+    """Every element of set 0's C against the oracle (run after the timing)."""
+    import numpy as np
+    import oracle
+    from tests import tolerance
+    (ops, C) = sets[0]
+    host = host_operands(kind, ops)
+    got = C.cpu().numpy().view(np.uint16).reshape(M, N)
+    t0 = time.perf_counter()
+    if kind == "bf16":
+        chk = tolerance.check(got, oracle.gemm_bf16_nt(host[0], host[1]), K)
+    elif kind == "bf16_gelu":
+        ms, ns = (x.ravel().astype(np.int32) for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+        ref, z = oracle.gemm_bf16_nt_bias_act_at(host[0], host[1], host[2], oracle.ACT_GELU_TANH, ms, ns,
+                                                 with_z=True)
+        chk = tolerance.check_fused(got, ref.reshape(M, N), z.reshape(M, N), K, oracle.ACT_GELU_TANH)
+    elif kind == "mx":
+        chk = tolerance.check(got, oracle.gemm_mxfp4_nt(*host, K), K, parity_sigma(kind, host, K))
+    else:
+        chk = tolerance.check(got, oracle.gemm_nvfp4_nt(*host, K), K, parity_sigma(kind, host, K))
+    return {"elements": M * N, "within_tolerance": bool(chk), "worst_ratio": round(float(chk.worst_ratio), 4),
+            "failures": int(chk.n_bad), "oracle_seconds": round(time.perf_counter() - t0, 1),
+            "cores": oracle.max_threads()}
 
 
 def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
@@ -168,12 +339,12 @@ def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
     import synthetic as syn
     from tests import tolerance
     (ops, C) = sets[0]
-    host = [o.cpu().numpy() for o in ops]
+    host = host_operands(kind, ops)
     if kind == "bf16":
-        A, B = (h.view(np.uint16) for h in host)
+        A, B = host
         fn = lambda ms, ns: oracle.gemm_bf16_nt_at(A, B, ms, ns)
     elif kind == "bf16_gelu":
-        A, B, bias = (h.view(np.uint16) for h in host)
+        A, B, bias = host
         fn = lambda ms, ns: oracle.gemm_bf16_nt_bias_act_at(A, B, bias, oracle.ACT_GELU_TANH, ms, ns, with_z=True)
     elif kind == "mx":
         Aq, SA, Bq, SB = host
@@ -198,19 +369,7 @@ def cpu_baseline(kind, M, N, K, sets, seconds_target, seed=0):
         ref, z = ref
     # the same sample doubles as a spot check of the GPU output of set 0
     got = C.cpu().numpy().view(np.uint16).reshape(M, N)[ms, ns]
-    sigma = 1.0
-    if kind == "fp4":
-        sub = slice(0, min(M, 256))
-        sigma = (tolerance.sigma_of(oracle.decode_nvfp4(host[0][sub], host[1][sub], K)) *
-                 tolerance.sigma_of(oracle.decode_nvfp4(host[2][sub], host[3][sub], K)))
-    if kind == "mx":
-        # decoded rows from the oracle's per-code and per-scale values
-        e2 = np.array([oracle.e2m1_to_double(c) for c in range(16)])
-        e8 = np.array([oracle.e8m0_to_double(b) if b != 0xFF else np.nan for b in range(256)])
-        def dec(Q, S):
-            Q, S = Q[:256], S[:256]
-            return e2[np.stack([Q & 15, Q >> 4], -1).reshape(Q.shape[0], -1)] * np.repeat(e8[S], 32, axis=1)
-        sigma = tolerance.sigma_of(dec(host[0], host[1])) * tolerance.sigma_of(dec(host[2], host[3]))
+    sigma = parity_sigma(kind, host, K)
     if kind == "bf16_gelu":
         chk = tolerance.check_fused(got, ref, z, K, oracle.ACT_GELU_TANH)
     else:
@@ -243,11 +402,17 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warm-seconds", type=float, default=1.5,
+                    help="least wall time of untimed warm-up; steps beyond --warmup are reported apart")
+    ap.add_argument("--launch-samples", type=int, default=300,
+                    help="launches timed one by one (own event pair each) for the spread")
     ap.add_argument("--workload", default="bf16_8192", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (used for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the oracle's timed sample")
+    ap.add_argument("--parity-full", action="store_true",
+                    help="also compare every element of set 0's C with the oracle")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -274,30 +439,59 @@ def main(argv=None):
     sets = make_sets(kind, M, N, K, n_sets, CONFIG_INDEX[args.workload])
     stream = torch.cuda.current_stream()
     run = launcher(kind, M, N, K, stream)
+    clock = ClockSampler().start()
 
+    # warm-up: W steps, then more until --warm-seconds of sustained work
+    t_warm = time.perf_counter()
+    i = 0
     for i in range(args.warmup):
         run(*sets[i % n_sets])
     torch.cuda.synchronize()
+    extra = 0
+    while time.perf_counter() - t_warm < args.warm_seconds:
+        for _ in range(16):
+            run(*sets[(args.warmup + extra) % n_sets])
+            extra += 1
+        torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_warm
+    first = args.warmup + extra   # the timed steps continue the rotation
 
+    # timed region: exactly K steps between two events on the launch stream
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        run(*sets[i % n_sets])
+        run(*sets[(first + i) % n_sets])
     stop.record(stream)
     torch.cuda.synchronize()
+    t1 = time.perf_counter()
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / max(args.steps, 1)
     flops = 2.0 * M * N * K
     tflops = flops / (ms_step * 1e-3) / 1e12
 
-    # output of set 0 for the spot check: make sure it was produced last-ish
+    # per-launch pass: each launch between its own pair of events
+    P = max(args.launch_samples, 0)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(P)]
+    t2 = time.perf_counter()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        run(*sets[(first + args.steps + i) % n_sets])
+        b.record(stream)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    clock.stop()
+    launch_ms = percentiles([a.elapsed_time(b) for a, b in evs]) if P else None
+
+    # output of set 0 for the spot checks: recomputed last
     run(*sets[0])
     torch.cuda.synchronize()
 
     # NVFP4 operands are decoded to FP16 for the MFMA; MX operands enter it as FP4
     dtype = {"fp4": "fp16", "mx": "fp4"}.get(kind, "bf16")
-    traffic = read_traffic(args.workload, flops)
+    traffic = read_traffic(args.workload)
     alg_bytes = algorithmic_bytes(kind, M, N, K)
     ridge = PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
     if flops / alg_bytes >= ridge:
@@ -308,8 +502,15 @@ def main(argv=None):
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    roofline.update({"kernel": " + ".join(kernels_for(kind, M, N, K, cus)), "traffic": traffic,
+    roofline.update({"traffic": traffic,
+                     "traffic_kind": "l2_egress_bytes_per_launch (FETCH_SIZE + WRITE_SIZE scaled by a plain copy; "
+                                     "includes last-level-cache hits, so an upper bound on HBM bytes)",
+                     "kernel": " + ".join(kernels_for(kind, M, N, K, cus)),
                      "algorithmic_bytes": alg_bytes, "mean_launch_ms": round(ms_step, 5)})
+    clk = {"source": "amdsmi gpu_metrics (current gfx clock, mean over XCDs; socket power)",
+           "timed": clock.window(t0, t1), "per_launch_pass": clock.window(t2, t3)}
+    if clock.error:
+        clk["error"] = clock.error
     out = {
         "metric": "TFLOP/s for BF16 C=A·B^T at M=N=K=8192; % of MI355X dense BF16 peak"
         if args.workload == "bf16_8192" else
@@ -331,10 +532,19 @@ def main(argv=None):
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "percent_of_peak": round(100.0 * tflops / PEAK_TFLOPS[dtype], 2),
+        "warmup_extra": {"steps": extra, "seconds_total": round(warm_s, 3), "floor_seconds": args.warm_seconds},
+        "launch_ms": launch_ms,
+        "launch_tflops_p50": round(flops / (launch_ms["p50"] * 1e-3) / 1e12, 2) if launch_ms else None,
+        "clock": clk,
+        "device": {"name": torch.cuda.get_device_properties(0).name, "compute_units": cus},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(kind, M, N, K, sets, args.cpu_seconds)
+    if args.parity_full:
+        out["parity_full"] = parity_full(kind, M, N, K, sets)
     print(json.dumps(out), flush=True)
+    if args.parity_full and not out["parity_full"]["within_tolerance"]:
+        return 3
     return 0
 
 
