@@ -8,13 +8,17 @@ The functions mirror the C entry points declared in ``include/gemm355.h``:
 
     gemm_bf16_nt(M, N, K, A, B, C, stream=None)
     gemm_bf16_nt_bias_act(M, N, K, A, B, bias, activation, C, stream=None)
+    gemm_bf16_nt_ws(M, N, K, A, B, C, workspace, workspace_bytes=None, stream=None)
+    gemm_bf16_nt_bias_act_ws(M, N, K, A, B, bias, activation, C, workspace, workspace_bytes=None, stream=None)
+    workspace_size(M, N, K)           # bytes the *_ws calls need on the current device
     gemm_nvfp4_nt(M, N, K, Aq, SFA, Bq, SFB, C, stream=None)
     gemm_nvfp4_nt_bias_act(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, stream=None)
     gemm_mxfp4_nt(M, N, K, Aq, SA, Bq, SB, C, stream=None)
     gemm_mxfp4_nt_bias_act(M, N, K, Aq, SA, Bq, SB, bias, activation, C, stream=None)
     force_instance(instance)          # BF16 instance override (diagnostic)
     force_supergroup(width)           # band width of the tile order (diagnostic)
-    bf16_plan(M, N, K, compute_units)  # (instance, splits) gemm_bf16_nt would run
+    bf16_plan(M, N, K, compute_units, with_workspace=False)  # (instance, splits) a BF16 call would run
+    bf16_plan_workspace_bytes(M, N, K, compute_units)  # workspace bytes of the *_ws plan
 
 Operands may be torch tensors on a ROCm device (their storage is checked
 against the sizes before the call, since the C side cannot see it) or raw
@@ -45,7 +49,7 @@ ACT_GELU_TANH = 2
 INSTANCE_AUTO = 0    # gemm_bf16_nt picks the instance by shape
 INSTANCE_LARGE = 1   # 256 x 256 output tiles
 INSTANCE_SMALL = 2   # 64 x 64 output tiles
-INSTANCE_SPLITK = 3  # 128 x 128 output tiles, K split over workgroups, FP32 partials reduced
+INSTANCE_SPLITK = 3  # 128 x 128 output tiles; with a workspace (the *_ws calls) K split over workgroups
 
 _lib = None
 
@@ -73,6 +77,13 @@ def load() -> ctypes.CDLL:
     lib.gemm_bf16_nt.restype = i
     lib.gemm_bf16_nt_bias_act.argtypes = [i, i, i, p, p, p, i, p, p]
     lib.gemm_bf16_nt_bias_act.restype = i
+    sz = ctypes.c_size_t
+    lib.gemm_bf16_nt_ws.argtypes = [i, i, i, p, p, p, p, sz, p]
+    lib.gemm_bf16_nt_ws.restype = i
+    lib.gemm_bf16_nt_bias_act_ws.argtypes = [i, i, i, p, p, p, i, p, p, sz, p]
+    lib.gemm_bf16_nt_bias_act_ws.restype = i
+    lib.gemm_bf16_nt_workspace_size.argtypes = [i, i, i, ctypes.POINTER(sz)]
+    lib.gemm_bf16_nt_workspace_size.restype = i
     lib.gemm_nvfp4_nt.argtypes = [i, i, i, p, p, p, p, p, p]
     lib.gemm_nvfp4_nt.restype = i
     lib.gemm_nvfp4_nt_bias_act.argtypes = [i, i, i, p, p, p, p, p, i, p, p]
@@ -91,7 +102,7 @@ def load() -> ctypes.CDLL:
     lib.gemm355_force_instance.restype = i
     lib.gemm355_force_supergroup.argtypes = [i]
     lib.gemm355_force_supergroup.restype = i
-    lib.gemm355_bf16_plan.argtypes = [i, i, i, i, p, p]
+    lib.gemm355_bf16_plan.argtypes = [i, i, i, i, i, p, p, p]
     lib.gemm355_bf16_plan.restype = i
     _lib = lib
     return lib
@@ -170,6 +181,59 @@ def gemm_bf16_nt_bias_act(M: int, N: int, K: int, A, B, bias, activation: int, C
            "gemm_bf16_nt_bias_act")
 
 
+def _workspace(ws, nbytes):
+    """(address, bytes) of a workspace tensor, int address or None."""
+    if ws is None:
+        return None, 0 if nbytes is None else int(nbytes)
+    if isinstance(ws, int):
+        if nbytes is None:
+            raise ValueError("workspace_bytes is needed with a raw workspace address")
+        return ws, int(nbytes)
+    have = ws.numel() * ws.element_size()
+    nb = have if nbytes is None else int(nbytes)
+    if nb > have:
+        raise ValueError("workspace holds %d bytes, workspace_bytes says %d" % (have, nb))
+    return _addr(ws, nb, "workspace"), nb
+
+
+def gemm_bf16_nt_ws(M: int, N: int, K: int, A, B, C, workspace, workspace_bytes=None, stream=None) -> None:
+    """gemm_bf16_nt with a caller-owned workspace (a device tensor of at least
+    workspace_size(M, N, K) bytes, or None when that is 0), which lets the
+    128 x 128 instance split K."""
+    lib = load()
+    M, N, K = int(M), int(N), int(K)
+    nz = M > 0 and N > 0
+    a = _addr(A, M * K * 2 if nz else 0, "A")
+    b = _addr(B, N * K * 2 if nz else 0, "B")
+    c = _addr(C, M * N * 2 if nz else 0, "C")
+    w, nb = _workspace(workspace, workspace_bytes)
+    _check(lib.gemm_bf16_nt_ws(M, N, K, a, b, c, w, nb, _stream(stream)), "gemm_bf16_nt_ws")
+
+
+def gemm_bf16_nt_bias_act_ws(M: int, N: int, K: int, A, B, bias, activation: int, C, workspace,
+                             workspace_bytes=None, stream=None) -> None:
+    """gemm_bf16_nt_bias_act with a caller-owned workspace (see gemm_bf16_nt_ws)."""
+    lib = load()
+    M, N, K = int(M), int(N), int(K)
+    nz = M > 0 and N > 0
+    a = _addr(A, M * K * 2 if nz else 0, "A")
+    b = _addr(B, N * K * 2 if nz else 0, "B")
+    bb = _addr(bias, N * 2 if nz else 0, "bias")
+    c = _addr(C, M * N * 2 if nz else 0, "C")
+    w, nb = _workspace(workspace, workspace_bytes)
+    _check(lib.gemm_bf16_nt_bias_act_ws(M, N, K, a, b, bb, int(activation), c, w, nb, _stream(stream)),
+           "gemm_bf16_nt_bias_act_ws")
+
+
+def workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace gemm_bf16_nt_ws / gemm_bf16_nt_bias_act_ws need for
+    this shape on the current device (0: no split, no workspace)."""
+    out = ctypes.c_size_t(0)
+    _check(load().gemm_bf16_nt_workspace_size(int(M), int(N), int(K), ctypes.byref(out)),
+           "gemm_bf16_nt_workspace_size")
+    return out.value
+
+
 def gemm_nvfp4_nt(M: int, N: int, K: int, Aq, SFA, Bq, SFB, C, stream=None) -> None:
     """C (M x N, BF16) = dec(Aq, SFA) @ dec(Bq, SFB)^T for E2M1 codes + E4M3 scales."""
     lib = load()
@@ -241,14 +305,24 @@ def force_supergroup(width: int) -> None:
     _check(load().gemm355_force_supergroup(width), "gemm355_force_supergroup")
 
 
-def bf16_plan(M: int, N: int, K: int, compute_units: int):
-    """(instance, splits) that gemm_bf16_nt runs for this shape on a device
-    with `compute_units` compute units; host only."""
+def _plan(M, N, K, compute_units, with_workspace):
     inst = ctypes.c_int(0)
     splits = ctypes.c_int(0)
-    _check(load().gemm355_bf16_plan(M, N, K, compute_units, ctypes.byref(inst), ctypes.byref(splits)),
-           "gemm355_bf16_plan")
-    return inst.value, splits.value
+    nbytes = ctypes.c_size_t(0)
+    _check(load().gemm355_bf16_plan(M, N, K, compute_units, int(bool(with_workspace)), ctypes.byref(inst),
+                                    ctypes.byref(splits), ctypes.byref(nbytes)), "gemm355_bf16_plan")
+    return inst.value, splits.value, nbytes.value
+
+
+def bf16_plan(M: int, N: int, K: int, compute_units: int, with_workspace: bool = False):
+    """(instance, splits) that gemm_bf16_nt (or, with_workspace, gemm_bf16_nt_ws)
+    runs for this shape on a device with `compute_units` compute units; host only."""
+    return _plan(M, N, K, compute_units, with_workspace)[:2]
+
+
+def bf16_plan_workspace_bytes(M: int, N: int, K: int, compute_units: int) -> int:
+    """Workspace bytes of gemm_bf16_nt_ws's plan on such a device; host only."""
+    return _plan(M, N, K, compute_units, True)[2]
 
 
 def tile_order(tiles_m: int, tiles_n: int, supergroup: int):

@@ -51,11 +51,10 @@ struct Problem {
 
 // ---- fused epilogue --------------------------------------------------------
 //
-// An element-wise step applied to the FP32 accumulator before it is rounded
-// to BF16, while it still sits in registers ("NVFP4 GEMM on Blackwell",
-// "Kernel 1", "Epilogue Warps": the epilogue is where activations and other
-// element-wise operations would be fused): z = acc + bias[n] in FP32, then
-// the activation in FP32.
+// This library's fused epilogue ("NVFP4 GEMM on Blackwell", "Kernel 1",
+// "Epilogue Warps"): each FP32 sum gets its column's bias added and then the
+// chosen activation, both in FP32 and while the sum is still in registers,
+// and only then is it rounded to BF16 -- z = acc + bias[n], y = act(z).
 enum Activation { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2 };
 // Kernel template argument EPI: EPI_PLAIN (no fused epilogue: C = the rounded
 // sum), or the Activation of the fused epilogue (bias added in every case).

@@ -1,13 +1,14 @@
-// gemm355.hip -- host side of libgemm355: argument checks, grid sizing and
-// launches of the gfx950 kernels in gemm_bf16.hpp and gemm_fp4.hpp. The C ABI
-// is declared in include/gemm355.h.
+// gemm355.hip -- host side of libgemm355: argument checks, instance plans,
+// grid sizing and launches of the gfx950 kernels (gemm_bf16*.hpp,
+// gemm_fp4.hpp, gemm_mxfp4.hpp). The C ABI is declared in include/gemm355.h.
+// Nothing here allocates memory: the split-K partials live in a workspace the
+// caller passes to the *_ws entry points.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <stdint.h>
-#include <vector>
 
 #include "gemm355.h"
 #include "gemm_bf16.hpp"
@@ -54,22 +55,6 @@ constexpr double kHbmBytesPerUs = 4.5e6;
 std::mutex g_cu_lock;
 int g_cu_count[kMaxDevices];   // 0 = not queried yet
 
-// Workspace for the split-K partials: one buffer per (device, stream), used
-// only by work enqueued on that stream, so calls on one stream reuse it in
-// stream order and calls on different streams never share one. Buffers come
-// from a per-device memory pool of the library's own and grow with
-// stream-ordered allocation (the old buffer is freed on the same stream, after
-// the work already enqueued there); the pool keeps its memory.
-std::mutex g_pool_lock;
-hipMemPool_t g_pool[kMaxDevices];
-struct StreamWorkspace {
-    int dev;
-    hipStream_t stream;
-    void *ptr;
-    size_t bytes;
-};
-std::vector<StreamWorkspace> g_workspaces;   // guarded by g_pool_lock
-
 // Compute units of the current device, queried once per device.
 int compute_units(int *cus)
 {
@@ -87,45 +72,16 @@ int compute_units(int *cus)
     return GEMM355_OK;
 }
 
-// The workspace of `stream` on the current device, at least `bytes` long.
-int stream_workspace(hipStream_t stream, size_t bytes, void **ws)
+// One kernel launch on `stream`. The launch's own return code is the status:
+// the thread's pending HIP error is neither read nor cleared, so an error the
+// caller has not collected yet stays theirs.
+template <class Kernel, class Args>
+int launch_kernel(Kernel kernel, unsigned blocks, unsigned threads, Args &args, hipStream_t stream)
 {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return GEMM355_ERR_NO_DEVICE;
-    std::lock_guard<std::mutex> guard(g_pool_lock);
-    if (!g_pool[dev]) {
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t created = nullptr;
-        if (hipMemPoolCreate(&created, &props) != hipSuccess)
-            return GEMM355_ERR_LAUNCH;
-        uint64_t keep = UINT64_MAX;   // never hand memory back between calls
-        (void)hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep);
-        g_pool[dev] = created;
-    }
-    for (StreamWorkspace &w : g_workspaces) {
-        if (w.dev != dev || w.stream != stream)
-            continue;
-        if (w.bytes < bytes) {
-            void *grown = nullptr;
-            if (hipMallocFromPoolAsync(&grown, bytes, g_pool[dev], stream) != hipSuccess)
-                return GEMM355_ERR_LAUNCH;
-            (void)hipFreeAsync(w.ptr, stream);
-            w.ptr = grown;
-            w.bytes = bytes;
-        }
-        *ws = w.ptr;
-        return GEMM355_OK;
-    }
-    void *fresh = nullptr;
-    if (hipMallocFromPoolAsync(&fresh, bytes, g_pool[dev], stream) != hipSuccess)
-        return GEMM355_ERR_LAUNCH;
-    g_workspaces.push_back({dev, stream, fresh, bytes});
-    *ws = fresh;
-    return GEMM355_OK;
+    void *argv[] = {&args};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3(blocks), dim3(threads), argv,
+                                         0, stream);
+    return e == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -164,14 +120,13 @@ int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n =
     const int sg = g_supergroup.load(std::memory_order_relaxed);
     p.supergroup = sg > 0 ? sg : kSupergroup;
     p.grid = gemm355::persistent_grid(p.tiles, cus);
-    (void)hipGetLastError(); // clear a stale error so the check below is ours
-    hipLaunchKernelGGL(kernel, dim3(p.grid), dim3(threads), 0, static_cast<hipStream_t>(stream), p);
-    return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
+    return launch_kernel(kernel, (unsigned)p.grid, (unsigned)threads, p, static_cast<hipStream_t>(stream));
 }
 
 // Split-K plan for 128 x 128 tiles: enough splits to give every compute unit a
-// work item (at most MAX_SPLITS), each split at least 8 K steps long.
-void splitk_plan(int M, int N, int K, int cus, int *tiles_m, int *tiles_n, int *splits, int *steps_per_split)
+// work item (at most max_splits), each split at least 8 K steps long.
+void splitk_plan(int M, int N, int K, int cus, int max_splits, int *tiles_m, int *tiles_n, int *splits,
+                 int *steps_per_split)
 {
     namespace sk = gemm355::bf16_splitk;
     *tiles_m = (int)ceil_div(M, sk::TM);
@@ -179,7 +134,7 @@ void splitk_plan(int M, int N, int K, int cus, int *tiles_m, int *tiles_n, int *
     const int64_t tiles = int64_t(*tiles_m) * *tiles_n;
     const int nk = (int)ceil_div(K, sk::BK);
     int s = (int)std::max<int64_t>(1, cus / std::max<int64_t>(1, tiles));
-    s = std::min(s, sk::MAX_SPLITS);
+    s = std::min(s, max_splits);
     s = std::max(1, std::min(s, nk / 8));
     const int per = (int)std::max<int64_t>(1, ceil_div(nk, s));
     *steps_per_split = per;
@@ -210,34 +165,46 @@ double estimate_split(int M, int N, int K, int cus, int tiles_m, int tiles_n, in
     return t;
 }
 
-// The BF16 instance for a problem (forced: 0 = by shape, else 1..3) and, for
-// instance 3, the number of K splits. Pure host arithmetic.
-int choose_bf16_instance(int M, int N, int K, int cus, int forced, int *splits)
+// What a BF16 product runs: the instance (1 = 256 x 256, 2 = 64 x 64, 3 =
+// 128 x 128 tiles with split K), the K splits of instance 3 and the workspace
+// bytes its FP32 partials need (0 with one split).
+struct Bf16Plan {
+    int instance;
+    int splits;
+    size_t workspace_bytes;
+};
+
+// The plan for a problem (forced: 0 = by shape, else 1..3). Without a
+// workspace (the entry points that take none) K is never split. Pure host
+// arithmetic.
+Bf16Plan plan_bf16(int M, int N, int K, int cus, int forced, bool with_workspace)
 {
-    int tmn = 0, tnn = 0, per = 0;
-    splitk_plan(M, N, K, cus, &tmn, &tnn, splits, &per);
+    namespace sk = gemm355::bf16_splitk;
+    int tmn = 0, tnn = 0, per = 0, splits = 1;
+    splitk_plan(M, N, K, cus, with_workspace ? sk::MAX_SPLITS : 1, &tmn, &tnn, &splits, &per);
     int instance = forced;
     if (instance == 0) {
         instance = 1;
         if (2 * ceil_div(M, BM) * ceil_div(N, BN) < cus)
-            instance = estimate_small(M, N, K, cus) <= estimate_split(M, N, K, cus, tmn, tnn, *splits, per) ? 2 : 3;
+            instance = estimate_small(M, N, K, cus) <= estimate_split(M, N, K, cus, tmn, tnn, splits, per) ? 2 : 3;
     }
     if (instance == 1 && K <= 3 * gemm355::bf16::BK)
         instance = 2;   // the 256 x 256 kernel runs its tiles back to back and needs K > 192
     if (instance != 3)
-        *splits = 1;
-    return instance;
+        splits = 1;
+    const size_t ws = splits > 1 ? size_t(tmn) * size_t(tnn) * size_t(splits) * sk::TILE_FLOATS * sizeof(float) : 0;
+    return {instance, splits, ws};
 }
 
-// Split-K instance: partial tiles into a stream-ordered workspace, then the
+// Split-K instance: partial tiles into the caller's workspace, then the
 // reduction into C, both on `stream`; with one split the tiles go straight to
 // C and neither the workspace nor the reduction is used.
 template <int EPI>
-int launch_splitk(const Problem &p, void *stream)
+int launch_splitk(const Problem &p, const Bf16Plan &plan, void *workspace, void *stream)
 {
     namespace sk = gemm355::bf16_splitk;
     int cus = 0;
-    int rc = compute_units(&cus);
+    const int rc = compute_units(&cus);
     if (rc != GEMM355_OK)
         return rc;
     sk::SplitProblem sp = {};
@@ -248,45 +215,41 @@ int launch_splitk(const Problem &p, void *stream)
     sp.M = p.M;
     sp.N = p.N;
     sp.K = p.K;
-    splitk_plan(p.M, p.N, p.K, cus, &sp.tiles_m, &sp.tiles_n, &sp.splits, &sp.steps_per_split);
+    splitk_plan(p.M, p.N, p.K, cus, plan.splits, &sp.tiles_m, &sp.tiles_n, &sp.splits, &sp.steps_per_split);
     const int64_t items = int64_t(sp.tiles_m) * sp.tiles_n * sp.splits;
     if (items > (int64_t(1) << 30))
         return GEMM355_ERR_UNSUPPORTED;
+    if (sp.splits > 1)
+        sp.ws = static_cast<float *>(workspace);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (sp.splits > 1) {
-        void *ws = nullptr;
-        rc = stream_workspace(s, size_t(items) * sk::TILE_FLOATS * sizeof(float), &ws);
-        if (rc != GEMM355_OK)
-            return rc;
-        sp.ws = static_cast<float *>(ws);
-    }
-    (void)hipGetLastError(); // clear a stale error so the check below is ours
-    hipLaunchKernelGGL(sk::gemm_bf16_nt_splitk_kernel<EPI>, dim3((unsigned)items), dim3(gemm355::THREADS), 0, s, sp);
-    if (sp.splits > 1) {   // one split stores C itself
+    int st = launch_kernel(sk::gemm_bf16_nt_splitk_kernel<EPI>, (unsigned)items, (unsigned)gemm355::THREADS, sp, s);
+    if (st == GEMM355_OK && sp.splits > 1) {   // one split stores C itself
         const int64_t outs = int64_t(p.M) * (p.N / 8);
-        hipLaunchKernelGGL(sk::splitk_reduce_kernel<EPI>, dim3((unsigned)ceil_div(outs, sk::REDUCE_THREADS)),
-                           dim3(sk::REDUCE_THREADS), 0, s, sp);
+        st = launch_kernel(sk::splitk_reduce_kernel<EPI>, (unsigned)ceil_div(outs, sk::REDUCE_THREADS),
+                           (unsigned)sk::REDUCE_THREADS, sp, s);
     }
-    return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
+    return st;
 }
 
-// The chosen instance's kernels with epilogue EPI.
+// The planned instance's kernels with epilogue EPI.
 template <int EPI>
-int launch_instance(int instance, const Problem &p, void *stream)
+int launch_instance(const Bf16Plan &plan, const Problem &p, void *workspace, void *stream)
 {
-    if (instance == 3)
-        return launch_splitk<EPI>(p, stream);
-    if (instance == 2)
+    if (plan.instance == 3)
+        return launch_splitk<EPI>(p, plan, workspace, stream);
+    if (plan.instance == 2)
         return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel<EPI>, p, stream, gemm355::bf16_small::TM,
                       gemm355::bf16_small::TN);
     return launch(gemm355::bf16::gemm_bf16_nt_kernel<EPI>, p, stream);
 }
 
-// Shared by gemm_bf16_nt and gemm_bf16_nt_bias_act: validation, instance
-// choice, launch. FUSED selects the kernels with the fused epilogue.
-template <bool FUSED>
+// Shared by the BF16 entry points: validation, plan, launch. FUSED selects
+// the kernels with the fused epilogue; WS the entry points that take a
+// workspace (K may then be split; NULL with workspace_bytes 0 is allowed and
+// rules splitting out only if the plan needs none).
+template <bool FUSED, bool WS>
 int bf16_product(int M, int N, int K, const void *A, const void *B, const void *bias, int act, void *C,
-                 void *stream)
+                 void *workspace, size_t workspace_bytes, void *stream)
 {
     if (M < 0 || N < 0 || K < 0)
         return GEMM355_ERR_INVALID_ARG;
@@ -301,7 +264,14 @@ int bf16_product(int M, int N, int K, const void *A, const void *B, const void *
         return GEMM355_ERR_INVALID_ARG;
     if (FUSED && overlaps(C, c_bytes, bias, size_t(N) * 2))
         return GEMM355_ERR_INVALID_ARG;
-    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(bias, 16))
+    if (WS && workspace_bytes > 0 && !workspace)
+        return GEMM355_ERR_INVALID_ARG;
+    if (WS && (overlaps(workspace, workspace_bytes, C, c_bytes) ||
+               (K > 0 && (overlaps(workspace, workspace_bytes, A, size_t(M) * K * 2) ||
+                          overlaps(workspace, workspace_bytes, B, size_t(N) * K * 2))) ||
+               (FUSED && overlaps(workspace, workspace_bytes, bias, size_t(N) * 2))))
+        return GEMM355_ERR_INVALID_ARG;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(bias, 16) || !aligned(workspace, 16))
         return GEMM355_ERR_UNSUPPORTED;
     if (K % 8 != 0 || N % 8 != 0)
         return GEMM355_ERR_UNSUPPORTED;
@@ -320,35 +290,71 @@ int bf16_product(int M, int N, int K, const void *A, const void *B, const void *
     const int rc = compute_units(&cus);
     if (rc != GEMM355_OK)
         return rc;
-    int splits = 0;
-    const int instance = choose_bf16_instance(M, N, K, cus, g_bf16_instance.load(std::memory_order_relaxed), &splits);
+    const Bf16Plan plan = plan_bf16(M, N, K, cus, g_bf16_instance.load(std::memory_order_relaxed), WS);
+    if (plan.workspace_bytes > workspace_bytes)
+        return GEMM355_ERR_UNSUPPORTED;   // the caller's workspace is smaller than the plan needs
     if (!FUSED)
-        return launch_instance<gemm355::EPI_PLAIN>(instance, p, stream);
+        return launch_instance<gemm355::EPI_PLAIN>(plan, p, workspace, stream);
     if (act == GEMM355_ACT_RELU)
-        return launch_instance<gemm355::ACT_RELU>(instance, p, stream);
+        return launch_instance<gemm355::ACT_RELU>(plan, p, workspace, stream);
     if (act == GEMM355_ACT_GELU_TANH)
-        return launch_instance<gemm355::ACT_GELU_TANH>(instance, p, stream);
-    return launch_instance<gemm355::ACT_NONE>(instance, p, stream);
+        return launch_instance<gemm355::ACT_GELU_TANH>(plan, p, workspace, stream);
+    return launch_instance<gemm355::ACT_NONE>(plan, p, workspace, stream);
 }
 
 } // namespace
 
 extern "C" int gemm_bf16_nt(int M, int N, int K, const void *A, const void *B, void *C, void *stream)
 {
-    return bf16_product<false>(M, N, K, A, B, nullptr, GEMM355_ACT_NONE, C, stream);
+    return bf16_product<false, false>(M, N, K, A, B, nullptr, GEMM355_ACT_NONE, C, nullptr, 0, stream);
 }
 
 extern "C" int gemm_bf16_nt_bias_act(int M, int N, int K, const void *A, const void *B, const void *bias,
                                      int activation, void *C, void *stream)
 {
-    return bf16_product<true>(M, N, K, A, B, bias, activation, C, stream);
+    return bf16_product<true, false>(M, N, K, A, B, bias, activation, C, nullptr, 0, stream);
 }
 
-extern "C" int gemm355_bf16_plan(int M, int N, int K, int compute_units, int *instance, int *splits)
+extern "C" int gemm_bf16_nt_ws(int M, int N, int K, const void *A, const void *B, void *C, void *workspace,
+                               size_t workspace_bytes, void *stream)
 {
-    if (M <= 0 || N <= 0 || K < 0 || compute_units <= 0 || !instance || !splits)
+    return bf16_product<false, true>(M, N, K, A, B, nullptr, GEMM355_ACT_NONE, C, workspace, workspace_bytes,
+                                     stream);
+}
+
+extern "C" int gemm_bf16_nt_bias_act_ws(int M, int N, int K, const void *A, const void *B, const void *bias,
+                                        int activation, void *C, void *workspace, size_t workspace_bytes,
+                                        void *stream)
+{
+    return bf16_product<true, true>(M, N, K, A, B, bias, activation, C, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gemm_bf16_nt_workspace_size(int M, int N, int K, size_t *bytes)
+{
+    if (M < 0 || N < 0 || K < 0 || !bytes)
         return GEMM355_ERR_INVALID_ARG;
-    *instance = choose_bf16_instance(M, N, K, compute_units, g_bf16_instance.load(std::memory_order_relaxed), splits);
+    if (M == 0 || N == 0) {
+        *bytes = 0;
+        return GEMM355_OK;
+    }
+    int cus = 0;
+    const int rc = compute_units(&cus);
+    if (rc != GEMM355_OK)
+        return rc;
+    *bytes = plan_bf16(M, N, K, cus, g_bf16_instance.load(std::memory_order_relaxed), true).workspace_bytes;
+    return GEMM355_OK;
+}
+
+extern "C" int gemm355_bf16_plan(int M, int N, int K, int compute_units, int with_workspace, int *instance,
+                                 int *splits, size_t *workspace_bytes)
+{
+    if (M <= 0 || N <= 0 || K < 0 || compute_units <= 0 || !instance || !splits || !workspace_bytes)
+        return GEMM355_ERR_INVALID_ARG;
+    const Bf16Plan plan =
+        plan_bf16(M, N, K, compute_units, g_bf16_instance.load(std::memory_order_relaxed), with_workspace != 0);
+    *instance = plan.instance;
+    *splits = plan.splits;
+    *workspace_bytes = plan.workspace_bytes;
     return GEMM355_OK;
 }
 

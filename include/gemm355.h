@@ -15,24 +15,31 @@
  *
  * Conventions shared by every entry point
  *  - All array pointers are DEVICE pointers owned by the caller. The library
- *    keeps no per-call state and never synchronises: it enqueues the work on
- *    `stream` and returns. It allocates device memory only for the split-K
- *    workspace of gemm_bf16_nt (see there), stream-ordered. `stream` is a hipStream_t
- *    passed as void*; NULL means the default (null) stream.
+ *    allocates no memory, keeps no per-call state and never synchronises: it
+ *    enqueues the work on `stream` and returns. The only scratch memory, the
+ *    FP32 partials of a split K, is a workspace the caller passes to the
+ *    *_ws entry points. `stream` is a hipStream_t passed as void*; NULL means
+ *    the default (null) stream.
  *  - Arrays are dense, row-major, with no padding between rows (the leading
  *    dimension of A and B is K, that of C is N). C must not overlap any input.
  *  - Only the M x N elements of C are written.
  *  - Results for inputs holding NaN or infinity are unspecified.
  *  - Every argument check happens before the first HIP runtime call, so a
- *    rejected call touches neither the device nor the stream. Faults that
- *    happen during the asynchronous execution surface at the caller's next
- *    synchronisation, as usual for HIP.
+ *    rejected call touches neither the device nor the stream. A launch that
+ *    fails returns GEMM355_ERR_LAUNCH (the status of the launch call itself);
+ *    the library never reads or clears the thread's pending HIP error, so an
+ *    error from the caller's own earlier HIP calls stays for the caller to
+ *    collect. Faults that happen during the asynchronous execution surface at
+ *    the caller's next synchronisation, as usual for HIP.
  *  - Calls are thread-safe: the library holds no mutable state apart from a
  *    per-device cache of the compute-unit count, filled once under a lock,
- *    and the instance override set by gemm355_force_instance.
+ *    and the overrides set by gemm355_force_instance and
+ *    gemm355_force_supergroup. Calls may be captured into HIP graphs.
  */
 #ifndef GEMM355_H
 #define GEMM355_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -66,20 +73,11 @@ typedef enum gemm355_status {
  * padded up to a multiple of 256 rows, spans less than 2^31 bytes.
  * Three kernel instances compute it: 256 x 256 output tiles; or, when the
  * 256 x 256 tiling has fewer tiles than half the compute units, either
- * 64 x 64 tiles or 128 x 128 tiles whose K range may be split over up to 8
- * workgroups (at least 8 steps of 64 each) writing FP32 partial tiles that a
- * second kernel on the same stream adds in split order and rounds once to
- * BF16 (with one split the tiles are stored directly) -- whichever has the
- * shorter estimated time (the busiest compute unit's K steps at a measured
- * cost per step, or the operand and partial traffic at a loaded HBM rate,
- * plus fixed costs); whenever K <= 192, not 256 x 256 tiles.
- * gemm355_bf16_plan reports the choice.
- * The split's partials live in one workspace per (device, stream), which only
- * work enqueued on that stream uses; it comes from a memory pool of the
- * library's own, grows by stream-ordered allocation, and is kept until the
- * process ends (at most 8 x 64 KiB per 128 x 128 output tile). Calls on
- * different streams never share a workspace; a stream handle reused after
- * hipStreamDestroy while work of the old stream is still pending would.
+ * 64 x 64 tiles or 128 x 128 tiles -- whichever has the shorter estimated
+ * time (the busiest compute unit's K steps at a measured cost per step, or
+ * the operand traffic at a loaded HBM rate, plus fixed costs); whenever
+ * K <= 192, not 256 x 256 tiles. This entry point never splits K (that needs
+ * a workspace: gemm_bf16_nt_ws). gemm355_bf16_plan reports the choice.
  * All instances give results within the same bound; they may sum in different
  * orders. Each instance is deterministic: the same call gives the same bits.
  */
@@ -95,9 +93,8 @@ typedef enum gemm355_activation {
 /*
  * gemm_bf16_nt_bias_act -- C = act(A * B^T + bias), BF16 in and out, with the
  * bias and the activation applied in the epilogue while the FP32 sums are
- * still in registers ("NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue
- * Warps": the epilogue is where activations and other element-wise operations
- * would be fused).
+ * still in registers, so C is written once and never re-read ("NVFP4 GEMM on
+ * Blackwell", "Kernel 1", "Epilogue Warps").
  *
  *   C[m][n] = bf16_rne(act(z)),  z = fp32(sum_k A[m][k] * B[n][k]) + bias[n]
  *
@@ -117,15 +114,68 @@ int gemm_bf16_nt_bias_act(int M, int N, int K, const void *A, const void *B, con
                           int activation, void *C, void *stream);
 
 /*
+ * gemm_bf16_nt_workspace_size -- workspace bytes gemm_bf16_nt_ws and
+ * gemm_bf16_nt_bias_act_ws need for M x N x K on the current device.
+ *
+ * A library interface, not a definition of the pages. Writes 0 when the plan
+ * does not split K (then the workspace may be NULL), else the bytes of the
+ * FP32 partial tiles: 64 KiB per 128 x 128 output tile and split, at most
+ * 64 KiB per compute unit (16 MiB on a 256-unit device). Returns
+ * GEMM355_ERR_INVALID_ARG for negative sizes or a NULL `bytes`,
+ * GEMM355_ERR_NO_DEVICE when the device cannot be queried; no other HIP call
+ * is made. The size depends on the shape, the device's compute-unit count and
+ * the gemm355_force_instance setting.
+ */
+int gemm_bf16_nt_workspace_size(int M, int N, int K, size_t *bytes);
+
+/*
+ * gemm_bf16_nt_ws -- gemm_bf16_nt with a caller-owned workspace, which lets
+ * the 128 x 128 instance split K over several workgroups.
+ *
+ * ("Achieve cuBLAS Performance on NVIDIA GB300 for HGEMM", opening paragraph,
+ * for the operation; "NVFP4 GEMM on Blackwell", "Production Kernel", "Swap
+ * AB", for why skinny problems need more workgroups than output tiles.)
+ * The result is as for gemm_bf16_nt. When the 128 x 128 instance is chosen,
+ * its K range may be split over up to 8 workgroups (at least 8 steps of 64
+ * each, enough splits to give every compute unit a work item) that write FP32
+ * partial tiles to `workspace`; a second kernel on the same stream adds each
+ * element's partials in split order and rounds once to BF16, so the result is
+ * deterministic.
+ *   workspace        device memory, 16-byte aligned, owned by the caller; its
+ *                    contents on entry do not matter and on return are
+ *                    unspecified. It must stay untouched until the product
+ *                    has run on `stream`, and two products running at the
+ *                    same time must not share one.
+ *   workspace_bytes  its size; at least gemm_bf16_nt_workspace_size(M, N, K),
+ *                    else GEMM355_ERR_UNSUPPORTED (nothing is enqueued).
+ *                    NULL with 0 bytes is accepted when the plan needs none.
+ * Errors otherwise as for gemm_bf16_nt; a workspace overlapping A, B or C ->
+ * GEMM355_ERR_INVALID_ARG, one not 16-byte aligned -> UNSUPPORTED, NULL with
+ * workspace_bytes > 0 -> INVALID_ARG.
+ */
+int gemm_bf16_nt_ws(int M, int N, int K, const void *A, const void *B, void *C, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * gemm_bf16_nt_bias_act_ws -- gemm_bf16_nt_bias_act with a caller-owned
+ * workspace, as gemm_bf16_nt_ws adds one to gemm_bf16_nt. With several K
+ * splits the reduction kernel adds the bias and applies the activation to the
+ * summed FP32 partials before rounding. A workspace overlapping the bias is
+ * also INVALID_ARG.
+ */
+int gemm_bf16_nt_bias_act_ws(int M, int N, int K, const void *A, const void *B, const void *bias, int activation,
+                             void *C, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gemm355_force_instance -- override the choice of gemm_bf16_nt's instance.
  *
  * A diagnostic for tests and measurements (it is not defined by the pages):
  * instance 0 restores the choice by shape, 1 forces 256 x 256 tiles (except
  * for K <= 192, which always takes the 64 x 64 instance), 2 forces 64 x 64
- * tiles, 3 forces 128 x 128 tiles with split K (as many splits as give every
- * compute unit a work item, at most 8, each at least 8 steps of 64; one
- * split when K is too short for two or the tiles alone fill the units), for
- * every later gemm_bf16_nt call in the process. Returns
+ * tiles, 3 forces 128 x 128 tiles (through the *_ws entry points with split K:
+ * as many splits as give every compute unit a work item, at most 8, each at
+ * least 8 steps of 64; one split when K is too short for two or the tiles
+ * alone fill the units), for every later BF16 product in the process. Returns
  * GEMM355_OK, or GEMM355_ERR_INVALID_ARG for any other value (the setting is
  * then unchanged). Calls racing with gemm_bf16_nt on other threads see either
  * the old or the new setting. No HIP call is made.
@@ -148,18 +198,21 @@ int gemm355_force_instance(int instance);
 int gemm355_force_supergroup(int supergroup);
 
 /*
- * gemm355_bf16_plan -- the instance gemm_bf16_nt would run for M x N x K on
+ * gemm355_bf16_plan -- the instance a BF16 product would run for M x N x K on
  * a device with `compute_units` compute units, under the current
- * gemm355_force_instance setting.
+ * gemm355_force_instance setting: gemm_bf16_nt / gemm_bf16_nt_bias_act when
+ * with_workspace is 0, the *_ws entry points otherwise.
  *
  * A diagnostic for tests and measurements (it is not defined by the pages).
- * Writes the instance (1 = 256 x 256, 2 = 64 x 64, 3 = 128 x 128 with split K)
- * to *instance and the number of K splits (1 unless the instance is 3) to
- * *splits. Returns GEMM355_OK, or GEMM355_ERR_INVALID_ARG for M <= 0,
- * N <= 0, K < 0, compute_units <= 0 or a NULL output pointer (outputs then
- * unchanged). Pure host arithmetic: no HIP call is made.
+ * Writes the instance (1 = 256 x 256, 2 = 64 x 64, 3 = 128 x 128) to
+ * *instance, the number of K splits (1 unless the instance is 3 and a
+ * workspace is allowed) to *splits and the workspace bytes the plan needs to
+ * *workspace_bytes. Returns GEMM355_OK, or GEMM355_ERR_INVALID_ARG for
+ * M <= 0, N <= 0, K < 0, compute_units <= 0 or a NULL output pointer
+ * (outputs then unchanged). Pure host arithmetic: no HIP call is made.
  */
-int gemm355_bf16_plan(int M, int N, int K, int compute_units, int *instance, int *splits);
+int gemm355_bf16_plan(int M, int N, int K, int compute_units, int with_workspace, int *instance, int *splits,
+                      size_t *workspace_bytes);
 
 /*
  * gemm_nvfp4_nt -- block-scaled FP4 operands, BF16 output.

@@ -263,9 +263,9 @@ int oracle_gemm_nvfp4_nt_at(int M, int N, int K, const uint8_t *Aq, const uint8_
 }
 
 /* ---- fused epilogue -----------------------------------------------------
- * An element-wise step applied to the sum before the output rounding ("NVFP4
- * GEMM on Blackwell", "Kernel 1", "Epilogue Warps": the epilogue is where
- * activation functions and other element-wise operations would be fused).
+ * A bias and an activation applied to each sum before the output rounding
+ * ("NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue Warps", which places
+ * such per-element work in the epilogue).
  * The pages name no particular operation; the one computed here is the common
  * linear-layer epilogue, all in binary64:
  *

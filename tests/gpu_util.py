@@ -42,6 +42,23 @@ class GuardedC:
         return bool(np.all(host[:GUARD] == CANARY) and np.all(host[GUARD + self.M * self.N:] == CANARY))
 
 
+def workspace_for(M: int, N: int, K: int):
+    """A device workspace for gemm_bf16_nt_ws at this shape (None when the
+    plan needs none), with a canary tail that the product must not touch."""
+    import dense_gemm_14_amd as g
+    nbytes = g.workspace_size(M, N, K)
+    if nbytes == 0:
+        return None, 0
+    buf = torch.full((nbytes // 2 + GUARD,), CANARY, dtype=torch.int16, device="cuda")
+    return buf, nbytes
+
+
+def workspace_tail_intact(buf, nbytes) -> bool:
+    if buf is None:
+        return True
+    return bool(np.all(buf[nbytes // 2:].cpu().numpy().view(np.uint16) == CANARY))
+
+
 def sample_positions(M: int, N: int, count: int, seed: int, tile: int = 256):
     """Random (m, n) plus every combination of tile-boundary rows and columns."""
     g = np.random.Generator(np.random.PCG64(seed))

@@ -19,7 +19,8 @@ def test_library_exports_every_declared_function():
     lib = g.load()
     names = g.declared_functions()
     assert set(names) >= {"gemm_bf16_nt", "gemm_bf16_nt_bias_act", "gemm_nvfp4_nt", "gemm_nvfp4_nt_bias_act",
-                          "gemm_mxfp4_nt", "gemm355_status_string",
+                          "gemm_mxfp4_nt", "gemm355_status_string", "gemm_bf16_nt_ws", "gemm_bf16_nt_bias_act_ws",
+                          "gemm_bf16_nt_workspace_size",
                           "gemm355_tile_order", "gemm355_schedule"}
     for n in names:
         assert hasattr(lib, n), n
@@ -226,37 +227,97 @@ def test_bf16_plan_for_the_workload_shapes():
     # tiles of 64 x 64, where that instance beats splitting K (measured).
     g.force_instance(g.INSTANCE_AUTO)
     g.force_supergroup(0)
-    assert g.bf16_plan(8192, 8192, 8192, 256) == (g.INSTANCE_LARGE, 1)
-    assert g.bf16_plan(8000, 8000, 8000, 256) == (g.INSTANCE_LARGE, 1)
-    assert g.bf16_plan(4096, 4096, 4096, 256) == (g.INSTANCE_LARGE, 1)
-    assert g.bf16_plan(256, 256, 256, 256) == (g.INSTANCE_SMALL, 1)
-    assert g.bf16_plan(128, 8192, 8192, 256) == (g.INSTANCE_SMALL, 1)
-    # fewer 64 x 64 tiles than compute units, or two rounds of them: split K
-    assert g.bf16_plan(64, 4096, 8192, 256) == (g.INSTANCE_SPLITK, 8)
-    assert g.bf16_plan(512, 4096, 8192, 256) == (g.INSTANCE_SPLITK, 2)
-    # short K: nothing to split
-    assert g.bf16_plan(128, 8192, 2048, 256) == (g.INSTANCE_SMALL, 1)
-    # mid shapes with a quarter of the units' worth of 256 x 256 tiles: one
-    # round of 128 x 128 tiles, stored directly (measured 27 us against 42 us
-    # for 64 x 64 tiles and 46 us for 256 x 256 ones at 2048^3)
-    assert g.bf16_plan(2048, 2048, 2048, 256) == (g.INSTANCE_SPLITK, 1)
-    assert g.bf16_plan(1024, 4096, 8192, 256) == (g.INSTANCE_SPLITK, 1)
-    # small square problems: 64 x 64 tiles at short K, split K at long K
-    assert g.bf16_plan(1024, 1024, 1024, 256) == (g.INSTANCE_SMALL, 1)
-    assert g.bf16_plan(1024, 1024, 16384, 256) == (g.INSTANCE_SPLITK, 4)
-    # half the units' worth of 256 x 256 tiles or more: that instance
-    assert g.bf16_plan(1024, 8192, 1024, 256) == (g.INSTANCE_LARGE, 1)
-    assert g.bf16_plan(3072, 3072, 3072, 256) == (g.INSTANCE_LARGE, 1)
-    # K too short for the 256 x 256 instance's four kinds of step
-    assert g.bf16_plan(4096, 4096, 192, 256) == (g.INSTANCE_SMALL, 1)
-    assert g.bf16_plan(4096, 4096, 200, 256)[0] == g.INSTANCE_LARGE
+    for ws in (False, True):
+        assert g.bf16_plan(8192, 8192, 8192, 256, ws) == (g.INSTANCE_LARGE, 1)
+        assert g.bf16_plan(8000, 8000, 8000, 256, ws) == (g.INSTANCE_LARGE, 1)
+        assert g.bf16_plan(4096, 4096, 4096, 256, ws) == (g.INSTANCE_LARGE, 1)
+        assert g.bf16_plan(256, 256, 256, 256, ws) == (g.INSTANCE_SMALL, 1)
+        assert g.bf16_plan(128, 8192, 8192, 256, ws) == (g.INSTANCE_SMALL, 1)
+        # short K: nothing to split
+        assert g.bf16_plan(128, 8192, 2048, 256, ws) == (g.INSTANCE_SMALL, 1)
+        # mid shapes with a quarter of the units' worth of 256 x 256 tiles: one
+        # round of 128 x 128 tiles, stored directly (measured 27 us against 42 us
+        # for 64 x 64 tiles and 46 us for 256 x 256 ones at 2048^3)
+        assert g.bf16_plan(2048, 2048, 2048, 256, ws) == (g.INSTANCE_SPLITK, 1)
+        assert g.bf16_plan(1024, 4096, 8192, 256, ws) == (g.INSTANCE_SPLITK, 1)
+        assert g.bf16_plan(1024, 1024, 1024, 256, ws) == (g.INSTANCE_SMALL, 1)
+        # half the units' worth of 256 x 256 tiles or more: that instance
+        assert g.bf16_plan(1024, 8192, 1024, 256, ws) == (g.INSTANCE_LARGE, 1)
+        assert g.bf16_plan(3072, 3072, 3072, 256, ws) == (g.INSTANCE_LARGE, 1)
+        # K too short for the 256 x 256 instance's four kinds of step
+        assert g.bf16_plan(4096, 4096, 192, 256, ws) == (g.INSTANCE_SMALL, 1)
+        assert g.bf16_plan(4096, 4096, 200, 256, ws)[0] == g.INSTANCE_LARGE
+    # fewer 64 x 64 tiles than compute units, or two rounds of them: split K,
+    # when a workspace is given; without one, the 64 x 64 instance
+    assert g.bf16_plan(64, 4096, 8192, 256, True) == (g.INSTANCE_SPLITK, 8)
+    assert g.bf16_plan(512, 4096, 8192, 256, True) == (g.INSTANCE_SPLITK, 2)
+    assert g.bf16_plan(1024, 1024, 16384, 256, True) == (g.INSTANCE_SPLITK, 4)
+    for shape in [(64, 4096, 8192), (512, 4096, 8192), (1024, 1024, 16384)]:
+        assert g.bf16_plan(*shape, 256) == (g.INSTANCE_SMALL, 1)
     # splitting never makes a split shorter than 8 steps of 64, or empty
     for M, N, K in [(128, 1032, 4104), (64, 64, 4104), (512, 4096, 8192), (128, 2048, 520), (2048, 2048, 2048)]:
-        inst, splits = g.bf16_plan(M, N, K, 256)
+        inst, splits = g.bf16_plan(M, N, K, 256, True)
         if inst == g.INSTANCE_SPLITK and splits > 1:
             steps = -(-K // 64)
             per = -(-steps // splits)
             assert splits <= 8 and per >= 8 and (splits - 1) * per < steps, (M, N, K, splits)
+
+
+def test_bf16_plan_workspace_bytes():
+    # 64 KiB of FP32 partials per 128 x 128 tile and split; none without a split
+    g.force_instance(g.INSTANCE_AUTO)
+    assert g.bf16_plan_workspace_bytes(8192, 8192, 8192, 256) == 0
+    assert g.bf16_plan_workspace_bytes(128, 8192, 8192, 256) == 0
+    assert g.bf16_plan_workspace_bytes(64, 4096, 8192, 256) == 32 * 8 * 65536
+    assert g.bf16_plan_workspace_bytes(136, 1032, 4104, 256) == 2 * 9 * 8 * 65536
+    # splits are chosen so that work items do not outnumber the units: the
+    # workspace never exceeds 64 KiB per compute unit, even when forced
+    rng = np.random.Generator(np.random.PCG64(5))
+    try:
+        for forced in (g.INSTANCE_AUTO, g.INSTANCE_SPLITK):
+            g.force_instance(forced)
+            for _ in range(300):
+                M, N = (int(x) for x in rng.integers(1, 4096, 2))
+                K = int(rng.integers(0, 32768))
+                cus = int(rng.choice([80, 104, 256, 304]))
+                inst, splits = g.bf16_plan(M, N, K, cus, True)
+                nb = g.bf16_plan_workspace_bytes(M, N, K, cus)
+                tiles = -(-M // 128) * -(-N // 128)
+                assert nb == (tiles * splits * 65536 if splits > 1 else 0), (M, N, K, cus)
+                assert nb <= cus * 65536, (M, N, K, cus)
+                assert g.bf16_plan(M, N, K, cus)[1] == 1
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+
+
+def _ws(M, N, K, w, nbytes, a=FAKE, b=FAKE + 0x100000, c=FAKE + 0x200000):
+    return g.load().gemm_bf16_nt_ws(M, N, K, a, b, c, w, nbytes, None)
+
+
+def test_workspace_rejections_happen_before_any_device_call():
+    lib = g.load()
+    assert _ws(-1, 8, 64, None, 0) == g.ERR_INVALID_ARG
+    assert _ws(0, 8, 64, None, 0) == g.OK                             # empty: nothing to do
+    assert _ws(8, 8, 64, None, 4096) == g.ERR_INVALID_ARG             # NULL with bytes
+    assert _ws(8, 8, 64, FAKE + 0x300008, 4096) == g.ERR_UNSUPPORTED  # not 16-byte aligned
+    assert _ws(8, 8, 64, FAKE + 0x200000, 4096) == g.ERR_INVALID_ARG  # overlaps C
+    assert _ws(8, 8, 64, FAKE, 4096) == g.ERR_INVALID_ARG             # overlaps A
+    assert _ws(8, 8, 64, FAKE + 0x100010, 4096) == g.ERR_INVALID_ARG  # overlaps B
+    assert lib.gemm_bf16_nt_bias_act_ws(8, 8, 64, FAKE, FAKE + 0x100000, FAKE + 0x300000, 2, FAKE + 0x200000,
+                                        FAKE + 0x300000, 4096, None) == g.ERR_INVALID_ARG   # overlaps the bias
+    assert lib.gemm_bf16_nt_bias_act_ws(8, 8, 64, FAKE, FAKE + 0x100000, None, 7, FAKE + 0x200000,
+                                        None, 0, None) == g.ERR_INVALID_ARG                 # unknown activation
+    out = ctypes.c_size_t(99)
+    assert lib.gemm_bf16_nt_workspace_size(-1, 8, 8, ctypes.byref(out)) == g.ERR_INVALID_ARG
+    assert lib.gemm_bf16_nt_workspace_size(8, 8, 8, None) == g.ERR_INVALID_ARG
+    assert lib.gemm_bf16_nt_workspace_size(0, 8, 8, ctypes.byref(out)) == g.OK and out.value == 0
+
+
+def test_no_allocation_reachable_from_the_library():
+    # the library allocates nothing: no allocation call appears in its host source
+    src = open(os.path.join(os.path.dirname(g.__file__), "csrc", "gemm355.hip")).read()
+    for call in ("hipMalloc", "hipFree", "hipMemPool", "hipHostMalloc", "hipExtMalloc", "malloc(", "new "):
+        assert call not in src, call
 
 
 def test_bf16_plan_follows_the_forced_instance_and_checks_arguments():
@@ -265,13 +326,18 @@ def test_bf16_plan_follows_the_forced_instance_and_checks_arguments():
         g.force_instance(g.INSTANCE_SMALL)
         assert g.bf16_plan(8192, 8192, 8192, 256) == (g.INSTANCE_SMALL, 1)
         g.force_instance(g.INSTANCE_SPLITK)
-        inst, splits = g.bf16_plan(8192, 8192, 8192, 256)
+        inst, splits = g.bf16_plan(8192, 8192, 8192, 256, True)
         assert inst == g.INSTANCE_SPLITK and splits >= 1
+        assert g.bf16_plan(128, 1032, 4104, 256) == (g.INSTANCE_SPLITK, 1)
         g.force_instance(g.INSTANCE_LARGE)
         assert g.bf16_plan(8192, 8192, 128, 256) == (g.INSTANCE_SMALL, 1)
     finally:
         g.force_instance(g.INSTANCE_AUTO)
     out = (ctypes.c_int * 2)()
+    nb = ctypes.c_size_t(0)
     for bad in [(0, 8, 8, 256), (8, -1, 8, 256), (8, 8, -8, 256), (8, 8, 8, 0)]:
-        assert lib.gemm355_bf16_plan(*bad, ctypes.byref(out, 0), ctypes.byref(out, 4)) == g.ERR_INVALID_ARG
-    assert lib.gemm355_bf16_plan(8, 8, 8, 256, None, ctypes.byref(out, 4)) == g.ERR_INVALID_ARG
+        assert lib.gemm355_bf16_plan(*bad, 1, ctypes.byref(out, 0), ctypes.byref(out, 4),
+                                     ctypes.byref(nb)) == g.ERR_INVALID_ARG
+    assert lib.gemm355_bf16_plan(8, 8, 8, 256, 0, None, ctypes.byref(out, 4), ctypes.byref(nb)) == g.ERR_INVALID_ARG
+    assert lib.gemm355_bf16_plan(8, 8, 8, 256, 0, ctypes.byref(out, 0), ctypes.byref(out, 4),
+                                 None) == g.ERR_INVALID_ARG

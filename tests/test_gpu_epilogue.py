@@ -1,12 +1,13 @@
 """gemm_bf16_nt_bias_act and gemm_nvfp4_nt_bias_act (bias and activation
 fused into the epilogue) against the oracle, through the C ABI: every BF16
-instance forced in turn, each activation, ragged shapes element by element,
-split K with several splits (the reduction applies the epilogue), exactly
+instance forced in turn (the 128 x 128 one both without a workspace and with
+one, through gemm_bf16_nt_bias_act_ws), each activation, ragged shapes element
+by element, split K with several splits (the reduction applies the epilogue), exactly
 summable inputs bitwise for the identity and ReLU, K = 0 (the activation of
 the bias), no bias, and the 8192^3 workloads on sampled elements.
 
-Reference: "NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue Warps" (the
-epilogue is where activations and element-wise operations would be fused).
+Reference: "NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue Warps" (per-element
+work on the sums belongs in the epilogue).
 """
 import numpy as np
 import pytest
@@ -16,28 +17,39 @@ import dense_gemm_14_amd as g
 import oracle
 import synthetic as syn
 from tests import tolerance
-from tests.gpu_util import GuardedC, need_gpu, sample_positions, to_dev
+from tests.gpu_util import (GuardedC, need_gpu, sample_positions, to_dev, workspace_for,
+                            workspace_tail_intact)
 
 pytestmark = pytest.mark.gpu
 
-INSTANCES = [g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_SPLITK]
+# (instance, through gemm_bf16_nt_bias_act_ws with a workspace)
+INSTANCES = [(g.INSTANCE_LARGE, False), (g.INSTANCE_SMALL, False), (g.INSTANCE_SPLITK, False),
+             (g.INSTANCE_SPLITK, True)]
+IDS = ["large", "small", "splitk_1", "splitk_ws"]
 ACTS = [g.ACT_NONE, g.ACT_RELU, g.ACT_GELU_TANH]
 
 
 @pytest.fixture
 def forced(request):
     need_gpu()
-    g.force_instance(request.param)
+    g.force_instance(request.param[0])
     yield request.param
     g.force_instance(g.INSTANCE_AUTO)
 
 
-def run_fused(A, B, bias, act, M, N, K):
+def run_fused(A, B, bias, act, M, N, K, ws=False):
     C = GuardedC(M, N)
-    g.gemm_bf16_nt_bias_act(M, N, K, to_dev(A) if A is not None else None, to_dev(B) if B is not None else None,
-                            to_dev(bias) if bias is not None else None, act, C.view)
+    ops = (to_dev(A) if A is not None else None, to_dev(B) if B is not None else None,
+           to_dev(bias) if bias is not None else None)
+    if ws:
+        buf, nbytes = workspace_for(M, N, K)
+        g.gemm_bf16_nt_bias_act_ws(M, N, K, *ops, act, C.view, buf, nbytes)
+    else:
+        g.gemm_bf16_nt_bias_act(M, N, K, *ops, act, C.view)
     torch.cuda.synchronize()
     assert C.guards_intact(), "write outside C"
+    if ws:
+        assert workspace_tail_intact(buf, nbytes), "write past the workspace"
     return C.bits()
 
 
@@ -47,7 +59,7 @@ def reference(A, B, bias, act, M, N):
     return ref.reshape(M, N), z.reshape(M, N)
 
 
-@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True, ids=IDS)
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("M,N,K", [(300, 264, 520), (65, 72, 64), (257, 520, 1032)])
 def test_fused_matches_oracle(forced, act, M, N, K):
@@ -55,7 +67,7 @@ def test_fused_matches_oracle(forced, act, M, N, K):
     A = syn.bf16_uniform(M, K, seed=M + 3 * K + act)
     B = syn.bf16_uniform(N, K, seed=N + 3 * K + 1)
     bias = syn.bf16_uniform(1, N, seed=N + 17, lo=-2.0, hi=2.0)[0]
-    got = run_fused(A, B, bias, act, M, N, K)
+    got = run_fused(A, B, bias, act, M, N, K, forced[1])
     ref, z = reference(A, B, bias, act, M, N)
     res = tolerance.check_fused(got, ref, z, K, act)
     assert res, res
@@ -68,18 +80,18 @@ def test_fused_split_reduction(act):
     need_gpu()
     M, N, K = 136, 1032, 4104
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    inst, splits = g.bf16_plan(M, N, K, cus)
+    inst, splits = g.bf16_plan(M, N, K, cus, with_workspace=True)
     assert inst == g.INSTANCE_SPLITK and splits > 1
     A = syn.bf16_uniform(M, K, seed=51)
     B = syn.bf16_uniform(N, K, seed=52)
     bias = syn.bf16_uniform(1, N, seed=53, lo=-8.0, hi=8.0)[0]
-    got = run_fused(A, B, bias, act, M, N, K)
+    got = run_fused(A, B, bias, act, M, N, K, ws=True)
     ref, z = reference(A, B, bias, act, M, N)
     res = tolerance.check_fused(got, ref, z, K, act)
     assert res, res
 
 
-@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True, ids=IDS)
 @pytest.mark.parametrize("act", [g.ACT_NONE, g.ACT_RELU])
 def test_fused_exact_inputs_bitwise(forced, act):
     # multiples of 1/16 with K = 264: every partial sum, and the bias added to
@@ -88,15 +100,16 @@ def test_fused_exact_inputs_bitwise(forced, act):
     A = syn.bf16_sixteenths(M, K, seed=61)
     B = syn.bf16_sixteenths(N, K, seed=62)
     bias = syn.bf16_sixteenths(1, N, seed=63, jmax=64)[0]
-    assert np.array_equal(run_fused(A, B, bias, act, M, N, K), oracle.gemm_bf16_nt_bias_act(A, B, bias, act))
+    assert np.array_equal(run_fused(A, B, bias, act, M, N, K, forced[1]),
+                          oracle.gemm_bf16_nt_bias_act(A, B, bias, act))
 
 
-@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True, ids=IDS)
 @pytest.mark.parametrize("act", ACTS)
 def test_fused_empty_sum_is_activation_of_bias(forced, act):
     M, N = 70, 72
     bias = syn.bf16_uniform(1, N, seed=71, lo=-4.0, hi=4.0)[0]
-    got = run_fused(None, None, bias, act, M, N, 0)
+    got = run_fused(None, None, bias, act, M, N, 0, forced[1])
     ref = oracle.gemm_bf16_nt_bias_act(np.zeros((M, 0), np.uint16), np.zeros((N, 0), np.uint16), bias, act)
     z = np.broadcast_to(tolerance.bf16_bits_to_f64(bias), (M, N))
     res = tolerance.check_fused(got, ref, z, 0, act)

@@ -1,10 +1,11 @@
 """The three BF16 kernel instances (256 x 256 output tiles, 64 x 64 tiles, and
-128 x 128 tiles with split K and a reduction of FP32 partials, or a direct
-store when there is one split), each forced
-through gemm355_force_instance, against the oracle: ragged shapes element by
-element, exactly summable inputs bitwise, K = 0, and B = I bitwise. The
-automatic choice routes small and skinny problems away from the 256 x 256
-instance, so without forcing it would only see the large workload shapes."""
+128 x 128 tiles -- through gemm_bf16_nt with one split storing C directly,
+through gemm_bf16_nt_ws with K split over workgroups, FP32 partials in the
+caller's workspace and a reduction), each forced through
+gemm355_force_instance, against the oracle: ragged shapes element by element,
+exactly summable inputs bitwise, K = 0, and B = I bitwise. The automatic
+choice routes small and skinny problems away from the 256 x 256 instance, so
+without forcing it would only see the large workload shapes."""
 import numpy as np
 import pytest
 import torch
@@ -13,28 +14,38 @@ import dense_gemm_14_amd as g
 import oracle
 import synthetic as syn
 from tests import tolerance
-from tests.gpu_util import GuardedC, need_gpu, sample_positions, to_dev
+from tests.gpu_util import (GuardedC, need_gpu, sample_positions, to_dev, workspace_for,
+                            workspace_tail_intact)
 
 pytestmark = pytest.mark.gpu
 
-INSTANCES = [g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_SPLITK]
+# (instance, through gemm_bf16_nt_ws with a workspace)
+INSTANCES = [(g.INSTANCE_LARGE, False), (g.INSTANCE_SMALL, False), (g.INSTANCE_SPLITK, False),
+             (g.INSTANCE_SPLITK, True)]
+IDS = ["large", "small", "splitk_1", "splitk_ws"]
 
 
 @pytest.fixture
 def forced(request):
     need_gpu()
-    g.force_instance(request.param)
+    g.force_instance(request.param[0])
     yield request.param
     g.force_instance(g.INSTANCE_AUTO)
 
 
-def run_bf16(A_bits, B_bits, M, N, K):
+def run_bf16(A_bits, B_bits, M, N, K, ws=False):
     A = to_dev(A_bits) if A_bits is not None else None
     B = to_dev(B_bits) if B_bits is not None else None
     C = GuardedC(M, N)
-    g.gemm_bf16_nt(M, N, K, A, B, C.view)
+    if ws:
+        buf, nbytes = workspace_for(M, N, K)
+        g.gemm_bf16_nt_ws(M, N, K, A, B, C.view, buf, nbytes)
+    else:
+        g.gemm_bf16_nt(M, N, K, A, B, C.view)
     torch.cuda.synchronize()
     assert C.guards_intact(), "write outside C"
+    if ws:
+        assert workspace_tail_intact(buf, nbytes), "write past the workspace"
     return C.bits()
 
 
@@ -42,35 +53,35 @@ SHAPES = [(1, 8, 8), (63, 72, 40), (65, 64, 136), (257, 264, 520), (300, 8, 1000
           (520, 264, 72)]
 
 
-@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True, ids=IDS)
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_forced_instance_matches_oracle(forced, M, N, K):
     A = syn.bf16_uniform(M, K, seed=5 * M + N + 3 * K)
     B = syn.bf16_uniform(N, K, seed=5 * M + N + 3 * K + 1)
-    C = run_bf16(A, B, M, N, K)
+    C = run_bf16(A, B, M, N, K, forced[1])
     res = tolerance.check(C, oracle.gemm_bf16_nt(A, B), K)
     assert res, res
 
 
-@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True, ids=IDS)
 @pytest.mark.parametrize("M,N,K", [(200, 136, 2056), (64, 64, 64), (513, 520, 264)])
 def test_forced_instance_exact_sums_bitwise(forced, M, N, K):
     A = syn.bf16_sixteenths(M, K, seed=31 + K)
     B = syn.bf16_sixteenths(N, K, seed=32 + K)
-    assert np.array_equal(run_bf16(A, B, M, N, K), oracle.gemm_bf16_nt(A, B))
+    assert np.array_equal(run_bf16(A, B, M, N, K, forced[1]), oracle.gemm_bf16_nt(A, B))
 
 
-@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True, ids=IDS)
 def test_forced_instance_k_zero(forced):
-    assert np.array_equal(run_bf16(None, None, 70, 72, 0), np.zeros((70, 72), np.uint16))
+    assert np.array_equal(run_bf16(None, None, 70, 72, 0, forced[1]), np.zeros((70, 72), np.uint16))
 
 
-@pytest.mark.parametrize("forced", INSTANCES, indirect=True)
+@pytest.mark.parametrize("forced", INSTANCES, indirect=True, ids=IDS)
 def test_forced_instance_identity(forced):
     M, K = 96, 520
     A = syn.bf16_uniform(M, K, seed=77)
     B = syn.bf16_identity(K)
-    assert np.array_equal(run_bf16(A, B, M, K, K), A)
+    assert np.array_equal(run_bf16(A, B, M, K, K, forced[1]), A)
 
 
 def test_instances_agree_within_bound_at_a_medium_shape():
@@ -80,10 +91,10 @@ def test_instances_agree_within_bound_at_a_medium_shape():
     B = syn.bf16_uniform(N, K, seed=92)
     ref = oracle.gemm_bf16_nt(A, B)
     try:
-        for inst in (g.INSTANCE_AUTO, g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_SPLITK):
+        for inst, ws in [(g.INSTANCE_AUTO, False), (g.INSTANCE_AUTO, True)] + INSTANCES:
             g.force_instance(inst)
-            res = tolerance.check(run_bf16(A, B, M, N, K), ref, K)
-            assert res, (inst, res)
+            res = tolerance.check(run_bf16(A, B, M, N, K, ws), ref, K)
+            assert res, (inst, ws, res)
     finally:
         g.force_instance(g.INSTANCE_AUTO)
 
@@ -131,15 +142,18 @@ def test_large_instance_multi_tile_exact_every_element():
 
 
 def test_splitk_many_splits_exact_every_element():
-    # 2 x 9 tiles of 128 x 128 and 65 K steps: the automatic plan splits K
-    # eight ways (the last split has two steps, the last step a K tail). With
-    # multiples of 1/16 every partial sum and the sum of the partials is exact
-    # in FP32, so every element must match the correctly rounded sum.
+    # 2 x 9 tiles of 128 x 128 and 65 K steps: the automatic plan with a
+    # workspace splits K eight ways (the last split has two steps, the last
+    # step a K tail). With multiples of 1/16 every partial sum and the sum of
+    # the partials is exact in FP32, so every element must match the
+    # correctly rounded sum.
     need_gpu()
     M, N, K = 136, 1032, 4104
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert g.bf16_plan(M, N, K, cus, with_workspace=True) == (g.INSTANCE_SPLITK, 8)
     A = syn.bf16_sixteenths(M, K, seed=71)
     B = syn.bf16_sixteenths(N, K, seed=72)
-    C = run_bf16(A, B, M, N, K)
+    C = run_bf16(A, B, M, N, K, ws=True)
     want = oracle.bf16_from_double(tolerance.bf16_bits_to_f64(A) @ tolerance.bf16_bits_to_f64(B).T)
     assert np.array_equal(oracle.gemm_bf16_nt(A[:3], B), want[:3])
     bad = np.argwhere(C != want)
@@ -166,11 +180,14 @@ def test_single_split_direct_store_exact_every_element(M, N, K):
 
 
 def test_splitk_streams_and_determinism():
-    # The partials live in stream-ordered memory: the same product on a side
-    # stream and on the default stream, and twice in a row, is bitwise equal
-    # (splits are added in a fixed order) and within the bound of the oracle.
+    # The same split product on a side stream and on the default stream, each
+    # with its own workspace, and twice in a row: bitwise equal (splits are
+    # added in a fixed order) and within the bound of the oracle; the product
+    # without a workspace (no split) is within the bound too.
     need_gpu()
     M, N, K = 128, 2048, 4096
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert g.bf16_plan(M, N, K, cus, with_workspace=True)[1] > 1
     A = syn.bf16_uniform(M, K, seed=81)
     B = syn.bf16_uniform(N, K, seed=82)
     s = torch.cuda.Stream()
@@ -180,14 +197,34 @@ def test_splitk_streams_and_determinism():
     for stream in (s, None, None):
         if stream is None:
             C = GuardedC(M, N)
-            g.gemm_bf16_nt(M, N, K, dA, dB, C.view)
+            buf, nbytes = workspace_for(M, N, K)
+            g.gemm_bf16_nt_ws(M, N, K, dA, dB, C.view, buf, nbytes)
         else:
             with torch.cuda.stream(stream):
                 C = GuardedC(M, N)
-                g.gemm_bf16_nt(M, N, K, dA, dB, C.view, stream=stream)
+                buf, nbytes = workspace_for(M, N, K)
+                g.gemm_bf16_nt_ws(M, N, K, dA, dB, C.view, buf, nbytes, stream=stream)
         torch.cuda.synchronize()
         assert C.guards_intact(), "write outside C"
         outs.append(C.bits())
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
-    res = tolerance.check(outs[0], oracle.gemm_bf16_nt(A, B), K)
+    ref = oracle.gemm_bf16_nt(A, B)
+    res = tolerance.check(outs[0], ref, K)
     assert res, res
+    res = tolerance.check(run_bf16(A, B, M, N, K), ref, K)
+    assert res, res
+
+
+def test_workspace_too_small_is_rejected_without_launching():
+    need_gpu()
+    M, N, K = 128, 2048, 4096
+    nbytes = g.workspace_size(M, N, K)
+    assert nbytes > 0
+    buf = torch.zeros(nbytes // 2, dtype=torch.int16, device="cuda")
+    C = GuardedC(M, N)
+    with pytest.raises(g.Gemm355Error) as e:
+        g.gemm_bf16_nt_ws(M, N, K, to_dev(syn.bf16_uniform(M, K, 1)), to_dev(syn.bf16_uniform(N, K, 2)), C.view,
+                          buf, nbytes - 16)
+    assert e.value.status == g.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert np.all(C.bits() == 0x7FC1), "C written by a rejected call"

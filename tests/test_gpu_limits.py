@@ -6,7 +6,8 @@ rows past M or N into zeros). These tests sit just inside that limit:
 
   * K at the limit with M = 3, N = 16: the offsets the kernels form for the
     padded rows 3 .. 255 reach 2^31 - 4 KiB and must all fall outside A's
-    range; every BF16 instance forced in turn, the FP4 kernel, and the
+    range; every BF16 instance forced in turn (split K through the workspace
+    entry point), the FP4 kernel, and the
     microscaled FP4 kernel at K = 2^24 - 512;
   * C (and A) at the limit with M = 2^27 - 300, N = K = 8: the store offsets
     reach 2^31 - 8 KiB; sampled rows, including the last tile's, compared
@@ -20,7 +21,7 @@ import dense_gemm_14_amd as g
 import oracle
 import synthetic as syn
 from tests import tolerance
-from tests.gpu_util import GuardedC, need_gpu, to_dev
+from tests.gpu_util import GuardedC, need_gpu, to_dev, workspace_for, workspace_tail_intact
 
 pytestmark = pytest.mark.gpu
 
@@ -29,21 +30,30 @@ K_FP4 = (1 << 24) - 64       # 256 padded rows x K / 2 bytes = 2^31 - 8192
 K_MX = (1 << 24) - 512       # the same for the microscaled product (K % 512 == 0)
 
 
-@pytest.mark.parametrize("instance", [g.INSTANCE_LARGE, g.INSTANCE_SMALL, g.INSTANCE_SPLITK, g.INSTANCE_AUTO])
-def test_bf16_k_at_extent_limit(instance):
+@pytest.mark.parametrize("instance,ws", [(g.INSTANCE_LARGE, False), (g.INSTANCE_SMALL, False),
+                                         (g.INSTANCE_SPLITK, False), (g.INSTANCE_SPLITK, True),
+                                         (g.INSTANCE_AUTO, False), (g.INSTANCE_AUTO, True)])
+def test_bf16_k_at_extent_limit(instance, ws):
     need_gpu()
     M, N, K = 3, 16, K_BF16
-    print("bf16 K limit", instance, M, N, K, flush=True)
+    print("bf16 K limit", instance, ws, M, N, K, flush=True)
     A = syn.bf16_uniform(M, K, seed=101)
     B = syn.bf16_uniform(N, K, seed=102)
     C = GuardedC(M, N)
     try:
         g.force_instance(instance)
-        g.gemm_bf16_nt(M, N, K, to_dev(A), to_dev(B), C.view)
+        if ws:   # one 128 x 128 tile: K is split eight ways
+            buf, nbytes = workspace_for(M, N, K)
+            assert instance == g.INSTANCE_AUTO or nbytes == 8 * 65536
+            g.gemm_bf16_nt_ws(M, N, K, to_dev(A), to_dev(B), C.view, buf, nbytes)
+        else:
+            g.gemm_bf16_nt(M, N, K, to_dev(A), to_dev(B), C.view)
         torch.cuda.synchronize()
     finally:
         g.force_instance(g.INSTANCE_AUTO)
     assert C.guards_intact(), "write outside C"
+    if ws:
+        assert workspace_tail_intact(buf, nbytes), "write past the workspace"
     res = tolerance.check(C.bits(), oracle.gemm_bf16_nt(A, B), K)
     assert res, res
 

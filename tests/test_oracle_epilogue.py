@@ -4,8 +4,8 @@ of round-to-nearest-even, a library routine for the GELU (torch's tanh-form
 GELU in binary64), closed forms of the activations, and planted mistakes that
 the fused parity bound must catch. CPU only.
 
-Reference: "NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue Warps" (the
-epilogue is where activations and element-wise operations would be fused);
+Reference: "NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue Warps" (per-element
+work on the sums belongs in the epilogue);
 the operation itself (bias per output column, then ReLU or the tanh-form GELU)
 is this library's reading, since the page names none.
 """
