@@ -11,6 +11,7 @@ The functions mirror the C entry points declared in ``include/gemm355.h``:
     gemm_bf16_nt_ws(M, N, K, A, B, C, workspace, workspace_bytes=None, stream=None)
     gemm_bf16_nt_bias_act_ws(M, N, K, A, B, bias, activation, C, workspace, workspace_bytes=None, stream=None)
     workspace_size(M, N, K)           # bytes the *_ws calls need on the current device
+    gemm_bf16_nt_noalloc(M, N, K, A, B, C, stream=None)   # *_ws plan, library's fixed scratch
     gemm_nvfp4_nt(M, N, K, Aq, SFA, Bq, SFB, C, stream=None)
     gemm_nvfp4_nt_bias_act(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, stream=None)
     gemm_mxfp4_nt(M, N, K, Aq, SA, Bq, SB, C, stream=None)
@@ -82,6 +83,8 @@ def load() -> ctypes.CDLL:
     lib.gemm_bf16_nt_ws.restype = i
     lib.gemm_bf16_nt_bias_act_ws.argtypes = [i, i, i, p, p, p, i, p, p, sz, p]
     lib.gemm_bf16_nt_bias_act_ws.restype = i
+    lib.gemm_bf16_nt_noalloc.argtypes = [i, i, i, p, p, p, p]
+    lib.gemm_bf16_nt_noalloc.restype = i
     lib.gemm_bf16_nt_workspace_size.argtypes = [i, i, i, ctypes.POINTER(sz)]
     lib.gemm_bf16_nt_workspace_size.restype = i
     lib.gemm_nvfp4_nt.argtypes = [i, i, i, p, p, p, p, p, p]
@@ -223,6 +226,19 @@ def gemm_bf16_nt_bias_act_ws(M: int, N: int, K: int, A, B, bias, activation: int
     w, nb = _workspace(workspace, workspace_bytes)
     _check(lib.gemm_bf16_nt_bias_act_ws(M, N, K, a, b, bb, int(activation), c, w, nb, _stream(stream)),
            "gemm_bf16_nt_bias_act_ws")
+
+
+def gemm_bf16_nt_noalloc(M: int, N: int, K: int, A, B, C, stream=None) -> None:
+    """gemm_bf16_nt_ws's product with the library's fixed scratch array as
+    the workspace: allocates nothing (for graph capture and the like); calls
+    overlapping on one GPU race on the scratch."""
+    lib = load()
+    M, N, K = int(M), int(N), int(K)
+    nz = M > 0 and N > 0
+    a = _addr(A, M * K * 2 if nz else 0, "A")
+    b = _addr(B, N * K * 2 if nz else 0, "B")
+    c = _addr(C, M * N * 2 if nz else 0, "C")
+    _check(lib.gemm_bf16_nt_noalloc(M, N, K, a, b, c, _stream(stream)), "gemm_bf16_nt_noalloc")
 
 
 def workspace_size(M: int, N: int, K: int) -> int:

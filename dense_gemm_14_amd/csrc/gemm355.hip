@@ -18,6 +18,14 @@
 #include "gemm_fp4.hpp"
 #include "schedule.hpp"
 
+// Scratch of gemm_bf16_nt_noalloc: the split-K partials of the largest plan
+// on a 256-unit device (64 KiB per compute unit). Every GPU the library runs
+// on holds its own copy until the process ends. In host code `scratch` names
+// a host-side stand-in, never the device memory: the device address comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+static constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
 namespace {
 
 using gemm355::BM;
@@ -54,6 +62,26 @@ constexpr double kHbmBytesPerUs = 4.5e6;
 
 std::mutex g_cu_lock;
 int g_cu_count[kMaxDevices];   // 0 = not queried yet
+
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device; guarded by g_cu_lock
+
+// The device address of the current device's scratch array, looked up on the
+// first call on that device (with that device current).
+int scratch_address(void **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GEMM355_ERR_NO_DEVICE;
+    std::lock_guard<std::mutex> guard(g_cu_lock);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return GEMM355_ERR_NO_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return GEMM355_OK;
+}
 
 // Compute units of the current device, queried once per device.
 int compute_units(int *cus)
@@ -246,8 +274,9 @@ int launch_instance(const Bf16Plan &plan, const Problem &p, void *workspace, voi
 // Shared by the BF16 entry points: validation, plan, launch. FUSED selects
 // the kernels with the fused epilogue; WS the entry points that take a
 // workspace (K may then be split; NULL with workspace_bytes 0 is allowed and
-// rules splitting out only if the plan needs none).
-template <bool FUSED, bool WS>
+// rules splitting out only if the plan needs none); SCRATCH (with WS) uses
+// the library's fixed scratch array as the workspace instead of the caller's.
+template <bool FUSED, bool WS, bool SCRATCH = false>
 int bf16_product(int M, int N, int K, const void *A, const void *B, const void *bias, int act, void *C,
                  void *workspace, size_t workspace_bytes, void *stream)
 {
@@ -291,6 +320,14 @@ int bf16_product(int M, int N, int K, const void *A, const void *B, const void *
     if (rc != GEMM355_OK)
         return rc;
     const Bf16Plan plan = plan_bf16(M, N, K, cus, g_bf16_instance.load(std::memory_order_relaxed), WS);
+    if (SCRATCH && plan.workspace_bytes > 0) {
+        if (plan.workspace_bytes > kScratchBytes)
+            return GEMM355_ERR_UNSUPPORTED;   // the plan's partials exceed the fixed scratch
+        const int sr = scratch_address(&workspace);
+        if (sr != GEMM355_OK)
+            return sr;
+        workspace_bytes = kScratchBytes;
+    }
     if (plan.workspace_bytes > workspace_bytes)
         return GEMM355_ERR_UNSUPPORTED;   // the caller's workspace is smaller than the plan needs
     if (!FUSED)
@@ -327,6 +364,11 @@ extern "C" int gemm_bf16_nt_bias_act_ws(int M, int N, int K, const void *A, cons
                                         void *stream)
 {
     return bf16_product<true, true>(M, N, K, A, B, bias, activation, C, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gemm_bf16_nt_noalloc(int M, int N, int K, const void *A, const void *B, void *C, void *stream)
+{
+    return bf16_product<false, true, true>(M, N, K, A, B, nullptr, GEMM355_ACT_NONE, C, nullptr, 0, stream);
 }
 
 extern "C" int gemm_bf16_nt_workspace_size(int M, int N, int K, size_t *bytes)
@@ -506,7 +548,8 @@ extern "C" const char *gemm355_status_string(int status)
     case GEMM355_ERR_INVALID_ARG:
         return "invalid argument (negative size, NULL pointer or overlapping output)";
     case GEMM355_ERR_UNSUPPORTED:
-        return "unsupported (alignment, K or N granularity, or operand extent)";
+        return "unsupported (alignment, K or N granularity, operand extent, or a workspace smaller than the plan "
+               "needs)";
     case GEMM355_ERR_NO_DEVICE:
         return "no usable HIP device";
     case GEMM355_ERR_LAUNCH:

@@ -167,6 +167,28 @@ int gemm_bf16_nt_bias_act_ws(int M, int N, int K, const void *A, const void *B, 
                              void *C, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gemm_bf16_nt_noalloc -- gemm_bf16_nt_ws for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.
+ *
+ * Computes what gemm_bf16_nt_ws computes, with the same plan and bitwise the
+ * same result, but the split-K partials live in a fixed 16 MiB scratch array
+ * inside the library (one per device, held until the process ends) instead of
+ * a caller's workspace. No memory is allocated or freed, by the library or by
+ * any routine it calls. The first call on a device that splits K looks the
+ * array's device address up (hipGetSymbolAddress) with that device current.
+ * Every call on one device shares that device's array: calls whose execution
+ * overlaps on one GPU (other streams, other threads) race on it when both
+ * split K and give undefined results; calls ordered on one stream are safe.
+ * The array keeps the last call's partials; nothing needs to start at zero.
+ * Errors: as for gemm_bf16_nt_ws; a plan whose partials exceed 16 MiB (only
+ * possible on a device with more than 256 compute units) ->
+ * GEMM355_ERR_UNSUPPORTED, nothing enqueued; the address lookup failing ->
+ * GEMM355_ERR_NO_DEVICE.
+ */
+int gemm_bf16_nt_noalloc(int M, int N, int K, const void *A, const void *B, void *C, void *stream);
+
+/*
  * gemm355_force_instance -- override the choice of gemm_bf16_nt's instance.
  *
  * A diagnostic for tests and measurements (it is not defined by the pages):

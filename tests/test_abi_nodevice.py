@@ -313,6 +313,18 @@ def test_workspace_rejections_happen_before_any_device_call():
     assert lib.gemm_bf16_nt_workspace_size(0, 8, 8, ctypes.byref(out)) == g.OK and out.value == 0
 
 
+def test_noalloc_rejections_happen_before_any_device_call():
+    lib = g.load()
+    f = lambda M, N, K, a=FAKE, b=FAKE + 0x100000, c=FAKE + 0x200000: lib.gemm_bf16_nt_noalloc(M, N, K, a, b, c, None)
+    assert f(-1, 8, 64) == g.ERR_INVALID_ARG
+    assert f(0, 8, 64, None, None, None) == g.OK
+    assert f(8, 8, 64, c=None) == g.ERR_INVALID_ARG
+    assert f(8, 8, 64, a=None) == g.ERR_INVALID_ARG
+    assert f(8, 8, 12) == g.ERR_UNSUPPORTED                      # K % 8
+    assert f(8, 8, 64, c=FAKE + 0x900008) == g.ERR_UNSUPPORTED   # C not 16-byte aligned
+    assert f(8, 8, 64, c=FAKE + 0x100010) == g.ERR_INVALID_ARG   # C overlaps B
+
+
 def test_no_allocation_reachable_from_the_library():
     # the library allocates nothing: no allocation call appears in its host source
     src = open(os.path.join(os.path.dirname(g.__file__), "csrc", "gemm355.hip")).read()
