@@ -49,10 +49,28 @@ def compile_source(src: str, out: str) -> str:
     return out
 
 
+SANITIZE_DRIVER = os.path.join(_HERE, "sanitize_driver.c")
+SANITIZED_PATH = os.path.join(_HERE, "oracle355_sanitized")
+SANITIZE_FLAGS = ["-O1", "-g", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+                  "-fno-omit-frame-pointer", "-fsanitize=address,undefined,float-cast-overflow",
+                  "-fno-sanitize-recover=all"]
+
+
+def build_sanitized() -> str:
+    """gcc oracle355.c with sanitize_driver.c into one executable built with
+    AddressSanitizer and UndefinedBehaviorSanitizer (CPU tests only)."""
+    tmp = SANITIZED_PATH + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *SANITIZE_FLAGS, "-o", tmp, _SRC, SANITIZE_DRIVER, "-lm"], check=True)
+    os.replace(tmp, SANITIZED_PATH)
+    return SANITIZED_PATH
+
+
 def build(force: bool = True) -> str:
-    """Compile ``liboracle355.so`` with gcc (no HIP, no GPU headers)."""
+    """Compile ``liboracle355.so`` with gcc (no HIP, no GPU headers), and the
+    sanitizer build of the same source used by the CPU tests."""
     if not force and os.path.exists(LIB_PATH):
         return LIB_PATH
+    build_sanitized()
     return compile_source(_SRC, LIB_PATH)
 
 
