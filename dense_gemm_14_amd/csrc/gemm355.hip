@@ -418,6 +418,20 @@ extern "C" int gemm355_force_supergroup(int supergroup)
 
 namespace {
 
+// The NVFP4 kernel for the epilogue and the K granularity (KTAIL: K % 64 == 32).
+template <bool FUSED, bool KTAIL>
+int fp4_launch(const Problem &p, int act, void *stream)
+{
+    using namespace gemm355;
+    if (!FUSED)
+        return launch(fp4::gemm_nvfp4_nt_kernel<EPI_PLAIN, KTAIL>, p, stream);
+    if (act == GEMM355_ACT_RELU)
+        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_RELU, KTAIL>, p, stream);
+    if (act == GEMM355_ACT_GELU_TANH)
+        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_GELU_TANH, KTAIL>, p, stream);
+    return launch(fp4::gemm_nvfp4_nt_kernel<ACT_NONE, KTAIL>, p, stream);
+}
+
 // Shared by gemm_nvfp4_nt and gemm_nvfp4_nt_bias_act: validation, launch.
 template <bool FUSED>
 int fp4_product(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq, const void *SFB,
@@ -440,7 +454,7 @@ int fp4_product(int M, int N, int K, const void *Aq, const void *SFA, const void
     if (!aligned(Aq, 16) || !aligned(Bq, 16) || !aligned(C, 16) || !aligned(SFA, 4) || !aligned(SFB, 4) ||
         !aligned(bias, 16))
         return GEMM355_ERR_UNSUPPORTED;
-    if (K % 64 != 0 || N % 8 != 0)
+    if (K % 32 != 0 || N % 8 != 0)
         return GEMM355_ERR_UNSUPPORTED;
     if (!extent_ok(M, int64_t(K) / 2) || !extent_ok(N, int64_t(K) / 2) || !extent_ok(M, int64_t(N) * 2))
         return GEMM355_ERR_UNSUPPORTED;
@@ -455,13 +469,9 @@ int fp4_product(int M, int N, int K, const void *Aq, const void *SFA, const void
     p.M = M;
     p.N = N;
     p.K = K;
-    if (!FUSED)
-        return launch(gemm355::fp4::gemm_nvfp4_nt_kernel<gemm355::EPI_PLAIN>, p, stream);
-    if (act == GEMM355_ACT_RELU)
-        return launch(gemm355::fp4::gemm_nvfp4_nt_kernel<gemm355::ACT_RELU>, p, stream);
-    if (act == GEMM355_ACT_GELU_TANH)
-        return launch(gemm355::fp4::gemm_nvfp4_nt_kernel<gemm355::ACT_GELU_TANH>, p, stream);
-    return launch(gemm355::fp4::gemm_nvfp4_nt_kernel<gemm355::ACT_NONE>, p, stream);
+    if (K % 64 != 0)
+        return fp4_launch<FUSED, true>(p, act, stream);
+    return fp4_launch<FUSED, false>(p, act, stream);
 }
 
 } // namespace

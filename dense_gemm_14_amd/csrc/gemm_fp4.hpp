@@ -110,8 +110,13 @@ constexpr int LOADS = 8;         // staging loads per thread and step
 constexpr int LOAD_AT = 2;       // first of them (then one every 4 instructions)
 
 // EPI: EPI_PLAIN, or the activation of the fused epilogue (bias, then the
-// activation, before rounding).
-template <int EPI>
+// activation, before rounding). KTAIL: K % 64 == 32 (else K % 64 == 0), so
+// the upper 32-element half of the last step lies past K: its code and scale
+// loads are pointed out of range and read zeros (rows are contiguous, so
+// reading on would fetch the next row's codes), and a half's two scale bytes
+// are loaded with a 16-bit load, since rows of K / 16 scale bytes are then
+// only 2-byte aligned.
+template <int EPI, bool KTAIL>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_nvfp4_nt_kernel(Problem p)
 {
@@ -140,7 +145,8 @@ void gemm_nvfp4_nt_kernel(Problem p)
     // chunks 4 kh .. 4 kh + 3 of each row. wpos[d]: LDS position of chunk
     // 4 kh + d of row r0; row r0 + 128 is 128 rows further.
     const int r0 = tid >> 1, kh = tid & 1;
-    const int sf_shift = 16 * kh;   // this half's two scale bytes, moved to bytes 0 and 1
+    // this half's two scale bytes, moved to bytes 0 and 1 (a 16-bit load puts them there already)
+    const int sf_shift = KTAIL ? 0 : 16 * kh;
     int wpos[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
@@ -163,28 +169,42 @@ void gemm_nvfp4_nt_kernel(Problem p)
         supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
 
         const int a_code_off = (tm * BM + r0) * (int)kc + 16 * kh, b_code_off = (tn * BN + r0) * (int)kc + 16 * kh;
-        const int a_sf_off = (tm * BM + r0) * (int)ks, b_sf_off = (tn * BN + r0) * (int)ks;
+        const int a_sf_off = (tm * BM + r0) * (int)ks + (KTAIL ? 2 * kh : 0);
+        const int b_sf_off = (tn * BN + r0) * (int)ks + (KTAIL ? 2 * kh : 0);
         const int row2_codes = 128 * (int)kc, row2_sf = 128 * (int)ks;   // row r0 + 128
         StageRegs regs[2];
         // load q (0..7) of step kt into register set `set`: codes of row r0,
         // codes of row r0 + 128, scales of r0, scales of r0 + 128, for A (q < 4)
         // then B. The per-lane part of the offset is fixed for the tile (rows
         // past M or N lie beyond the buffer and read zeros); the step's K
-        // offset is uniform and goes in the scalar offset. K % 64 == 0, so a
-        // step is whole or past K; steps past K are requests made ahead for a
-        // step the tile never computes, and read step 0 again instead.
+        // offset is uniform and goes in the scalar offset. A step is whole or
+        // past K, except with KTAIL the upper half of the last step, whose
+        // loads go out of range and read zeros (zero codes: the half adds
+        // nothing). Steps past K are requests made ahead for a step the tile
+        // never computes, and read step 0 again instead.
         auto load = [&](int kt, int set, int q) {
             const int k0 = kt * BK < K ? kt * BK : 0;
+            // per-lane offset of this half (row r0 or r0 + 128 of either operand)
+            auto at = [&](int off) {
+                if constexpr (KTAIL)
+                    return (kh && kt == nk - 1) ? OOB : off;
+                return off;
+            };
+            auto sf = [&](__amdgpu_buffer_rsrc_t rs, int off) -> unsigned {
+                if constexpr (KTAIL)
+                    return __builtin_amdgcn_raw_buffer_load_b16(rs, at(off), k0 / 16, 0);
+                return __builtin_amdgcn_raw_buffer_load_b32(rs, off, k0 / 16, 0);
+            };
             StageRegs &r = regs[set];
             switch (q) {
-            case 0: r.a_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_code_off, k0 / 2, 0)); break;
-            case 1: r.a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_code_off + row2_codes, k0 / 2, 0)); break;
-            case 2: r.a_sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, a_sf_off, k0 / 16, 0); break;
-            case 3: r.a_sf[1] = __builtin_amdgcn_raw_buffer_load_b32(rsa, a_sf_off + row2_sf, k0 / 16, 0); break;
-            case 4: r.b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_code_off, k0 / 2, 0)); break;
-            case 5: r.b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_code_off + row2_codes, k0 / 2, 0)); break;
-            case 6: r.b_sf[0] = __builtin_amdgcn_raw_buffer_load_b32(rsb, b_sf_off, k0 / 16, 0); break;
-            default: r.b_sf[1] = __builtin_amdgcn_raw_buffer_load_b32(rsb, b_sf_off + row2_sf, k0 / 16, 0); break;
+            case 0: r.a_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, at(a_code_off), k0 / 2, 0)); break;
+            case 1: r.a_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, at(a_code_off + row2_codes), k0 / 2, 0)); break;
+            case 2: r.a_sf[0] = sf(rsa, a_sf_off); break;
+            case 3: r.a_sf[1] = sf(rsa, a_sf_off + row2_sf); break;
+            case 4: r.b_code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, at(b_code_off), k0 / 2, 0)); break;
+            case 5: r.b_code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, at(b_code_off + row2_codes), k0 / 2, 0)); break;
+            case 6: r.b_sf[0] = sf(rsb, b_sf_off); break;
+            default: r.b_sf[1] = sf(rsb, b_sf_off + row2_sf); break;
             }
         };
         // chunk c (0..15) of register set `set` into `stage`: A for c < 8,

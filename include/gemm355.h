@@ -254,7 +254,8 @@ int gemm355_bf16_plan(int M, int N, int K, int compute_units, int with_workspace
  * (at most 6 significant bits, magnitude within [2^-10, 2688]).
  * Edge cases as for gemm_bf16_nt.
  * Requirements, else GEMM355_ERR_UNSUPPORTED: Aq, Bq, C 16-byte aligned; SFA,
- * SFB 4-byte aligned; K % 64 == 0; N % 8 == 0; extents as for gemm_bf16_nt.
+ * SFB 4-byte aligned; K % 32 == 0 (whole 16-byte groups of codes per row and
+ * whole pairs of scale blocks); N % 8 == 0; extents as for gemm_bf16_nt.
  */
 int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
                   const void *SFB, void *C, void *stream);

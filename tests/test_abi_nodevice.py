@@ -89,7 +89,7 @@ def _fused4(M, N, K, act=0, bias=FAKE + 0x500000, c=FAKE + 0x400000):
 
 
 def test_fp4_fused_epilogue_rejections():
-    assert _fused4(8, 8, 32) == g.ERR_UNSUPPORTED                  # K % 64
+    assert _fused4(8, 8, 48) == g.ERR_UNSUPPORTED                  # K % 32
     for bad_act in (-1, 3):
         assert _fused4(8, 8, 64, act=bad_act) == g.ERR_INVALID_ARG
     assert _fused4(8, 8, 64, bias=FAKE + 0x500004) == g.ERR_UNSUPPORTED
@@ -126,13 +126,18 @@ def test_extent_limits_are_exact():
     assert lib.gemm_bf16_nt(3, 16, 1 << 22, big[0], big[1], big[2], None) == g.ERR_UNSUPPORTED
     assert lib.gemm_nvfp4_nt(3, 16, (1 << 24) - 64, *big, None) == g.ERR_NO_DEVICE
     assert lib.gemm_nvfp4_nt(3, 16, 1 << 24, *big, None) == g.ERR_UNSUPPORTED
+    # K % 32 == 0 is accepted (here the call then stops at the missing device)
+    for K in (32, 96, 8160):
+        assert lib.gemm_nvfp4_nt(3, 16, K, *big, None) == g.ERR_NO_DEVICE, K
+        assert lib.gemm_nvfp4_nt_bias_act(3, 16, K, *big[:4], None, 2, big[4], None) == g.ERR_NO_DEVICE, K
     assert lib.gemm_bf16_nt((1 << 27) - 300, 8, 8, big[0], big[1], big[2], None) == g.ERR_NO_DEVICE   # C, A
     assert lib.gemm_bf16_nt(1 << 27, 8, 8, big[0], big[1], big[2], None) == g.ERR_UNSUPPORTED
 
 
 def test_fp4_specific_rejections():
     assert _fp4(8, 8, 64, sfa=None) == g.ERR_INVALID_ARG
-    assert _fp4(8, 8, 32) == g.ERR_UNSUPPORTED                    # K % 64
+    assert _fp4(8, 8, 48) == g.ERR_UNSUPPORTED                    # K % 32
+    assert _fp4(8, 8, 16) == g.ERR_UNSUPPORTED
     assert _fp4(8, 8, 64, sfb=FAKE + 0x300002) == g.ERR_UNSUPPORTED  # scales need 4-byte alignment
     assert _fp4(8, 8, 64, aq=FAKE + 8) == g.ERR_UNSUPPORTED
 

@@ -101,3 +101,76 @@ def test_fp4_workload_exactly_summable_every_element():
     assert np.array_equal(oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns), want[ms, ns])
     bad = np.argwhere(C != want)
     assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+
+
+# ---- K % 64 == 32: the last K step is half past K -----------------------------
+# Rows are contiguous, so the upper half of the last step, read as it stands,
+# would fetch the first codes and scales of the next row; the kernel must read
+# zeros there instead. Random codes in every row make any such leak visible.
+
+@pytest.mark.parametrize("M,N,K", [(257, 264, 32), (300, 520, 96), (65, 264, 8160), (4352, 4104, 96),
+                                   (8, 8, 32)])
+def test_k_half_step_tail_matches_oracle(M, N, K):
+    need_gpu()
+    print("fp4 K tail", M, N, K, flush=True)
+    Aq, SFA = syn.fp4_operand(M, K, seed=M + 7 * N + K)
+    Bq, SFB = syn.fp4_operand(N, K, seed=M + 7 * N + K + 1)
+    C = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+    sig = _sigma(Aq[:512], SFA[:512], K) * _sigma(Bq[:512], SFB[:512], K)
+    if M * N <= 300 * 520:
+        res = tolerance.check(C, oracle.gemm_nvfp4_nt(Aq, SFA, Bq, SFB, K), K, sig)
+    else:   # two rounds of tiles per workgroup: sampled, every tile edge included
+        ms, ns = sample_positions(M, N, 4000, seed=K)
+        res = tolerance.check(C[ms, ns], oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns), K, sig)
+    assert res, res
+
+
+@pytest.mark.parametrize("M,N,K", [(264, 520, 480), (513, 256, 96), (4352, 4104, 32)])
+def test_k_half_step_tail_exact_bitwise(M, N, K):
+    # scales 2^0 * (1 + m/8), all 16 codes, K <= 512: every partial sum is
+    # exact in FP32, so the answer is unique and a leaked half step would show
+    need_gpu()
+    print("fp4 K tail exact", M, N, K, flush=True)
+    Aq = syn.fp4_codes(M, K, seed=K + 61)
+    Bq = syn.fp4_codes(N, K, seed=K + 62)
+    SFA = syn.e4m3_scales(M, K, seed=K + 63, u_lo=0, u_hi=0)
+    SFB = syn.e4m3_scales(N, K, seed=K + 64, u_lo=0, u_hi=0)
+    C = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+    Ad, Bd = oracle.decode_nvfp4(Aq, SFA, K), oracle.decode_nvfp4(Bq, SFB, K)
+    want = oracle.bf16_from_double(Ad @ Bd.T)
+    ms, ns = sample_positions(M, N, 300, seed=K)
+    assert np.array_equal(oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns), want[ms, ns])
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+
+
+def test_k_half_step_tail_decoded_identity():
+    # B = I (code 2 on the diagonal, unit scales) at K = 480: C = dec(A)
+    need_gpu()
+    M, K = 300, 480
+    Aq, SFA = syn.fp4_operand(M, K, seed=66)
+    codes = np.zeros((K, K), np.uint8)
+    codes[np.arange(K), np.arange(K)] = 2
+    Bq = syn.pack_nibbles(codes)
+    SFB = np.full((K, K // 16), 0x38, np.uint8)
+    C = run_fp4(Aq, SFA, Bq, SFB, M, K, K)
+    want = syn.to_bf16_bits(oracle.decode_nvfp4(Aq, SFA, K))
+    assert np.array_equal(tolerance.bf16_bits_to_f64(C), tolerance.bf16_bits_to_f64(want))
+
+
+def test_k_half_step_tail_fused_epilogue():
+    need_gpu()
+    M, N, K = 300, 264, 96
+    Aq, SFA = syn.fp4_operand(M, K, seed=67)
+    Bq, SFB = syn.fp4_operand(N, K, seed=68)
+    bias = syn.bf16_uniform(1, N, seed=69, lo=-64.0, hi=64.0)[0]
+    C = GuardedC(M, N)
+    g.gemm_nvfp4_nt_bias_act(M, N, K, *(to_dev(x) for x in (Aq, SFA, Bq, SFB)), to_dev(bias), g.ACT_GELU_TANH,
+                             C.view)
+    torch.cuda.synchronize()
+    assert C.guards_intact(), "write outside C"
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    ref, z = oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, bias, g.ACT_GELU_TANH, ms, ns, with_z=True)
+    sig = _sigma(Aq, SFA, K) * _sigma(Bq, SFB, K)
+    res = tolerance.check_fused(C.bits(), ref.reshape(M, N), z.reshape(M, N), K, g.ACT_GELU_TANH, sig)
+    assert res, res

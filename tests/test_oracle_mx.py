@@ -95,3 +95,19 @@ def test_mx_fused_oracle_rejects_bad_arguments():
         oracle.gemm_mxfp4_nt_bias_act_at(Aq, SA, Bq, SB, 64, None, oracle.ACT_NONE, np.array([2]), np.array([0]))
     with pytest.raises(ValueError):
         oracle.gemm_mxfp4_nt_bias_act_at(Aq[:, :8], SA[:, :1], Bq[:, :8], SB[:, :1], 16, None, oracle.ACT_NONE, ms, ns)
+
+
+def test_mx_equals_decode_then_bf16_path():
+    # with the workload's scales (2^u, u in -4..4) every decoded element is
+    # e2m1 * 2^u, at most 2 significant bits: exact in BF16, so the
+    # microscaled product is the BF16 product of the decoded operands
+    K = 256
+    Aq, SA = syn.mxfp4_operand(33, K, seed=30)
+    Bq, SB = syn.mxfp4_operand(17, K, seed=31)
+    e2 = np.array([oracle.e2m1_to_double(c) for c in range(16)])
+    e8 = np.array([oracle.e8m0_to_double(b) for b in range(255)] + [np.nan])
+    dec = lambda Q, S: e2[np.stack([Q & 15, Q >> 4], -1).reshape(Q.shape[0], -1)] * np.repeat(e8[S], 32, axis=1)
+    Ad, Bd = dec(Aq, SA), dec(Bq, SB)
+    Ab, Bb = oracle.bf16_from_double(Ad), oracle.bf16_from_double(Bd)
+    assert np.array_equal(oracle.bf16_to_double(Ab), Ad)
+    assert np.array_equal(oracle.gemm_mxfp4_nt(Aq, SA, Bq, SB, K), oracle.gemm_bf16_nt(Ab, Bb))
