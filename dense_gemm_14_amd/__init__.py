@@ -18,6 +18,8 @@ The functions mirror the C entry points declared in ``include/gemm355.h``:
     gemm_mxfp4_nt_bias_act(M, N, K, Aq, SA, Bq, SB, bias, activation, C, stream=None)
     force_instance(instance)          # BF16 instance override (diagnostic)
     force_supergroup(width)           # band width of the tile order (diagnostic)
+    supergroup(tiles_n, K, kernel)    # the default band width of a kernel's visiting order
+    force_schedule(mode)              # static or dynamic tile order of the NVFP4 kernel (diagnostic)
     bf16_plan(M, N, K, compute_units, with_workspace=False)  # (instance, splits) a BF16 call would run
     bf16_plan_workspace_bytes(M, N, K, compute_units)  # workspace bytes of the *_ws plan
 
@@ -50,6 +52,12 @@ ACT_GELU_TANH = 2
 INSTANCE_AUTO = 0    # gemm_bf16_nt picks the instance by shape
 INSTANCE_LARGE = 1   # 256 x 256 output tiles
 INSTANCE_SMALL = 2   # 64 x 64 output tiles
+KERNEL_BF16 = 0     # kernels of the supergroup rule (gemm355_supergroup)
+KERNEL_NVFP4 = 1
+KERNEL_MXFP4 = 2
+KERNEL_BF16_SMALL = 3
+SCHEDULE_STATIC = 0  # the NVFP4 kernel's tile order (gemm355_force_schedule)
+SCHEDULE_DYNAMIC = 1
 INSTANCE_SPLITK = 3  # 128 x 128 output tiles; with a workspace (the *_ws calls) K split over workgroups
 
 _lib = None
@@ -103,6 +111,10 @@ def load() -> ctypes.CDLL:
     lib.gemm355_schedule.restype = i
     lib.gemm355_force_instance.argtypes = [i]
     lib.gemm355_force_instance.restype = i
+    lib.gemm355_force_schedule.argtypes = [i]
+    lib.gemm355_force_schedule.restype = i
+    lib.gemm355_supergroup.argtypes = [i, i, i]
+    lib.gemm355_supergroup.restype = i
     lib.gemm355_force_supergroup.argtypes = [i]
     lib.gemm355_force_supergroup.restype = i
     lib.gemm355_bf16_plan.argtypes = [i, i, i, i, i, p, p, p]
@@ -328,6 +340,21 @@ def _plan(M, N, K, compute_units, with_workspace):
     _check(load().gemm355_bf16_plan(M, N, K, compute_units, int(bool(with_workspace)), ctypes.byref(inst),
                                     ctypes.byref(splits), ctypes.byref(nbytes)), "gemm355_bf16_plan")
     return inst.value, splits.value, nbytes.value
+
+
+def force_schedule(mode: int) -> None:
+    """Tile order of the NVFP4 kernel for the whole process: SCHEDULE_STATIC
+    (default) or SCHEDULE_DYNAMIC (a measurement option)."""
+    _check(load().gemm355_force_schedule(mode), "gemm355_force_schedule")
+
+
+def supergroup(tiles_n: int, K: int, kernel: int = 0) -> int:
+    """Default band width of the visiting order (kernel: KERNEL_BF16,
+    KERNEL_NVFP4, KERNEL_MXFP4 or KERNEL_BF16_SMALL); host only."""
+    r = load().gemm355_supergroup(int(kernel), int(tiles_n), int(K))
+    if r < 0:
+        raise Gemm355Error(-r, "gemm355_supergroup")
+    return r
 
 
 def bf16_plan(M: int, N: int, K: int, compute_units: int, with_workspace: bool = False):

@@ -33,11 +33,39 @@ using gemm355::BN;
 using gemm355::Problem;
 
 constexpr int kMaxDevices = 64;
-constexpr int kSupergroup = 8; // adjacent N tiles per band of the visiting order
+// Band width of the supergroup visiting order ("NVFP4 GEMM on Blackwell",
+// "Production Kernel", "Supergroup Size"). One XCD's L2 (4 MB) serves the
+// grid / 8 = 32 tiles its workgroups compute at once; a band of w adjacent N
+// tiles makes those tiles a (32 / w) x w block, whose A and B strips number
+// 32 / w + w: fewest (12) at w = 4 or 8, and the K steps of a strip are what
+// each L2 re-serves. That decides whenever the tile's K loop is long. When it
+// is short (K <= 1024: at most 16 steps) the C writes weigh as much as the
+// operands, all of which fit in the 256 MB last-level cache, and a wide band
+// keeps w tiles of the same C rows in flight, so C is written in runs of
+// w x 512 bytes. Measured (256 x 256 tiles, min of round-robin passes):
+//  * BF16 (27 shapes, M, N in {4096, 8192, 16384}, K in {1024, 4096, 16384})
+//    and microscaled FP4: w = 16 is 4-6 % (BF16) and 6-16 % (FP4) faster than
+//    8 when K <= 1024 with at least 64 tiles across N; elsewhere 8 is best or
+//    within noise;
+//  * NVFP4 (decode-bound, a prologue per tile): w = 16 is 3-15 % faster from
+//    32 tiles across N when K <= 2048, and 1-2 % slower at 16 tiles.
+enum Kernel { KERNEL_BF16 = 0, KERNEL_NVFP4 = 1, KERNEL_MXFP4 = 2, KERNEL_BF16_SMALL = 3 };
+int supergroup_for(int kernel, int tiles_n, int K)
+{
+    if (kernel == KERNEL_NVFP4)
+        return (K <= 2048 && tiles_n >= 32) ? 16 : 8;
+    if (kernel == KERNEL_BF16 || kernel == KERNEL_MXFP4)
+        return (K <= 1024 && tiles_n >= 64) ? 16 : 8;
+    return 8;   // the 64 x 64 instance (few tiles; not ablated)
+}
 
-// Band width override for measurements (0 = kSupergroup); set through
+// Band width override for measurements (0 = supergroup_for); set through
 // gemm355_force_supergroup.
 std::atomic<int> g_supergroup{0};
+
+// Tile order of the NVFP4 kernel: 0 static, 1 dynamic (a measurement option;
+// set through gemm355_force_schedule).
+std::atomic<int> g_schedule{0};
 
 // BF16 kernel instance: 0 = chosen by shape, 1 = 256 x 256 tiles, 2 = 64 x 64
 // tiles, 3 = 128 x 128 tiles with split K (set through gemm355_force_instance,
@@ -135,8 +163,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // One launch of a persistent kernel on `stream`: tile counts for tile_m x
 // tile_n output tiles, the supergroup width, a grid of at most one workgroup
 // per compute unit, `threads` work-items per workgroup.
-template <class Kernel>
-int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n = BN, int threads = gemm355::THREADS)
+template <class KernelFn>
+int launch(KernelFn kernel, int which, Problem p, void *stream, int tile_m = BM, int tile_n = BN,
+           int threads = gemm355::THREADS)
 {
     int cus = 0;
     const int rc = compute_units(&cus);
@@ -146,7 +175,7 @@ int launch(Kernel kernel, Problem p, void *stream, int tile_m = BM, int tile_n =
     p.tiles_n = (int)ceil_div(p.N, tile_n);
     p.tiles = p.tiles_m * p.tiles_n;
     const int sg = g_supergroup.load(std::memory_order_relaxed);
-    p.supergroup = sg > 0 ? sg : kSupergroup;
+    p.supergroup = sg > 0 ? sg : supergroup_for(which, p.tiles_n, p.K);
     p.grid = gemm355::persistent_grid(p.tiles, cus);
     return launch_kernel(kernel, (unsigned)p.grid, (unsigned)threads, p, static_cast<hipStream_t>(stream));
 }
@@ -266,9 +295,9 @@ int launch_instance(const Bf16Plan &plan, const Problem &p, void *workspace, voi
     if (plan.instance == 3)
         return launch_splitk<EPI>(p, plan, workspace, stream);
     if (plan.instance == 2)
-        return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel<EPI>, p, stream, gemm355::bf16_small::TM,
-                      gemm355::bf16_small::TN);
-    return launch(gemm355::bf16::gemm_bf16_nt_kernel<EPI>, p, stream);
+        return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel<EPI>, KERNEL_BF16_SMALL, p, stream,
+                      gemm355::bf16_small::TM, gemm355::bf16_small::TN);
+    return launch(gemm355::bf16::gemm_bf16_nt_kernel<EPI>, KERNEL_BF16, p, stream);
 }
 
 // Shared by the BF16 entry points: validation, plan, launch. FUSED selects
@@ -408,6 +437,21 @@ extern "C" int gemm355_force_instance(int instance)
     return GEMM355_OK;
 }
 
+extern "C" int gemm355_force_schedule(int mode)
+{
+    if (mode < 0 || mode > 1)
+        return GEMM355_ERR_INVALID_ARG;
+    g_schedule.store(mode, std::memory_order_relaxed);
+    return GEMM355_OK;
+}
+
+extern "C" int gemm355_supergroup(int kernel, int tiles_n, int K)
+{
+    if (kernel < KERNEL_BF16 || kernel > KERNEL_BF16_SMALL || tiles_n <= 0 || K < 0)
+        return -GEMM355_ERR_INVALID_ARG;
+    return supergroup_for(kernel, tiles_n, K);
+}
+
 extern "C" int gemm355_force_supergroup(int supergroup)
 {
     if (supergroup < 0 || supergroup > 4096)
@@ -423,13 +467,15 @@ template <bool FUSED, bool KTAIL>
 int fp4_launch(const Problem &p, int act, void *stream)
 {
     using namespace gemm355;
+    if (!FUSED && !KTAIL && g_schedule.load(std::memory_order_relaxed) == 1)
+        return launch(fp4::gemm_nvfp4_nt_kernel<EPI_PLAIN, false, true>, KERNEL_NVFP4, p, stream);
     if (!FUSED)
-        return launch(fp4::gemm_nvfp4_nt_kernel<EPI_PLAIN, KTAIL>, p, stream);
+        return launch(fp4::gemm_nvfp4_nt_kernel<EPI_PLAIN, KTAIL>, KERNEL_NVFP4, p, stream);
     if (act == GEMM355_ACT_RELU)
-        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_RELU, KTAIL>, p, stream);
+        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_RELU, KTAIL>, KERNEL_NVFP4, p, stream);
     if (act == GEMM355_ACT_GELU_TANH)
-        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_GELU_TANH, KTAIL>, p, stream);
-    return launch(fp4::gemm_nvfp4_nt_kernel<ACT_NONE, KTAIL>, p, stream);
+        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_GELU_TANH, KTAIL>, KERNEL_NVFP4, p, stream);
+    return launch(fp4::gemm_nvfp4_nt_kernel<ACT_NONE, KTAIL>, KERNEL_NVFP4, p, stream);
 }
 
 // Shared by gemm_nvfp4_nt and gemm_nvfp4_nt_bias_act: validation, launch.
@@ -528,12 +574,12 @@ int mx_product(int M, int N, int K, const void *Aq, const void *SA, const void *
     p.K = K;
     using namespace gemm355;
     if (!FUSED)
-        return launch(mx::gemm_mxfp4_nt_kernel<EPI_PLAIN>, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
+        return launch(mx::gemm_mxfp4_nt_kernel<EPI_PLAIN>, KERNEL_MXFP4, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
     if (act == GEMM355_ACT_RELU)
-        return launch(mx::gemm_mxfp4_nt_kernel<ACT_RELU>, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
+        return launch(mx::gemm_mxfp4_nt_kernel<ACT_RELU>, KERNEL_MXFP4, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
     if (act == GEMM355_ACT_GELU_TANH)
-        return launch(mx::gemm_mxfp4_nt_kernel<ACT_GELU_TANH>, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
-    return launch(mx::gemm_mxfp4_nt_kernel<ACT_NONE>, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
+        return launch(mx::gemm_mxfp4_nt_kernel<ACT_GELU_TANH>, KERNEL_MXFP4, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
+    return launch(mx::gemm_mxfp4_nt_kernel<ACT_NONE>, KERNEL_MXFP4, p, stream, mx::TM, mx::TN, mx::THREADS_MX);
 }
 
 } // namespace

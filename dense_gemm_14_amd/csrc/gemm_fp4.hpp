@@ -16,11 +16,16 @@
 //     stage s^1, and the slice after it is requested from memory. One
 //     workgroup barrier per K step separates reuse of a stage.
 //   * LDS rows are 128 bytes (64 FP16 values); the 16-byte chunk c of row r is
-//     stored at chunk position c ^ ((r >> 1) & 7). gfx950's LDS serves a
-//     ds_read_b128 16 lanes (256 bytes, 64 banks of 4 bytes) per cycle; the 16
-//     consecutive rows one such group reads at the same logical chunk then
-//     cover all 16 bank groups (row parity picks the 128-byte half of the bank
-//     space, (r >> 1) & 7 the chunk within it), so the reads are conflict-free.
+//     stored at chunk position c ^ s(r), s(r) = ((r >> 1) & 7) ^ ((r & 1) << 1).
+//     Measured on gfx950 (a probe timing each access pattern): ds_read_b128
+//     serves 16 lanes (256 bytes over 64 four-byte banks) per cycle, and the
+//     fragment reads -- 16 rows at one logical chunk -- hit 16 distinct bank
+//     groups for any s whose (row parity, s) pairs are distinct; ds_write_b128
+//     serves 8 lanes per cycle within a 128-byte bank window, and a staging
+//     write -- four consecutive rows, two chunks 4 apart each -- needs s & 3
+//     distinct over every aligned group of four rows. The plain (r >> 1) & 7
+//     fails the second (16 against 13 cycles per write); folding row bit 0
+//     into bit 1 satisfies both.
 #pragma once
 
 #include "common.hpp"
@@ -40,7 +45,7 @@ constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
 // Physical 16-byte chunk position of logical chunk `chunk` in LDS tile row `row`.
 __device__ inline int swizzle(int row, int chunk)
 {
-    return chunk ^ ((row >> 1) & 7);
+    return chunk ^ (((row >> 1) & 7) ^ ((row & 1) << 1));
 }
 
 // ---- block-scaled FP4 operands ---------------------------------------------
@@ -105,22 +110,45 @@ __device__ inline f16x2 scale2(f16x2 s)
 // spread over several matrix instructions (on gfx950 a wave fits about four
 // vector instructions under one 32 x 32 x 16 matrix instruction before the
 // matrix rate drops; measured).
+// ---- dynamic tile order (a measurement option) -------------------------------
+//
+// "NVFP4 GEMM on Blackwell", "Production Kernel", "Static vs Dynamic Tile
+// Scheduling": instead of the fixed round-robin order, a workgroup asks for
+// its next tile when it starts the current one. Here a ticket counter per XCD
+// keeps each XCD's tiles the ones the static order gives it (so their A and B
+// strips still share that XCD's L2); a workgroup whose XCD has no tiles left
+// takes them from the other XCDs' counters in turn, which is where the order
+// can rebalance work. Ticket i of XCD x (g = grid / 8 workgroups per XCD) is
+// position (i / g) grid + x g + i % g of the visiting order; tickets 0 .. g - 1
+// are the first round, which each workgroup takes without asking. Each
+// counter has its own 256-byte line. The counters start at zero, and the last
+// workgroup to finish sets them back to zero, so every launch finds them
+// cleared; launches that overlap on one GPU share them and must not use this
+// option.
+struct DynamicOrder {
+    unsigned next[8][64];   // next[x][0]: tickets handed out on XCD x beyond the first round
+    unsigned done[64];      // done[0]: workgroups that found no tile left
+};
+__device__ DynamicOrder g_dynamic_order;
+
 constexpr int CHUNK_EVERY = 3;   // matrix instructions per written chunk
 constexpr int LOADS = 8;         // staging loads per thread and step
 constexpr int LOAD_AT = 2;       // first of them (then one every 4 instructions)
 
 // EPI: EPI_PLAIN, or the activation of the fused epilogue (bias, then the
-// activation, before rounding). KTAIL: K % 64 == 32 (else K % 64 == 0), so
+// activation, before rounding). DYN: the dynamic tile order above instead of
+// the static one. KTAIL: K % 64 == 32 (else K % 64 == 0), so
 // the upper 32-element half of the last step lies past K: its code and scale
 // loads are pointed out of range and read zeros (rows are contiguous, so
 // reading on would fetch the next row's codes), and a half's two scale bytes
 // are loaded with a 16-bit load, since rows of K / 16 scale bytes are then
 // only 2-byte aligned.
-template <int EPI, bool KTAIL>
+template <int EPI, bool KTAIL, bool DYN = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_nvfp4_nt_kernel(Problem p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+    __shared__ int next_pos;   // DYN: the workgroup's next tile, written by thread 0
     typedef f16x8 frag;
 
     const int tid = threadIdx.x;
@@ -161,10 +189,22 @@ void gemm_nvfp4_nt_kernel(Problem p)
     const __amdgpu_buffer_rsrc_t rbias = make_rsrc(p.bias, EPI != EPI_PLAIN && p.bias ? (unsigned)p.N * 2u : 0u);
     const int nk = (K + BK - 1) / BK;
 
+    // dynamic order: XCDs (counters) and workgroups per XCD, and this one's XCD
+    const int nx = p.grid % 8 == 0 ? 8 : 1, per_xcd = p.grid / nx, xcd = blockIdx.x % nx;
+    auto ticket_position = [&](int x, unsigned i) {
+        return (int)(i / (unsigned)per_xcd) * p.grid + x * per_xcd + (int)(i % (unsigned)per_xcd);
+    };
+    int pos = schedule_position(blockIdx.x, 0, p.grid);
     for (int round = 0;; ++round) {
-        const int pos = schedule_position(blockIdx.x, round, p.grid);
+        if (!DYN)
+            pos = schedule_position(blockIdx.x, round, p.grid);
         if (pos >= p.tiles)
             break;
+        // DYN: the ticket for the next tile, requested now (one lane, a
+        // vector-memory atomic), turned into a position after the prologue
+        unsigned ticket = 0;
+        if (DYN && tid == 0)
+            ticket = atomicAdd(&g_dynamic_order.next[xcd][0], 1u);
         int tm, tn;
         supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
 
@@ -248,6 +288,17 @@ void gemm_nvfp4_nt_kernel(Problem p)
         for (int q = 0; q < LOADS; ++q)
             load(1, 1, q);
         static_for<16>([&](auto c) { write_chunk(lds, 0, c); });
+        // DYN: the ticket has returned by now (it was requested before the
+        // loads just written out); thread 0 turns it into the next tile
+        if (DYN && tid == 0) {
+            int np = ticket_position(xcd, (unsigned)per_xcd + ticket);
+            // this XCD has no tile left: take one from the other XCDs in turn
+            for (int d = 1; d < nx && np >= p.tiles; ++d) {
+                const int y = (xcd + d) % nx;
+                np = ticket_position(y, (unsigned)per_xcd + atomicAdd(&g_dynamic_order.next[y][0], 1u));
+            }
+            next_pos = np;
+        }
         lds_barrier();
         read_frags(lds, 0, 0);
         SCHED_FENCE();
@@ -310,6 +361,17 @@ void gemm_nvfp4_nt_kernel(Problem p)
         }
 
         store_tile<EPI>(acc, rc, rbias, p.M, p.N, tm * BM + wm * 128, tn * BN + wn * 128, l32, half);
+        if (DYN)
+            pos = next_pos;   // written before the prologue's barrier, rewritten only after the next one
+    }
+    if (DYN && tid == 0) {
+        // every workgroup that finished has stopped asking for tickets: the
+        // last one clears the counters for the next launch
+        if (atomicAdd(&g_dynamic_order.done[0], 1u) == (unsigned)p.grid - 1) {
+            for (int x = 0; x < 8; ++x)
+                atomicExch(&g_dynamic_order.next[x][0], 0u);
+            atomicExch(&g_dynamic_order.done[0], 0u);
+        }
     }
 }
 

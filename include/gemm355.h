@@ -210,14 +210,52 @@ int gemm355_force_instance(int instance);
  * pages ablate this width per shape) used by the persistent kernels of
  * gemm_bf16_nt and gemm_nvfp4_nt.
  *
- * A diagnostic for measurements: 0 restores the default (8 adjacent N tiles
- * per band), 1..4096 forces that width for every later launch in the process.
+ * A diagnostic for measurements: 0 restores the default (gemm355_supergroup's
+ * width for 256 x 256 tiles, 8 for the 64 x 64 instance), 1..4096 forces that
+ * width for every later launch in the process.
  * The result of a product does not depend on it (every tile is computed the
  * same way, only the order changes). Returns GEMM355_OK, or
  * GEMM355_ERR_INVALID_ARG for any other value (the setting is then
  * unchanged). No HIP call is made.
  */
 int gemm355_force_supergroup(int supergroup);
+
+/* Kernels of gemm355_supergroup's rule. */
+typedef enum gemm355_kernel {
+    GEMM355_KERNEL_BF16 = 0,        /* gemm_bf16_nt, 256 x 256 tiles      */
+    GEMM355_KERNEL_NVFP4 = 1,       /* gemm_nvfp4_nt                       */
+    GEMM355_KERNEL_MXFP4 = 2,       /* gemm_mxfp4_nt                       */
+    GEMM355_KERNEL_BF16_SMALL = 3   /* gemm_bf16_nt, 64 x 64 tiles        */
+} gemm355_kernel;
+
+/*
+ * gemm355_supergroup -- the default band width of the supergroup visiting
+ * order ("NVFP4 GEMM on Blackwell", "Production Kernel", "Supergroup Size")
+ * for a kernel (a gemm355_kernel), the number of output tiles across N and K.
+ * A measured rule: 16 for short K loops with many tiles across N, where wide
+ * bands write C in longer runs (BF16 and microscaled FP4: K <= 1024 and at
+ * least 64 tiles; NVFP4: K <= 2048 and at least 32 tiles), else 8 (the
+ * fewest A and B strips for the 32 tiles one XCD's L2 serves at once; always
+ * for the 64 x 64 instance). Returns the width, or -GEMM355_ERR_INVALID_ARG
+ * for an unknown kernel, tiles_n <= 0 or K < 0. Pure host arithmetic.
+ */
+int gemm355_supergroup(int kernel, int tiles_n, int K);
+
+/*
+ * gemm355_force_schedule -- tile order of gemm_nvfp4_nt's persistent kernel
+ * ("NVFP4 GEMM on Blackwell", "Production Kernel", "Static vs Dynamic Tile
+ * Scheduling"), a diagnostic for measurements: 0 (the default) the static
+ * order; 1 a dynamic order -- one ticket counter per XCD, each workgroup
+ * asking for its next tile as it starts the current one (one lane's atomic
+ * add), taking tiles from the other XCDs once its own has none left. Applies
+ * to gemm_nvfp4_nt with K % 64 == 0 (other calls keep the static order). The
+ * result does not depend on the order. The counters are one fixed set per
+ * device, cleared by the last workgroup of each launch: products running at
+ * the same time on one GPU must not use the dynamic order. Returns GEMM355_OK
+ * or GEMM355_ERR_INVALID_ARG for another mode (setting unchanged). No HIP
+ * call is made.
+ */
+int gemm355_force_schedule(int mode);
 
 /*
  * gemm355_bf16_plan -- the instance a BF16 product would run for M x N x K on

@@ -218,6 +218,32 @@ def test_force_instance_accepts_only_known_instances():
         assert lib.gemm355_force_instance(ok) == g.OK
 
 
+def test_force_schedule_accepts_only_known_modes():
+    lib = g.load()
+    for bad in (-1, 2, 7):
+        assert lib.gemm355_force_schedule(bad) == g.ERR_INVALID_ARG
+    for ok in (g.SCHEDULE_DYNAMIC, g.SCHEDULE_STATIC):
+        assert lib.gemm355_force_schedule(ok) == g.OK
+
+
+def test_supergroup_rule():
+    # 16 only for short K loops with many tiles across N, where the ablations
+    # measured it faster; 8 everywhere else
+    for k in (g.KERNEL_BF16, g.KERNEL_MXFP4):
+        assert g.supergroup(64, 1024, k) == 16 and g.supergroup(128, 256, k) == 16
+        assert g.supergroup(63, 1024, k) == 8 and g.supergroup(64, 1032, k) == 8
+        assert g.supergroup(32, 8192, k) == 8 and g.supergroup(1, 0, k) == 8
+    nv = g.KERNEL_NVFP4
+    assert g.supergroup(32, 2048, nv) == 16 and g.supergroup(64, 512, nv) == 16
+    assert g.supergroup(31, 1024, nv) == 8 and g.supergroup(32, 2080, nv) == 8 and g.supergroup(32, 8192, nv) == 8
+    assert g.supergroup(4096, 64, g.KERNEL_BF16_SMALL) == 8
+    lib = g.load()
+    assert lib.gemm355_supergroup(0, 0, 8) == -g.ERR_INVALID_ARG
+    assert lib.gemm355_supergroup(0, 8, -1) == -g.ERR_INVALID_ARG
+    assert lib.gemm355_supergroup(4, 8, 8) == -g.ERR_INVALID_ARG
+    assert lib.gemm355_supergroup(-1, 8, 8) == -g.ERR_INVALID_ARG
+
+
 def test_force_supergroup_range():
     lib = g.load()
     for bad in (-1, 4097):

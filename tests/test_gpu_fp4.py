@@ -174,3 +174,51 @@ def test_k_half_step_tail_fused_epilogue():
     sig = _sigma(Aq, SFA, K) * _sigma(Bq, SFB, K)
     res = tolerance.check_fused(C.bits(), ref.reshape(M, N), z.reshape(M, N), K, g.ACT_GELU_TANH, sig)
     assert res, res
+
+
+# ---- dynamic tile order (gemm355_force_schedule) ------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 1024), (4352, 4104, 1024), (520, 776, 512), (2304, 2304, 256),
+                                   (300, 264, 256)])
+def test_dynamic_order_gives_the_static_result(M, N, K):
+    # Every tile is computed the same way whichever workgroup takes it, so
+    # the dynamic order must reproduce the static result bitwise. 4352 x 4104
+    # has 289 tiles: the second round's 33 tiles all sit on one XCD's share,
+    # so the other XCDs' workgroups take them from its counter. 520 x 776
+    # (12 tiles, a grid of 8) and 300 x 264 (4 tiles, a grid of 4: one
+    # counter) cover the small grids. Three dynamic launches in a row: a
+    # counter left uncleared would make later launches skip tiles (their C
+    # would keep the canary values).
+    need_gpu()
+    print("fp4 dynamic order", M, N, K, flush=True)
+    Aq, SFA = syn.fp4_operand(M, K, seed=M + N + 3)
+    Bq, SFB = syn.fp4_operand(N, K, seed=M + N + 4)
+    want = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+    try:
+        g.force_schedule(g.SCHEDULE_DYNAMIC)
+        for launch in range(3):
+            got = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+            bad = np.argwhere(got != want)
+            assert bad.size == 0, "launch %d: %d differ, first %s" % (launch, len(bad), bad[:5].tolist())
+    finally:
+        g.force_schedule(g.SCHEDULE_STATIC)
+    ms, ns = sample_positions(M, N, 500, seed=M)
+    sig = _sigma(Aq[:512], SFA[:512], K) * _sigma(Bq[:512], SFB[:512], K)
+    res = tolerance.check(want[ms, ns], oracle.gemm_nvfp4_nt_at(Aq, SFA, Bq, SFB, K, ms, ns), K, sig)
+    assert res, res
+
+
+def test_dynamic_order_leaves_other_calls_static():
+    # the fused and the K % 64 == 32 instances keep the static order: results
+    # with the option set equal those without it
+    need_gpu()
+    M, N, K = 520, 264, 96
+    Aq, SFA = syn.fp4_operand(M, K, seed=91)
+    Bq, SFB = syn.fp4_operand(N, K, seed=92)
+    want = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+    try:
+        g.force_schedule(g.SCHEDULE_DYNAMIC)
+        got = run_fp4(Aq, SFA, Bq, SFB, M, N, K)
+    finally:
+        g.force_schedule(g.SCHEDULE_STATIC)
+    assert np.array_equal(got, want)

@@ -58,13 +58,13 @@ def test_bf16_every_element(M, N, K):
     _check_all(got, oracle.gemm_bf16_nt(A, B), K, what=(M, N, K))
 
 
-def _checked_tiles(M, N, cus):
+def _checked_tiles(M, N, K, cus):
     """(tm, tn) of the tiles computed by the first and last workgroup of each
     XCD in every round, plus the last row, last column and corner tiles."""
     tm_n, tn_n = -(-M // TILE), -(-N // TILE)
     tiles = tm_n * tn_n
     grid = min(tiles, cus) & ~7
-    order_m, order_n = g.tile_order(tm_n, tn_n, 8)
+    order_m, order_n = g.tile_order(tm_n, tn_n, g.supergroup(tn_n, K))
     slots = g.schedule(tiles, grid)
     picked = set()
     for x in range(8):
@@ -88,7 +88,7 @@ def test_bf16_whole_tiles(M, N, K):
     A = syn.bf16_uniform(M, K, seed=syn.seed_for(cfg, 0) + 2)
     B = syn.bf16_uniform(N, K, seed=syn.seed_for(cfg, 0) + 3)
     got = _run(lambda c: g.gemm_bf16_nt(M, N, K, to_dev(A), to_dev(B), c), M, N)
-    tiles = _checked_tiles(M, N, cus)
+    tiles = _checked_tiles(M, N, K, cus)
     assert len(tiles) >= 64
     ms, ns = [], []
     for tm, tn in tiles:
