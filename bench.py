@@ -78,6 +78,7 @@ CONFIG_INDEX = {"bf16_256": 0, "bf16_4096": 1, "bf16_8192": 2, "bf16_8000": 3, "
 KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel<%d>", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel",
                "mx": "gemm355::mx::gemm_mxfp4_nt_kernel<-1>",
                "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel<%d>",
+               "bf16_small_long": "gemm355::bf16_small_long::gemm_bf16_nt_small_long_kernel<%d, 4>",
                "bf16_splitk": "gemm355::bf16_splitk::gemm_bf16_nt_splitk_kernel<%d>",
                "bf16_splitk_reduce": "gemm355::bf16_splitk::splitk_reduce_kernel<%d>"}
 EPILOGUE = {"bf16": -1, "bf16_gelu": 2}
@@ -94,7 +95,10 @@ def kernels_for(kind: str, M: int, N: int, K: int, compute_units: int = 256) -> 
     if instance == 3:
         names = [KERNEL_NAME["bf16_splitk"] % epi]
         return names + [KERNEL_NAME["bf16_splitk_reduce"] % epi] if splits > 1 else names
-    return [KERNEL_NAME["bf16_small" if instance == 2 else "bf16"] % epi]
+    if instance == 2:   # the 64 x 64 instance's long-K staging (same rule as the library's)
+        long_k = K >= 4096 and 2 * -(-M // 64) * -(-N // 64) >= compute_units
+        return [KERNEL_NAME["bf16_small_long" if long_k else "bf16_small"] % epi]
+    return [KERNEL_NAME["bf16"] % epi]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 

@@ -13,6 +13,7 @@
 #include "gemm355.h"
 #include "gemm_bf16.hpp"
 #include "gemm_bf16_small.hpp"
+#include "gemm_bf16_small_long.hpp"
 #include "gemm_bf16_splitk.hpp"
 #include "gemm_mxfp4.hpp"
 #include "gemm_fp4.hpp"
@@ -288,15 +289,34 @@ int launch_splitk(const Problem &p, const Bf16Plan &plan, void *workspace, void 
     return st;
 }
 
+// The 64 x 64 instance's B staging: 512-byte row segments (the _long kernel)
+// for K >= 4096 with at least half the compute units' worth of tiles.
+bool small_long_variant(int M, int N, int K, int cus)
+{
+    return K >= 4096 && 2 * ceil_div(M, 64) * ceil_div(N, 64) >= cus;
+}
+
 // The planned instance's kernels with epilogue EPI.
 template <int EPI>
 int launch_instance(const Bf16Plan &plan, const Problem &p, void *workspace, void *stream)
 {
+    int cus = 0;
+    const int rc = compute_units(&cus);
+    if (rc != GEMM355_OK)
+        return rc;
     if (plan.instance == 3)
         return launch_splitk<EPI>(p, plan, workspace, stream);
-    if (plan.instance == 2)
+    if (plan.instance == 2) {
+        // B in 512-byte row segments where HBM streaming decides: long K and
+        // at least half the units' worth of tiles (measured: 128 x 8192 x 8192
+        // 42.2 -> 38.7 us; with 64 tiles or K <= 2048 the per-step kernel is
+        // 3-10 % faster)
+        if (small_long_variant(p.M, p.N, p.K, cus))
+            return launch(gemm355::bf16_small_long::gemm_bf16_nt_small_long_kernel<EPI, 4>, KERNEL_BF16_SMALL, p,
+                          stream, gemm355::bf16_small_long::TM, gemm355::bf16_small_long::TN);
         return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel<EPI>, KERNEL_BF16_SMALL, p, stream,
                       gemm355::bf16_small::TM, gemm355::bf16_small::TN);
+    }
     return launch(gemm355::bf16::gemm_bf16_nt_kernel<EPI>, KERNEL_BF16, p, stream);
 }
 

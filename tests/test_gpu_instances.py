@@ -228,3 +228,63 @@ def test_workspace_too_small_is_rejected_without_launching():
     assert e.value.status == g.ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert np.all(C.bits() == 0x7FC1), "C written by a rejected call"
+
+
+# ---- the 64 x 64 instance's long-K staging (B in 512-byte row segments) -------
+# Taken when K >= 4096 and the 64 x 64 tiles number at least half the compute
+# units: ragged M and N, and K tails that end inside the last 4-step B unit.
+LONG_SHAPES = [(520, 1040, 4104), (136, 8200, 4160), (128, 8192, 8192), (264, 2056, 4352)]
+
+
+@pytest.mark.parametrize("M,N,K", LONG_SHAPES)
+def test_small_instance_long_k_matches_oracle(M, N, K):
+    need_gpu()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert K >= 4096 and 2 * (-(-M // 64)) * (-(-N // 64)) >= cus
+    print("small long-K", M, N, K, flush=True)
+    A = syn.bf16_uniform(M, K, seed=M + 5 * K)
+    B = syn.bf16_uniform(N, K, seed=N + 5 * K + 1)
+    try:
+        g.force_instance(g.INSTANCE_SMALL)
+        C = run_bf16(A, B, M, N, K)
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+    ms, ns = sample_positions(M, N, 4000, seed=M + N, tile=64)
+    res = tolerance.check(C[ms, ns], oracle.gemm_bf16_nt_at(A, B, ms, ns), K)
+    assert res, res
+
+
+@pytest.mark.parametrize("M,N,K", [(520, 1040, 4104), (136, 8200, 4160)])
+def test_small_instance_long_k_exact_every_element(M, N, K):
+    need_gpu()
+    A = syn.bf16_sixteenths(M, K, seed=M + 11)
+    B = syn.bf16_sixteenths(N, K, seed=N + 12)
+    try:
+        g.force_instance(g.INSTANCE_SMALL)
+        C = run_bf16(A, B, M, N, K)
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+    want = oracle.bf16_from_double(tolerance.bf16_bits_to_f64(A) @ tolerance.bf16_bits_to_f64(B).T)
+    assert np.array_equal(oracle.gemm_bf16_nt(A[:2], B), want[:2])
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+
+
+def test_small_instance_long_k_fused_epilogue():
+    need_gpu()
+    M, N, K = 264, 2056, 4352
+    A = syn.bf16_uniform(M, K, seed=21)
+    B = syn.bf16_uniform(N, K, seed=22)
+    bias = syn.bf16_uniform(1, N, seed=23, lo=-8.0, hi=8.0)[0]
+    C = GuardedC(M, N)
+    try:
+        g.force_instance(g.INSTANCE_SMALL)
+        g.gemm_bf16_nt_bias_act(M, N, K, to_dev(A), to_dev(B), to_dev(bias), g.ACT_GELU_TANH, C.view)
+        torch.cuda.synchronize()
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+    assert C.guards_intact()
+    ms, ns = sample_positions(M, N, 3000, seed=24, tile=64)
+    ref, z = oracle.gemm_bf16_nt_bias_act_at(A, B, bias, g.ACT_GELU_TANH, ms, ns, with_z=True)
+    res = tolerance.check_fused(C.bits()[ms, ns], ref, z, K, g.ACT_GELU_TANH)
+    assert res, res
