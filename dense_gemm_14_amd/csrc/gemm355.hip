@@ -488,14 +488,14 @@ int fp4_launch(const Problem &p, int act, void *stream)
 {
     using namespace gemm355;
     if (!FUSED && !KTAIL && g_schedule.load(std::memory_order_relaxed) == 1)
-        return launch(fp4::gemm_nvfp4_nt_kernel<EPI_PLAIN, false, true>, KERNEL_NVFP4, p, stream);
+        return launch(fp4::gemm_nvfp4_nt_kernel<EPI_PLAIN, false, true>, KERNEL_NVFP4, p, stream, BM, BN, fp4::THREADS_FP4);
     if (!FUSED)
-        return launch(fp4::gemm_nvfp4_nt_kernel<EPI_PLAIN, KTAIL>, KERNEL_NVFP4, p, stream);
+        return launch(fp4::gemm_nvfp4_nt_kernel<EPI_PLAIN, KTAIL>, KERNEL_NVFP4, p, stream, BM, BN, fp4::THREADS_FP4);
     if (act == GEMM355_ACT_RELU)
-        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_RELU, KTAIL>, KERNEL_NVFP4, p, stream);
+        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_RELU, KTAIL>, KERNEL_NVFP4, p, stream, BM, BN, fp4::THREADS_FP4);
     if (act == GEMM355_ACT_GELU_TANH)
-        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_GELU_TANH, KTAIL>, KERNEL_NVFP4, p, stream);
-    return launch(fp4::gemm_nvfp4_nt_kernel<ACT_NONE, KTAIL>, KERNEL_NVFP4, p, stream);
+        return launch(fp4::gemm_nvfp4_nt_kernel<ACT_GELU_TANH, KTAIL>, KERNEL_NVFP4, p, stream, BM, BN, fp4::THREADS_FP4);
+    return launch(fp4::gemm_nvfp4_nt_kernel<ACT_NONE, KTAIL>, KERNEL_NVFP4, p, stream, BM, BN, fp4::THREADS_FP4);
 }
 
 // Shared by gemm_nvfp4_nt and gemm_nvfp4_nt_bias_act: validation, launch.
