@@ -280,7 +280,7 @@ int launch_splitk(const Problem &p, const Bf16Plan &plan, void *workspace, void 
     if (sp.splits > 1)
         sp.ws = static_cast<float *>(workspace);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    int st = launch_kernel(sk::gemm_bf16_nt_splitk_kernel<EPI>, (unsigned)items, (unsigned)gemm355::THREADS, sp, s);
+    int st = launch_kernel(sk::gemm_bf16_nt_splitk_kernel<EPI>, (unsigned)items, (unsigned)sk::THREADS_SK, sp, s);
     if (st == GEMM355_OK && sp.splits > 1) {   // one split stores C itself
         const int64_t outs = int64_t(p.M) * (p.N / 8);
         st = launch_kernel(sk::splitk_reduce_kernel<EPI>, (unsigned)ceil_div(outs, sk::REDUCE_THREADS),

@@ -11,20 +11,24 @@
 // half as much per unit (128 + 128 rows x K / 4) for the same multiply-adds;
 // the partials cost 64 KiB per workgroup.
 //
-//   * 4 waves in 2 x 2, each wave 64 x 64 = 4 x 4 blocks of
-//     v_mfma_f32_16x16x32_bf16 (64 accumulation registers per lane).
+//   * 8 waves in 2 x 4 (two per SIMD), each wave 64 x 32 = 4 x 2 blocks of
+//     v_mfma_f32_16x16x32_bf16 (32 accumulation registers per lane). Eight
+//     waves rather than four because the transfer is the bound and more
+//     waves issuing copies move more: a probe streaming these tiles' operand
+//     traffic alone (LDS-DMA, split 4 of 128 x 8192 x 8192) takes 34.2 us
+//     with 4 waves and 28.5 us with 8.
 //   * K advances 64 per step; a unit is the A tile or the B tile of one step
 //     (128 rows of 128 bytes, same chunk swizzle as the other BF16 kernels,
 //     16 KiB). LDS holds a ring of 3 A units and a ring of 7 B units. Waves 0
-//     and 1 copy A rows 0..63 and 64..127, waves 2 and 3 the same rows of B
-//     (eight 1 KiB LDS-DMA copies per wave and step, four per m0 through the
+//     to 3 copy A rows 32 w .. 32 w + 31, waves 4 to 7 the same rows of B
+//     (four 1 KiB LDS-DMA copies per wave and step under one m0, through the
 //     instruction offset), so B, which streams from HBM, is requested five
 //     steps ahead and A, which stays in L2, one step ahead.
 //   * Step s: copy step s + stages - 1 of the wave's operand into the slot of
 //     step s - 1 (read by every wave before the previous barrier), wait until
-//     this wave's copies of step s + 1 have landed, one barrier, then the 32
+//     this wave's copies of step s + 1 have landed, one barrier, then the 16
 //     matrix instructions of step s on fragments read during step s - 1, with
-//     the 16 fragment reads of step s + 1 interleaved.
+//     the 12 fragment reads of step s + 1 interleaved.
 //   * The result is deterministic: each split sums its K range in a fixed
 //     order and the reduction adds the splits in index order.
 #pragma once
@@ -45,13 +49,14 @@ constexpr int B_UNIT = TN * ROW_BYTES;       // B tile of one step: 16 KiB
 constexpr int A_STAGES = 3;                  // A ring (its rows come from L2): one step ahead
 constexpr int B_STAGES = 7;                  // B ring (its rows stream from HBM): five steps ahead
 constexpr int LDS_BYTES = A_STAGES * A_UNIT + B_STAGES * B_UNIT;
-constexpr int COPIES = 8;                    // 1 KiB copies per copying wave per step
+constexpr int COPIES = 4;                    // 1 KiB copies per wave per step
+constexpr int THREADS_SK = 512;              // 8 waves, two per SIMD
 constexpr int TILE_FLOATS = TM * TN;         // one partial tile
 constexpr int MAX_SPLITS = 8;
 constexpr int REDUCE_THREADS = 256;
 
 static_assert(LDS_BYTES <= 163840, "LDS rings exceed the 160 KiB of a gfx950 workgroup");
-static_assert(TM == 128 && TN == 128 && THREADS == 256, "the copy map assumes 128 x 128 tiles and 4 waves");
+static_assert(TM == 128 && TN == 128 && THREADS_SK == 512, "the copy map assumes 128 x 128 tiles and 8 waves");
 static_assert(COPIES * (B_STAGES - 1) <= 63, "vmcnt counts at most 63 outstanding operations");
 
 // Kernel arguments. Work item w = tile * splits + split; tile = tm * tiles_n + tn.
@@ -107,9 +112,9 @@ template <int N>
 __device__ inline void wait_copies_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Copy duty is split by operand: waves 0 and 1 copy the A tile (64 rows each)
+// Copy duty is split by operand: waves 0 to 3 copy the A tile (32 rows each)
 // through a short ring, since the few A rows of a skinny problem stay in L2;
-// waves 2 and 3 copy the B tile through a deep ring, since B streams from
+// waves 4 to 7 copy the B tile through a deep ring, since B streams from
 // HBM, whose loaded latency is several microseconds: a wave's copies
 // complete in issue order, so a wave copying both operands would wait for its
 // older B copies whenever it waits for A, and B's prefetch depth would shrink
@@ -117,7 +122,7 @@ __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "m
 // EPI: EPI_PLAIN, or the activation of the fused epilogue, applied here with
 // one split (with several, by the reduction).
 template <int EPI>
-__global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(THREADS_SK, THREADS_SK), amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_nt_splitk_kernel(SplitProblem p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
@@ -127,12 +132,12 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1;   // 64-row half of the tile (A rows)
-    const int wn = wave >> 1;  // 64-column half (B rows)
+    const int wn = wave >> 1;  // 32-column quarter (B rows)
     const int l16 = lane & 15;
     const int grp = lane >> 4;
     const int K = p.K;
-    const bool copies_b = wave >= 2;              // uniform per wave
-    const int half = wave & 1;                    // which 64 rows of its operand this wave copies
+    const bool copies_b = wave >= 4;              // uniform per wave
+    const int quarter = wave & 3;                 // which 32 rows of its operand this wave copies
 
     const int item = blockIdx.x;
     const int tile = item / p.splits;
@@ -148,7 +153,7 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
     // the step) or 4 + grp (second half); blocks start at multiples of 16 rows.
     const int kofs[2] = {swizzle(l16, grp) << 4, swizzle(l16, 4 + grp) << 4};
     const int a_frag = (64 * wm + l16) * ROW_BYTES;
-    const int b_frag = A_STAGES * A_UNIT + (64 * wn + l16) * ROW_BYTES;
+    const int b_frag = A_STAGES * A_UNIT + (32 * wn + l16) * ROW_BYTES;
     const int copy_row = lane >> 3;
 
     const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
@@ -156,15 +161,15 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
         ? rsrc_words(static_cast<const uint8_t *>(p.b) - SHIFT, (unsigned)p.N * (unsigned)K * 2u + SHIFT)
         : rsrc_words(static_cast<const uint8_t *>(p.a) - SHIFT, (unsigned)p.M * (unsigned)K * 2u + SHIFT);
     const int stages = copies_b ? B_STAGES : A_STAGES;
-    const unsigned ring = lds_base + (unsigned)(copies_b ? A_STAGES * A_UNIT : 0) + (unsigned)(half * 8192);
+    const unsigned ring = lds_base + (unsigned)(copies_b ? A_STAGES * A_UNIT : 0) + (unsigned)(quarter * 4096);
 
-    // Copy t (0..7): rows 64 half + 8 t .. + 7 of this wave's operand tile;
+    // Copy t (0..3): rows 32 quarter + 8 t .. + 7 of this wave's operand tile;
     // lane i fills position i & 7 of row i / 8.
     unsigned off[COPIES];
     int chunk_k[2];
 #pragma unroll
     for (int t = 0; t < COPIES; ++t) {
-        const int row = 64 * half + 8 * t + copy_row;
+        const int row = 32 * quarter + 8 * t + copy_row;
         const int c = swizzle(row, lane & 7);
         if (t < 2)
             chunk_k[t] = 8 * c;   // depends on the block's parity only
@@ -182,7 +187,6 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
         for (int t = 0; t < COPIES; ++t)
             v[t] = in && k0 + chunk_k[t & 1] < K ? off[t] + (unsigned)(k0 * 2) : OOB_SHIFTED;
         copy_four(rsrc, __builtin_amdgcn_readfirstlane(slot), v[0], v[1], v[2], v[3]);
-        copy_four(rsrc, __builtin_amdgcn_readfirstlane(slot + 4096u), v[4], v[5], v[6], v[7]);
     };
     // This wave's copies of the next step to be read have landed.
     auto wait_next = [&]() {
@@ -195,34 +199,34 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
     // fused epilogue with one split: bias[n .. n + 3] of this lane's columns
     // in block column j (requested before any copy, so landed by the first
     // step's wait; zeros past N and without a bias)
-    u32x2 bias_w[4];
+    u32x2 bias_w[2];
     if constexpr (FUSED) {
         const __amdgpu_buffer_rsrc_t rbias = make_rsrc(p.bias, p.bias && p.splits == 1 ? (unsigned)p.N * 2u : 0u);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = tn * TN + 64 * wn + 16 * j + 4 * grp;
+        for (int j = 0; j < 2; ++j) {
+            const int n = tn * TN + 32 * wn + 16 * j + 4 * grp;
             bias_w[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rbias, n < p.N ? n * 2 : OOB, 0, 0));
         }
     }
 
-    f32x4 acc[4][4];
-    bf16x8 fa[2][2][4], fb[2][2][4];   // [buffer][half][block]
-    // Read q (0..15) of local step ls: half q / 8; A block q % 8 for q % 8 < 4,
-    // else B block q % 8 - 4.
+    f32x4 acc[4][2];
+    bf16x8 fa[2][2][4], fb[2][2][2];   // [buffer][half][block]
+    // Read q (0..11) of local step ls: half q / 6; A block q % 6 for q % 6 < 4,
+    // else B block q % 6 - 4.
     auto read = [&](int ls, int buf, int q) {
-        const int h = q >> 3, r = q & 7, blk = r & 3;
+        const int h = q / 6, r = q % 6, blk = r & 3;
         if (r < 4)
             fa[buf][h][blk] = *reinterpret_cast<const bf16x8 *>(lds + (ls % A_STAGES) * A_UNIT + a_frag +
                                                                 blk * 16 * ROW_BYTES + kofs[h]);
         else
-            fb[buf][h][blk] = *reinterpret_cast<const bf16x8 *>(lds + (ls % B_STAGES) * B_UNIT + b_frag +
-                                                                blk * 16 * ROW_BYTES + kofs[h]);
+            fb[buf][h][r - 4] = *reinterpret_cast<const bf16x8 *>(lds + (ls % B_STAGES) * B_UNIT + b_frag +
+                                                                  (r - 4) * 16 * ROW_BYTES + kofs[h]);
     };
-    // Matrix instruction t (0..31): half t / 16, block ((t / 4) % 4, t % 4).
+    // Matrix instruction t (0..15): half t / 8, block ((t / 2) % 4, t % 2).
     // B rows are the first operand, so each 16 x 16 result arrives transposed
     // (lane (l16, grp) holds C[16 i + l16][16 j + 4 grp .. + 3]).
     auto mma = [&](int buf, int t, bool first) {
-        const int h = t >> 4, i = (t >> 2) & 3, j = t & 3;
+        const int h = t >> 3, i = (t >> 1) & 3, j = t & 1;
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][h][j], fa[buf][h][i],
                                                            (first && h == 0) ? f32x4{} : acc[i][j], 0, 0, 0);
     };
@@ -233,7 +237,7 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
     wait_next();
     lds_barrier();
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
+    for (int q = 0; q < 12; ++q)
         read(0, 0, q);
 
     auto step = [&](int ls, auto buf_c, bool first) {
@@ -246,10 +250,10 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
         wait_next();
         lds_barrier();
         SCHED_FENCE();
-        static_for<32>([&](auto tc) {
+        static_for<16>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             mma(buf, t, first);
-            if constexpr (t < 16)
+            if constexpr (t < 12)
                 read(ls + 1, buf ^ 1, t);
             SCHED_VALU_ONLY();
         });
@@ -259,7 +263,7 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
                 acc[i][j] = f32x4{};
     } else {
         step(0, Int<0>{}, true);
@@ -273,7 +277,7 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
     }
 
     // Lane (l16, grp) of block (i, j) holds row 64 wm + 16 i + l16, columns
-    // 64 wn + 16 j + 4 grp .. + 3 of the tile.
+    // 32 wn + 16 j + 4 grp .. + 3 of the tile.
     if (p.splits == 1) {
         // One split: the tile is final; round to BF16 and store it into C
         // (8 bytes per lane and block; rows past M and columns past N masked,
@@ -282,8 +286,8 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int m = tm * TM + 64 * wm + 16 * i + l16, n = tn * TN + 64 * wn + 16 * j + 4 * grp;
+            for (int j = 0; j < 2; ++j) {
+                const int m = tm * TM + 64 * wm + 16 * i + l16, n = tn * TN + 32 * wn + 16 * j + 4 * grp;
                 const int off = (m < p.M && n < p.N) ? (m * p.N + n) * 2 : OOB;
                 f32x4 x = acc[i][j];
                 if constexpr (FUSED)
@@ -296,8 +300,8 @@ void gemm_bf16_nt_splitk_kernel(SplitProblem p)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 64 * wm + 16 * i + l16, c = 64 * wn + 16 * j + 4 * grp;
+            for (int j = 0; j < 2; ++j) {
+                const int r = 64 * wm + 16 * i + l16, c = 32 * wn + 16 * j + 4 * grp;
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw, (r * TN + c) * 4, 0, 0);
             }
     }
