@@ -102,15 +102,45 @@ def kernels_for(kind: str, M: int, N: int, K: int, compute_units: int = 256) -> 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
-    """SHA-256 over the HIP sources; counter figures are used only if it matches."""
+# the source file of each kernel family; a family's counters also depend on
+# the shared helpers and the tile order
+KERNEL_SOURCE = {"bf16": "gemm_bf16.hpp", "bf16_small": "gemm_bf16_small.hpp",
+                 "bf16_small_long": "gemm_bf16_small_long.hpp", "bf16_splitk": "gemm_bf16_splitk.hpp",
+                 "fp4": "gemm_fp4.hpp", "mx": "gemm_mxfp4.hpp"}
+SHARED_SOURCES = ("common.hpp", "schedule.hpp")
+
+
+def dominant_family(workload: str) -> str:
+    """Kernel family (KERNEL_SOURCE key) of the first kernel the workload launches."""
+    kind, M, N, K = WORKLOADS[workload]
+    first = kernels_for(kind, M, N, K)[0]
+    for fam in ("bf16_small_long", "bf16_small", "bf16_splitk", "fp4", "mx"):
+        if KERNEL_NAME[fam].split("<")[0] in first:
+            return fam
+    return "bf16"
+
+
+def kernel_source_hash(workload: str) -> str:
+    """SHA-256 over the dominant kernel's source and the shared headers;
+    counter figures are used only if it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_14_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in (KERNEL_SOURCE[dominant_family(workload)],) + SHARED_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def launch_supergroup(workload: str) -> int:
+    """Band width of the tile order the library uses for the workload's kernel."""
+    import dense_gemm_14_amd as g
+    kind, M, N, K = WORKLOADS[workload]
+    fam = dominant_family(workload)
+    tile = {"bf16_small": 64, "bf16_small_long": 64, "bf16_splitk": 128}.get(fam, 256)
+    kernel = {"fp4": g.KERNEL_NVFP4, "mx": g.KERNEL_MXFP4, "bf16_small": g.KERNEL_BF16_SMALL,
+              "bf16_small_long": g.KERNEL_BF16_SMALL}.get(fam, g.KERNEL_BF16)
+    return g.supergroup(-(-N // tile), K, kernel)
 
 
 def set_bytes(kind, M, N, K):
@@ -167,9 +197,10 @@ def launcher(kind, M, N, K, stream):
 def read_traffic(workload: str):
     """L2-egress bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by a
     plain copy of known size) from the committed counter summary, or None when
-    it was taken from other kernel sources. These counters count the bytes L2
-    requests from the fabric, which include hits in the 256 MiB last-level
-    cache, so they bound the HBM bytes from above."""
+    it was taken from another version of the kernel's source or with another
+    tile-order band width. These counters count the bytes L2 requests from the
+    fabric, which include hits in the 256 MiB last-level cache, so they bound
+    the HBM bytes from above."""
     path = os.path.join(PROFILE_DIR, "traffic_%s.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -178,7 +209,9 @@ def read_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_source_sha256") != kernel_source_hash(workload):
+        return None
+    if fields.get("supergroup") != str(launch_supergroup(workload)):
         return None
     try:
         return float(fields["l2_egress_bytes_per_launch"])
