@@ -84,7 +84,7 @@ std::atomic<int> g_bf16_instance{0};
 // (M = 64 .. 512, N = 1024 .. 8192, K = 2048 .. 8192); only their ratios
 // decide.
 constexpr double kStep64 = 0.27;        // one K step of a 64 x 64 tile
-constexpr double kStep128 = 0.70;       // one K step of a 128 x 128 tile
+constexpr double kStep128 = 0.56;       // one K step of a 128 x 128 tile (8 waves)
 constexpr double kLaunchFixed = 3.0;    // prologue, epilogue, launch
 constexpr double kReduceFixed = 3.0;    // the reduction's own launch
 constexpr double kHbmBytesPerUs = 4.5e6;
