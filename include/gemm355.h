@@ -18,7 +18,8 @@
  *    allocates no memory, keeps no per-call state and never synchronises: it
  *    enqueues the work on `stream` and returns. The only scratch memory, the
  *    FP32 partials of a split K, is a workspace the caller passes to the
- *    *_ws entry points. `stream` is a hipStream_t passed as void*; NULL means
+ *    *_ws entry points, or, for gemm_bf16_nt_noalloc only, a fixed static
+ *    device array. `stream` is a hipStream_t passed as void*; NULL means
  *    the default (null) stream.
  *  - Arrays are dense, row-major, with no padding between rows (the leading
  *    dimension of A and B is K, that of C is N). C must not overlap any input.
@@ -33,8 +34,12 @@
  *    the caller's next synchronisation, as usual for HIP.
  *  - Calls are thread-safe: the library holds no mutable state apart from a
  *    per-device cache of the compute-unit count, filled once under a lock,
- *    and the overrides set by gemm355_force_instance and
- *    gemm355_force_supergroup. Calls may be captured into HIP graphs.
+ *    the overrides set by gemm355_force_instance, gemm355_force_supergroup
+ *    and gemm355_force_schedule (process-wide diagnostics), and two static
+ *    device arrays that only opt-in paths use: the scratch of
+ *    gemm_bf16_nt_noalloc and the tile counters of the dynamic tile order
+ *    (gemm355_force_schedule(1)); calls that use either and overlap on one
+ *    GPU race. Calls may be captured into HIP graphs.
  */
 #ifndef GEMM355_H
 #define GEMM355_H
