@@ -288,3 +288,41 @@ def test_small_instance_long_k_fused_epilogue():
     ref, z = oracle.gemm_bf16_nt_bias_act_at(A, B, bias, g.ACT_GELU_TANH, ms, ns, with_z=True)
     res = tolerance.check_fused(C.bits()[ms, ns], ref, z, K, g.ACT_GELU_TANH)
     assert res, res
+
+
+# The split instance on one row of 128 x 128 tiles (M <= 128), with and without
+# a workspace, ragged N and K tails. Multiples of 1/16 make every partial sum
+# exact, so every element must equal the correctly rounded sum whatever the
+# split.
+@pytest.mark.parametrize("M,N,K,ws", [(100, 1032, 4104, True), (128, 264, 8200, True), (7, 136, 1544, True),
+                                      (128, 1032, 4104, False), (33, 72, 72, True)])
+def test_one_tile_row_split_exact_every_element(M, N, K, ws):
+    need_gpu()
+    g.force_instance(g.INSTANCE_SPLITK)
+    try:
+        A = syn.bf16_sixteenths(M, K, seed=M + K)
+        B = syn.bf16_sixteenths(N, K, seed=N + K)
+        C = run_bf16(A, B, M, N, K, ws=ws)
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+    want = oracle.bf16_from_double(tolerance.bf16_bits_to_f64(A) @ tolerance.bf16_bits_to_f64(B).T)
+    assert np.array_equal(oracle.gemm_bf16_nt(A[:2], B), want[:2])
+    bad = np.argwhere(C != want)
+    assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+
+
+def test_one_tile_row_split_workload_every_element():
+    # The skinny workload shape, 128 x 8192 x 8192, through the split instance
+    # with a workspace (four splits of 32 K steps): all of C against the oracle
+    # on uniform inputs (about 1.5 s of oracle time).
+    need_gpu()
+    M, N, K = 128, 8192, 8192
+    A = syn.bf16_uniform(M, K, seed=syn.seed_for(3, 0) + 21)
+    B = syn.bf16_uniform(N, K, seed=syn.seed_for(3, 0) + 22)
+    g.force_instance(g.INSTANCE_SPLITK)
+    try:
+        C = run_bf16(A, B, M, N, K, ws=True)
+    finally:
+        g.force_instance(g.INSTANCE_AUTO)
+    res = tolerance.check(C, oracle.gemm_bf16_nt(A, B), K)
+    assert res and res.n_bad == 0, res
