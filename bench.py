@@ -36,7 +36,9 @@ CPU time at 8192^3) and adds the result to the line.
 Other workloads (--workload): bf16_4096, bf16_8000, bf16_skinny (128 x 8192 x
 8192, HBM roofline), bf16_256, fp4_8192 (E2M1 + E4M3 per 16, decoded to FP16),
 bf16_gelu_8192 (bias + GELU fused), mx_8192 (E2M1 + E8M0 per 32 on the scaled
-FP4 matrix instructions, against the FP4 peak).
+FP4 matrix instructions, against the FP4 peak), fp4_ws_8192 (the NVFP4 product
+through gemm_nvfp4_nt_ws: decoded once into a BF16 workspace allocated before
+the timing, then the BF16 kernels).
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -71,16 +73,20 @@ WORKLOADS = {
     "bf16_gelu_8192": ("bf16_gelu", 8192, 8192, 8192),
     # microscaled FP4 (E2M1 codes, E8M0 scale per 32) on the scaled matrix instructions
     "mx_8192": ("mx", 8192, 8192, 8192),
+    # the NVFP4 product through gemm_nvfp4_nt_ws: decoded once into a BF16
+    # workspace (allocated before timing), then the BF16 kernels
+    "fp4_ws_8192": ("fp4_ws", 8192, 8192, 8192),
 }
 CONFIG_INDEX = {"bf16_256": 0, "bf16_4096": 1, "bf16_8192": 2, "bf16_8000": 3, "bf16_skinny": 3,
-                "fp4_8192": 4, "bf16_gelu_8192": 2, "mx_8192": 4}
+                "fp4_8192": 4, "bf16_gelu_8192": 2, "mx_8192": 4, "fp4_ws_8192": 4}
 # BF16 kernels are templates over the epilogue: -1 plain, 2 bias + tanh-form GELU
 KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel<%d>", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel",
                "mx": "gemm355::mx::gemm_mxfp4_nt_kernel<-1>",
                "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel<%d>",
                "bf16_small_long": "gemm355::bf16_small_long::gemm_bf16_nt_small_long_kernel<%d, 4>",
                "bf16_splitk": "gemm355::bf16_splitk::gemm_bf16_nt_splitk_kernel<%d>",
-               "bf16_splitk_reduce": "gemm355::bf16_splitk::splitk_reduce_kernel<%d>"}
+               "bf16_splitk_reduce": "gemm355::bf16_splitk::splitk_reduce_kernel<%d>",
+               "fp4_decode": "gemm355::fp4::decode_nvfp4_bf16_kernel"}
 EPILOGUE = {"bf16": -1, "bf16_gelu": 2}
 
 
@@ -90,6 +96,10 @@ def kernels_for(kind: str, M: int, N: int, K: int, compute_units: int = 256) -> 
     if kind in ("fp4", "mx"):
         return [KERNEL_NAME[kind]]
     import dense_gemm_14_amd as g
+    if kind == "fp4_ws":
+        if not g.nvfp4_plan(M, N, K, compute_units)[0]:
+            return [KERNEL_NAME["fp4"]]
+        return [KERNEL_NAME["fp4_decode"]] * 2 + kernels_for("bf16", M, N, K, compute_units)
     instance, splits = g.bf16_plan(M, N, K, compute_units)
     epi = EPILOGUE[kind]
     if instance == 3:
@@ -173,7 +183,7 @@ def make_sets(kind, M, N, K, n_sets, cfg):
                 bias = syn.bf16_uniform(1, N, seed + 900, lo=-32.0, hi=32.0)[0]
                 ops = (A, B, torch.from_numpy(bias.view(np.int16)).cuda())
         else:
-            operand = syn.mxfp4_operand if kind == "mx" else syn.fp4_operand
+            operand = syn.mxfp4_operand if kind == "mx" else syn.fp4_operand   # fp4 and fp4_ws
             Aq, SFA = operand(M, K, seed)
             Bq, SFB = operand(N, K, seed + 500)
             ops = tuple(torch.from_numpy(x).cuda() for x in (Aq, SFA, Bq, SFB))
@@ -191,6 +201,11 @@ def launcher(kind, M, N, K, stream):
                                                       stream=stream)
     if kind == "mx":
         return lambda ops, C: g.gemm_mxfp4_nt(M, N, K, *ops, C, stream=stream)
+    if kind == "fp4_ws":
+        import torch
+        nbytes = g.nvfp4_workspace_size(M, N, K)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda") if nbytes else None
+        return lambda ops, C: g.gemm_nvfp4_nt_ws(M, N, K, *ops, C, ws, nbytes, stream=stream)
     return lambda ops, C: g.gemm_nvfp4_nt(M, N, K, *ops, C, stream=stream)
 
 
@@ -329,7 +344,7 @@ def parity_sigma(kind, host, K):
     import numpy as np
     import oracle
     from tests import tolerance
-    if kind == "fp4":
+    if kind in ("fp4", "fp4_ws"):
         sub = slice(0, 256)
         return (tolerance.sigma_of(oracle.decode_nvfp4(host[0][sub], host[1][sub], K)) *
                 tolerance.sigma_of(oracle.decode_nvfp4(host[2][sub], host[3][sub], K)))
@@ -527,7 +542,7 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     # NVFP4 operands are decoded to FP16 for the MFMA; MX operands enter it as FP4
-    dtype = {"fp4": "fp16", "mx": "fp4"}.get(kind, "bf16")
+    dtype = {"fp4": "fp16", "mx": "fp4"}.get(kind, "bf16")   # fp4_ws: BF16 matrix instructions
     traffic = read_traffic(args.workload)
     alg_bytes = algorithmic_bytes(kind, M, N, K)
     ridge = PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
@@ -562,7 +577,8 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp4": "fp4(e2m1+e4m3)->fp16", "mx": "fp4(e2m1+e8m0)"}.get(kind, "bf16"),
+        "dtype": {"fp4": "fp4(e2m1+e4m3)->fp16", "mx": "fp4(e2m1+e8m0)",
+                  "fp4_ws": "fp4(e2m1+e4m3)->bf16 (decoded once)"}.get(kind, "bf16"),
         "data": "synthetic",
         "config": {"workload": "%s_nt_%dx%dx%d" % (kind, M, N, K), "M": M, "N": N, "K": K,
                    "rotation_sets": n_sets, "footprint_MiB": round(n_sets * per_set / 2 ** 20, 1),

@@ -56,6 +56,9 @@ KERNEL_BF16 = 0     # kernels of the supergroup rule (gemm355_supergroup)
 KERNEL_NVFP4 = 1
 KERNEL_MXFP4 = 2
 KERNEL_BF16_SMALL = 3
+FP4_PATH_AUTO = 0    # gemm_nvfp4_nt_ws: decode first by shape (gemm355_force_fp4_path)
+FP4_PATH_STAGING = 1  # always the kernel that decodes while staging
+FP4_PATH_DECODE_FIRST = 2  # always decode into the workspace, then the BF16 product
 SCHEDULE_STATIC = 0  # the NVFP4 kernel's tile order (gemm355_force_schedule)
 SCHEDULE_DYNAMIC = 1
 INSTANCE_SPLITK = 3  # 128 x 128 output tiles; with a workspace (the *_ws calls) K split over workgroups
@@ -99,6 +102,14 @@ def load() -> ctypes.CDLL:
     lib.gemm_nvfp4_nt.restype = i
     lib.gemm_nvfp4_nt_bias_act.argtypes = [i, i, i, p, p, p, p, p, i, p, p]
     lib.gemm_nvfp4_nt_bias_act.restype = i
+    lib.gemm_nvfp4_nt_ws.argtypes = [i, i, i, p, p, p, p, p, p, sz, p]
+    lib.gemm_nvfp4_nt_ws.restype = i
+    lib.gemm_nvfp4_nt_workspace_size.argtypes = [i, i, i, ctypes.POINTER(sz)]
+    lib.gemm_nvfp4_nt_workspace_size.restype = i
+    lib.gemm355_nvfp4_plan.argtypes = [i, i, i, i, p, p]
+    lib.gemm355_nvfp4_plan.restype = i
+    lib.gemm355_force_fp4_path.argtypes = [i]
+    lib.gemm355_force_fp4_path.restype = i
     lib.gemm_mxfp4_nt.argtypes = [i, i, i, p, p, p, p, p, p]
     lib.gemm_mxfp4_nt.restype = i
     lib.gemm_mxfp4_nt_bias_act.argtypes = [i, i, i, p, p, p, p, p, i, p, p]
@@ -273,6 +284,47 @@ def gemm_nvfp4_nt(M: int, N: int, K: int, Aq, SFA, Bq, SFB, C, stream=None) -> N
     sfb = _addr(SFB, N * K // 16 if nz else 0, "SFB")
     c = _addr(C, M * N * 2 if nz else 0, "C")
     _check(lib.gemm_nvfp4_nt(M, N, K, aq, sfa, bq, sfb, c, _stream(stream)), "gemm_nvfp4_nt")
+
+
+def gemm_nvfp4_nt_ws(M: int, N: int, K: int, Aq, SFA, Bq, SFB, C, workspace, workspace_bytes=None,
+                     stream=None) -> None:
+    """gemm_nvfp4_nt with a caller-owned workspace (a device tensor of at least
+    nvfp4_workspace_size(M, N, K) bytes, or None when that is 0): large
+    products decode each operand once into BF16 there and run the BF16 core."""
+    lib = load()
+    M, N, K = int(M), int(N), int(K)
+    nz = M > 0 and N > 0
+    aq = _addr(Aq, M * K // 2 if nz else 0, "Aq")
+    sfa = _addr(SFA, M * K // 16 if nz else 0, "SFA")
+    bq = _addr(Bq, N * K // 2 if nz else 0, "Bq")
+    sfb = _addr(SFB, N * K // 16 if nz else 0, "SFB")
+    c = _addr(C, M * N * 2 if nz else 0, "C")
+    w, nb = _workspace(workspace, workspace_bytes)
+    _check(lib.gemm_nvfp4_nt_ws(M, N, K, aq, sfa, bq, sfb, c, w, nb, _stream(stream)), "gemm_nvfp4_nt_ws")
+
+
+def nvfp4_workspace_size(M: int, N: int, K: int) -> int:
+    """Workspace bytes gemm_nvfp4_nt_ws uses for this shape on the current device."""
+    out = ctypes.c_size_t(0)
+    _check(load().gemm_nvfp4_nt_workspace_size(int(M), int(N), int(K), ctypes.byref(out)),
+           "gemm_nvfp4_nt_workspace_size")
+    return out.value
+
+
+def nvfp4_plan(M: int, N: int, K: int, compute_units: int):
+    """(decode_first, workspace_bytes) of gemm_nvfp4_nt_ws on a device with
+    `compute_units` compute units; host only."""
+    d = ctypes.c_int(0)
+    nb = ctypes.c_size_t(0)
+    _check(load().gemm355_nvfp4_plan(int(M), int(N), int(K), int(compute_units), ctypes.byref(d), ctypes.byref(nb)),
+           "gemm355_nvfp4_plan")
+    return bool(d.value), nb.value
+
+
+def force_fp4_path(path: int) -> None:
+    """gemm_nvfp4_nt_ws's path for the whole process: FP4_PATH_AUTO (default),
+    FP4_PATH_STAGING or FP4_PATH_DECODE_FIRST (a diagnostic)."""
+    _check(load().gemm355_force_fp4_path(int(path)), "gemm355_force_fp4_path")
 
 
 def gemm_nvfp4_nt_bias_act(M: int, N: int, K: int, Aq, SFA, Bq, SFB, bias, activation: int, C,

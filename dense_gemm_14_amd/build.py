@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libgemm355.so")
 SOURCES = [os.path.join(CSRC, "gemm355.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("common.hpp", "gemm_bf16.hpp", "gemm_bf16_small.hpp", "gemm_bf16_small_long.hpp", "gemm_bf16_splitk.hpp",
-                                           "gemm_fp4.hpp", "gemm_mxfp4.hpp", "schedule.hpp")] + \
+                                           "gemm_fp4.hpp", "fp4_decode.hpp", "gemm_mxfp4.hpp", "schedule.hpp")] + \
     [os.path.join(INCLUDE, "gemm355.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

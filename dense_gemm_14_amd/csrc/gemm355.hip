@@ -17,6 +17,7 @@
 #include "gemm_bf16_splitk.hpp"
 #include "gemm_mxfp4.hpp"
 #include "gemm_fp4.hpp"
+#include "fp4_decode.hpp"
 #include "schedule.hpp"
 
 // Scratch of gemm_bf16_nt_noalloc: the split-K partials of the largest plan
@@ -67,6 +68,9 @@ std::atomic<int> g_supergroup{0};
 // Tile order of the NVFP4 kernel: 0 static, 1 dynamic (a measurement option;
 // set through gemm355_force_schedule).
 std::atomic<int> g_schedule{0};
+// gemm_nvfp4_nt_ws's path: 0 by shape, 1 always the staging-decode kernel,
+// 2 always decode first (set through gemm355_force_fp4_path).
+std::atomic<int> g_fp4_path{0};
 
 // BF16 kernel instance: 0 = chosen by shape, 1 = 256 x 256 tiles, 2 = 64 x 64
 // tiles, 3 = 128 x 128 tiles with split K (set through gemm355_force_instance,
@@ -498,17 +502,21 @@ int fp4_launch(const Problem &p, int act, void *stream)
     return launch(fp4::gemm_nvfp4_nt_kernel<ACT_NONE, KTAIL>, KERNEL_NVFP4, p, stream, BM, BN, fp4::THREADS_FP4);
 }
 
-// Shared by gemm_nvfp4_nt and gemm_nvfp4_nt_bias_act: validation, launch.
+// Argument checks of the NVFP4 products (GEMM355_OK: valid and not empty;
+// GEMM355_OK with *empty set: nothing to do).
 template <bool FUSED>
-int fp4_product(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq, const void *SFB,
-                const void *bias, int act, void *C, void *stream)
+int fp4_validate(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq, const void *SFB,
+                 const void *bias, int act, const void *C, bool *empty)
 {
+    *empty = false;
     if (M < 0 || N < 0 || K < 0)
         return GEMM355_ERR_INVALID_ARG;
     if (FUSED && (act < GEMM355_ACT_NONE || act > GEMM355_ACT_GELU_TANH))
         return GEMM355_ERR_INVALID_ARG;
-    if (M == 0 || N == 0)
+    if (M == 0 || N == 0) {
+        *empty = true;
         return GEMM355_OK;
+    }
     if (!C || (K > 0 && (!Aq || !SFA || !Bq || !SFB)))
         return GEMM355_ERR_INVALID_ARG;
     const size_t c_bytes = size_t(M) * size_t(N) * 2;
@@ -524,6 +532,18 @@ int fp4_product(int M, int N, int K, const void *Aq, const void *SFA, const void
         return GEMM355_ERR_UNSUPPORTED;
     if (!extent_ok(M, int64_t(K) / 2) || !extent_ok(N, int64_t(K) / 2) || !extent_ok(M, int64_t(N) * 2))
         return GEMM355_ERR_UNSUPPORTED;
+    return GEMM355_OK;
+}
+
+// Shared by gemm_nvfp4_nt and gemm_nvfp4_nt_bias_act: validation, launch.
+template <bool FUSED>
+int fp4_product(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq, const void *SFB,
+                const void *bias, int act, void *C, void *stream)
+{
+    bool empty = false;
+    const int v = fp4_validate<FUSED>(M, N, K, Aq, SFA, Bq, SFB, bias, act, C, &empty);
+    if (v != GEMM355_OK || empty)
+        return v;
 
     Problem p = {};
     p.a = Aq;
@@ -552,6 +572,113 @@ extern "C" int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const
                                       const void *SFB, const void *bias, int activation, void *C, void *stream)
 {
     return fp4_product<true>(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, stream);
+}
+
+namespace {
+
+// gemm_nvfp4_nt_ws's plan: decode first when the 256 x 256 tiles run at least
+// four rounds of the persistent grid (every A strip is then decoded by all
+// N / 256 tiles of its row and every B strip by all M / 256 of its column),
+// else the staging-decode kernel. Forced by gemm355_force_fp4_path.
+bool fp4_decode_first(int M, int N, int K, int cus)
+{
+    const int forced = g_fp4_path.load(std::memory_order_relaxed);
+    if (K == 0 || forced == 1)
+        return false;
+    if (forced == 2)
+        return true;
+    return ceil_div(M, BM) * ceil_div(N, BN) >= 4 * int64_t(cus);
+}
+
+constexpr size_t kFp4WsAlign = 256;
+size_t fp4_ws_a_bytes(int M, int K) { return (size_t(M) * size_t(K) * 2 + kFp4WsAlign - 1) / kFp4WsAlign * kFp4WsAlign; }
+size_t fp4_ws_bytes(int M, int N, int K) { return fp4_ws_a_bytes(M, K) + size_t(N) * size_t(K) * 2; }
+
+int launch_decode(const void *q, const void *sf, void *out, int rows, int K, void *stream)
+{
+    namespace f = gemm355::fp4;
+    f::DecodeArgs d = {static_cast<const uint8_t *>(q), static_cast<const uint8_t *>(sf), static_cast<uint16_t *>(out),
+                       rows, K};
+    const int64_t total = int64_t(rows) * (K / 32);
+    const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(total, f::DECODE_THREADS),
+                                                                             f::DECODE_MAX_BLOCKS));
+    return launch_kernel(f::decode_nvfp4_bf16_kernel, blocks, (unsigned)f::DECODE_THREADS, d,
+                         static_cast<hipStream_t>(stream));
+}
+
+} // namespace
+
+extern "C" int gemm_nvfp4_nt_workspace_size(int M, int N, int K, size_t *bytes)
+{
+    if (M < 0 || N < 0 || K < 0 || !bytes)
+        return GEMM355_ERR_INVALID_ARG;
+    *bytes = 0;
+    if (M == 0 || N == 0 || K == 0)
+        return GEMM355_OK;
+    int cus = 0;
+    const int rc = compute_units(&cus);
+    if (rc != GEMM355_OK)
+        return rc;
+    if (fp4_decode_first(M, N, K, cus))
+        *bytes = fp4_ws_bytes(M, N, K);
+    return GEMM355_OK;
+}
+
+extern "C" int gemm_nvfp4_nt_ws(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
+                                const void *SFB, void *C, void *workspace, size_t workspace_bytes, void *stream)
+{
+    bool empty = false;
+    const int v = fp4_validate<false>(M, N, K, Aq, SFA, Bq, SFB, nullptr, GEMM355_ACT_NONE, C, &empty);
+    if (v != GEMM355_OK || empty)
+        return v;
+    if (workspace_bytes > 0 && !workspace)
+        return GEMM355_ERR_INVALID_ARG;
+    if (workspace_bytes > 0) {   // checks of the workspace itself, before any HIP call
+        if (!aligned(workspace, 16))
+            return GEMM355_ERR_UNSUPPORTED;
+        if (overlaps(workspace, workspace_bytes, C, size_t(M) * size_t(N) * 2) ||
+            overlaps(workspace, workspace_bytes, Aq, size_t(M) * K / 2) ||
+            overlaps(workspace, workspace_bytes, Bq, size_t(N) * K / 2) ||
+            overlaps(workspace, workspace_bytes, SFA, size_t(M) * K / 16) ||
+            overlaps(workspace, workspace_bytes, SFB, size_t(N) * K / 16))
+            return GEMM355_ERR_INVALID_ARG;
+    }
+    int cus = 0;
+    const int rc = compute_units(&cus);
+    if (rc != GEMM355_OK)
+        return rc;
+    if (!fp4_decode_first(M, N, K, cus))
+        return fp4_product<false>(M, N, K, Aq, SFA, Bq, SFB, nullptr, GEMM355_ACT_NONE, C, stream);
+    if (workspace_bytes < fp4_ws_bytes(M, N, K))
+        return GEMM355_ERR_UNSUPPORTED;
+    if (!extent_ok(M, int64_t(K) * 2) || !extent_ok(N, int64_t(K) * 2))
+        return GEMM355_ERR_UNSUPPORTED;   // the decoded operands' extents, as for gemm_bf16_nt
+    uint8_t *a16 = static_cast<uint8_t *>(workspace);
+    uint8_t *b16 = a16 + fp4_ws_a_bytes(M, K);
+    int st = launch_decode(Aq, SFA, a16, M, K, stream);
+    if (st == GEMM355_OK)
+        st = launch_decode(Bq, SFB, b16, N, K, stream);
+    if (st != GEMM355_OK)
+        return st;
+    return bf16_product<false, false>(M, N, K, a16, b16, nullptr, GEMM355_ACT_NONE, C, nullptr, 0, stream);
+}
+
+extern "C" int gemm355_nvfp4_plan(int M, int N, int K, int compute_units, int *decode_first, size_t *workspace_bytes)
+{
+    if (M <= 0 || N <= 0 || K < 0 || compute_units <= 0 || !decode_first || !workspace_bytes)
+        return GEMM355_ERR_INVALID_ARG;
+    const bool d = fp4_decode_first(M, N, K, compute_units);
+    *decode_first = d ? 1 : 0;
+    *workspace_bytes = d ? fp4_ws_bytes(M, N, K) : 0;
+    return GEMM355_OK;
+}
+
+extern "C" int gemm355_force_fp4_path(int path)
+{
+    if (path < 0 || path > 2)
+        return GEMM355_ERR_INVALID_ARG;
+    g_fp4_path.store(path, std::memory_order_relaxed);
+    return GEMM355_OK;
 }
 
 namespace {

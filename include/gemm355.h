@@ -17,9 +17,9 @@
  *  - All array pointers are DEVICE pointers owned by the caller. The library
  *    allocates no memory, keeps no per-call state and never synchronises: it
  *    enqueues the work on `stream` and returns. The only scratch memory, the
- *    FP32 partials of a split K, is a workspace the caller passes to the
- *    *_ws entry points, or, for gemm_bf16_nt_noalloc only, a fixed static
- *    device array. `stream` is a hipStream_t passed as void*; NULL means
+ *    FP32 partials of a split K or the decoded operands of the decode-first
+ *    NVFP4 path, is a workspace the caller passes to the *_ws entry points,
+ *    or, for gemm_bf16_nt_noalloc only, a fixed static device array. `stream` is a hipStream_t passed as void*; NULL means
  *    the default (null) stream.
  *  - Arrays are dense, row-major, with no padding between rows (the leading
  *    dimension of A and B is K, that of C is N). C must not overlap any input.
@@ -34,8 +34,9 @@
  *    the caller's next synchronisation, as usual for HIP.
  *  - Calls are thread-safe: the library holds no mutable state apart from a
  *    per-device cache of the compute-unit count, filled once under a lock,
- *    the overrides set by gemm355_force_instance, gemm355_force_supergroup
- *    and gemm355_force_schedule (process-wide diagnostics), and two static
+ *    the overrides set by gemm355_force_instance, gemm355_force_supergroup,
+ *    gemm355_force_schedule and gemm355_force_fp4_path (process-wide
+ *    diagnostics), and two static
  *    device arrays that only opt-in paths use: the scratch of
  *    gemm_bf16_nt_noalloc and the tile counters of the dynamic tile order
  *    (gemm355_force_schedule(1)); calls that use either and overlap on one
@@ -316,6 +317,60 @@ int gemm_nvfp4_nt(int M, int N, int K, const void *Aq, const void *SFA, const vo
  */
 int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
                            const void *SFB, const void *bias, int activation, void *C, void *stream);
+
+/*
+ * gemm_nvfp4_nt_ws -- gemm_nvfp4_nt with a workspace the caller owns, for
+ * products large enough that decoding each operand once beats decoding it
+ * while staging. The staging-decode kernel decodes every operand strip again
+ * for each 256 x 256 tile that uses it (N/256 times for A, M/256 times for
+ * B), and that vector work and its LDS writes cost clock under the board
+ * power limit. When the tiles run at least four rounds of the persistent
+ * grid (M/256 * N/256 >= 4 x the compute units, e.g. M = N = 8192 on 256
+ * units), this call decodes A into M x K BF16 rows at the workspace start and
+ * B into N x K BF16 rows after it (at the next 256-byte boundary) -- the
+ * decoding of gemm_nvfp4_nt, exact in BF16 -- then runs the BF16 product
+ * (the kernels of gemm_bf16_nt) on them, all on `stream`. Otherwise it runs
+ * gemm_nvfp4_nt and leaves the workspace untouched.
+ * Results: within the parity bound of gemm_nvfp4_nt's (the FP32 sums run in
+ * another order), bitwise equal where every partial sum is exact.
+ * Arguments and requirements as for gemm_nvfp4_nt, plus: the workspace is
+ * device memory of at least gemm_nvfp4_nt_workspace_size bytes, 16-byte
+ * aligned, else GEMM355_ERR_UNSUPPORTED; NULL with workspace_bytes > 0, or a
+ * workspace overlapping an operand or C, is GEMM355_ERR_INVALID_ARG; the
+ * decoded operands (2 M K and 2 N K bytes, rows padded to 256) must stay
+ * below 2^31 bytes each, else GEMM355_ERR_UNSUPPORTED. The library keeps no
+ * reference to the workspace: it may be reused once the call's work on
+ * `stream` is done; calls that run concurrently need their own.
+ */
+int gemm_nvfp4_nt_ws(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq, const void *SFB,
+                     void *C, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gemm_nvfp4_nt_workspace_size -- *bytes = the workspace gemm_nvfp4_nt_ws
+ * uses for this shape on the current device: 2 M K rounded up to a multiple
+ * of 256, plus 2 N K, when it decodes first; else 0 (also for M, N or K = 0).
+ * Errors: GEMM355_ERR_INVALID_ARG (negative size, NULL bytes),
+ * GEMM355_ERR_NO_DEVICE.
+ */
+int gemm_nvfp4_nt_workspace_size(int M, int N, int K, size_t *bytes);
+
+/*
+ * gemm355_nvfp4_plan -- host-only: whether gemm_nvfp4_nt_ws decodes first
+ * for this shape on a device with `compute_units` compute units
+ * (*decode_first = 1) and the workspace bytes it then needs (0 otherwise),
+ * under the current gemm355_force_fp4_path setting. Errors:
+ * GEMM355_ERR_INVALID_ARG for M or N <= 0, K < 0, compute_units <= 0 or a
+ * NULL output.
+ */
+int gemm355_nvfp4_plan(int M, int N, int K, int compute_units, int *decode_first, size_t *workspace_bytes);
+
+/*
+ * gemm355_force_fp4_path -- gemm_nvfp4_nt_ws's choice, a process-wide
+ * diagnostic for tests and measurements: 0 (default) by shape as above, 1
+ * always the staging-decode kernel, 2 always decode first (when K > 0).
+ * Errors: GEMM355_ERR_INVALID_ARG for other values.
+ */
+int gemm355_force_fp4_path(int path);
 
 /*
  * gemm_mxfp4_nt -- C = A * B^T for microscaled FP4 operands (E2M1 codes with

@@ -384,3 +384,44 @@ def test_bf16_plan_follows_the_forced_instance_and_checks_arguments():
     assert lib.gemm355_bf16_plan(8, 8, 8, 256, 0, None, ctypes.byref(out, 4), ctypes.byref(nb)) == g.ERR_INVALID_ARG
     assert lib.gemm355_bf16_plan(8, 8, 8, 256, 0, ctypes.byref(out, 0), ctypes.byref(out, 4),
                                  None) == g.ERR_INVALID_ARG
+
+
+def test_nvfp4_ws_plan_and_rejections_before_any_device_call():
+    lib = g.load()
+    # the shape rule: decode first once the 256 x 256 tiles run four rounds
+    assert g.nvfp4_plan(8192, 8192, 8192, 256) == (True, 4 * 8192 * 8192)
+    assert g.nvfp4_plan(8192, 8192, 8192, 304) == (False, 0)          # 1024 tiles < 4 x 304
+    assert g.nvfp4_plan(4096, 4096, 8192, 256) == (False, 0)
+    assert g.nvfp4_plan(8192, 8192, 0, 256) == (False, 0)             # K = 0: nothing to decode
+    assert g.nvfp4_plan(4096, 16384, 1024, 256)[0]                     # 16 x 64 = 1024 tiles
+    assert not g.nvfp4_plan(4096, 16128, 1024, 256)[0]                 # 16 x 63 tiles
+    # workspace: 2 M K rounded up to 256 bytes, then 2 N K
+    try:
+        g.force_fp4_path(g.FP4_PATH_DECODE_FIRST)
+        assert g.nvfp4_plan(3, 8, 32, 256) == (True, 256 + 2 * 8 * 32)
+        assert g.nvfp4_plan(8, 3, 64, 256) == (True, 1024 + 2 * 3 * 64)
+        g.force_fp4_path(g.FP4_PATH_STAGING)
+        assert g.nvfp4_plan(8192, 8192, 8192, 256) == (False, 0)
+    finally:
+        g.force_fp4_path(g.FP4_PATH_AUTO)
+    assert lib.gemm355_force_fp4_path(3) == g.ERR_INVALID_ARG
+    d, nb = ctypes.c_int(0), ctypes.c_size_t(0)
+    assert lib.gemm355_nvfp4_plan(0, 8, 8, 256, ctypes.byref(d), ctypes.byref(nb)) == g.ERR_INVALID_ARG
+    assert lib.gemm355_nvfp4_plan(8, 8, 8, 0, ctypes.byref(d), ctypes.byref(nb)) == g.ERR_INVALID_ARG
+    out = ctypes.c_size_t(99)
+    assert lib.gemm_nvfp4_nt_workspace_size(-1, 8, 64, ctypes.byref(out)) == g.ERR_INVALID_ARG
+    assert lib.gemm_nvfp4_nt_workspace_size(8, 8, 64, None) == g.ERR_INVALID_ARG
+    assert lib.gemm_nvfp4_nt_workspace_size(0, 8, 64, ctypes.byref(out)) == g.OK and out.value == 0
+    assert lib.gemm_nvfp4_nt_workspace_size(8, 8, 0, ctypes.byref(out)) == g.OK and out.value == 0
+
+    def ws(M, N, K, w, nb, aq=FAKE, sfa=FAKE + 0x100000, bq=FAKE + 0x200000, sfb=FAKE + 0x300000, c=FAKE + 0x400000):
+        return lib.gemm_nvfp4_nt_ws(M, N, K, aq, sfa, bq, sfb, c, w, nb, None)
+    assert ws(-1, 8, 64, None, 0) == g.ERR_INVALID_ARG
+    assert ws(0, 8, 64, None, 0) == g.OK                                # empty: nothing to do
+    assert ws(8, 8, 48, FAKE + 0x500000, 4096) == g.ERR_UNSUPPORTED      # K % 32, as gemm_nvfp4_nt
+    assert ws(8, 8, 64, None, 4096) == g.ERR_INVALID_ARG                 # NULL with bytes
+    assert ws(8, 8, 64, FAKE + 0x500008, 4096) == g.ERR_UNSUPPORTED      # not 16-byte aligned
+    assert ws(8, 8, 64, FAKE + 0x400000, 4096) == g.ERR_INVALID_ARG      # overlaps C
+    assert ws(8, 8, 64, FAKE, 4096) == g.ERR_INVALID_ARG                 # overlaps Aq
+    assert ws(8, 8, 64, FAKE + 0x300000, 4096) == g.ERR_INVALID_ARG      # overlaps SFB
+    assert ws(8, 8, 64, FAKE + 0x500000, 4096) == g.ERR_NO_DEVICE        # valid: reaches the device query

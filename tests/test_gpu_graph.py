@@ -9,7 +9,8 @@ must equal the eager call's bitwise (the kernels are deterministic).
 Covered: the 64 x 64, 128 x 128 (one split) and 256 x 256 BF16 instances
 through gemm_bf16_nt, a split product with its reduction through
 gemm_bf16_nt_ws, gemm_bf16_nt_noalloc (its static scratch), the fused
-epilogue, and the NVFP4 and microscaled FP4 products."""
+epilogue, the NVFP4 and microscaled FP4 products, and the decode-first NVFP4
+path (two decode launches and the BF16 product in one graph)."""
 import numpy as np
 import pytest
 import torch
@@ -92,3 +93,19 @@ def test_fp4_replays(kind):
     C = torch.empty(M * N, dtype=torch.int16, device="cuda")
     f = g.gemm_mxfp4_nt if kind == "mx" else g.gemm_nvfp4_nt
     _capture_and_replay(lambda: f(M, N, K, *ops, C), C)
+
+
+def test_fp4_decode_first_replays():
+    need_gpu()
+    M, N, K = 1024, 1024, 1024
+    Aq, SA = syn.fp4_operand(M, K, seed=15)
+    Bq, SB = syn.fp4_operand(N, K, seed=16)
+    ops = [to_dev(x) for x in (Aq, SA, Bq, SB)]
+    C = torch.empty(M * N, dtype=torch.int16, device="cuda")
+    g.force_fp4_path(g.FP4_PATH_DECODE_FIRST)
+    try:
+        nbytes = g.nvfp4_workspace_size(M, N, K)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        _capture_and_replay(lambda: g.gemm_nvfp4_nt_ws(M, N, K, *ops, C, ws, nbytes), C)
+    finally:
+        g.force_fp4_path(g.FP4_PATH_AUTO)
