@@ -99,7 +99,7 @@ def kernels_for(kind: str, M: int, N: int, K: int, compute_units: int = 256) -> 
     if kind == "fp4_ws":
         if not g.nvfp4_plan(M, N, K, compute_units)[0]:
             return [KERNEL_NAME["fp4"]]
-        return [KERNEL_NAME["fp4_decode"]] * 2 + kernels_for("bf16", M, N, K, compute_units)
+        return [KERNEL_NAME["fp4_decode"]] + kernels_for("bf16", M, N, K, compute_units)
     instance, splits = g.bf16_plan(M, N, K, compute_units)
     epi = EPILOGUE[kind]
     if instance == 3:

@@ -10,11 +10,17 @@
 // BF16 kernel. Decoding once costs a read of the codes and a write and re-read
 // of 2 (M + N) K bytes of BF16 in HBM instead.
 //
-// A thread decodes 32 consecutive elements of one row: 16 code bytes, the two
-// E4M3 scales of their 16-element blocks, 64 bytes of BF16 out. The decode is
-// the staging kernel's (decode8, exact to FP16); FP16 -> BF16 is then exact as
-// well (every decoded value has at most 6 significant bits and lies in
-// [2^-10, 2688]), by way of FP32 and its top 16 bits.
+// Work is split into units of 512 consecutive elements of one row (256 code
+// bytes, 32 scale bytes, 1 KiB of BF16): lane l of a wave decodes elements
+// 8 l .. 8 l + 7 of a unit -- one code dword, its block's scale byte -- into
+// 16 bytes at byte 16 l of the unit's output, so every load and store
+// instruction of a wave covers one contiguous range (256, 32 and 1024 bytes).
+// Each wave takes four units per round, loads first. One launch decodes both
+// operands (A's units, then B's). The decode is the staging kernel's
+// (decode8, exact to FP16); FP16 -> BF16 is then exact as well (every decoded
+// value has at most 6 significant bits and lies in [2^-10, 2688]), by way of
+// FP32 and its top 16 bits. A row's last unit may be partial (K % 512 != 0):
+// lanes past K neither load nor store.
 #pragma once
 
 #include "gemm_fp4.hpp"
@@ -23,7 +29,9 @@ namespace gemm355 {
 namespace fp4 {
 
 constexpr int DECODE_THREADS = 256;
-constexpr int DECODE_MAX_BLOCKS = 8192;
+constexpr int DECODE_WAVES = DECODE_THREADS / 64;
+constexpr int DECODE_UNROLL = 4;
+constexpr int DECODE_MAX_BLOCKS = 2048;
 
 // Two FP16 values -> two BF16 values (exact for the decoded set), packed.
 __device__ inline unsigned bf16_pair(_Float16 lo, _Float16 hi)
@@ -31,34 +39,53 @@ __device__ inline unsigned bf16_pair(_Float16 lo, _Float16 hi)
     return (__builtin_bit_cast(unsigned, (float)lo) >> 16) | (__builtin_bit_cast(unsigned, (float)hi) & 0xFFFF0000u);
 }
 
-// rows x K operand (codes: rows x K/2 bytes, scales: rows x K/16 bytes, both
-// row-major) -> rows x K BF16, row-major. K % 32 == 0; 16-byte aligned codes
-// and output, 2-byte aligned scales.
+// Operand o (0 = A, 1 = B): rows x K codes (rows x K/2 bytes) and scales
+// (rows x K/16 bytes), row-major, into rows x K BF16, row-major. K % 32 == 0;
+// codes 4-byte aligned, output 16-byte aligned.
 struct DecodeArgs {
-    const uint8_t *q, *sf;
-    uint16_t *out;
-    int rows, K;
+    const uint8_t *q[2], *sf[2];
+    uint16_t *out[2];
+    int rows[2];
+    int K;
 };
 
 __global__ __launch_bounds__(DECODE_THREADS) void decode_nvfp4_bf16_kernel(DecodeArgs a)
 {
-    const uint8_t *q = a.q, *sf = a.sf;
-    uint16_t *out = a.out;
-    const int rows = a.rows, K = a.K;
-    const int per_row = K / 32;
-    const long long total = (long long)rows * per_row;
-    for (long long c = (long long)blockIdx.x * DECODE_THREADS + threadIdx.x; c < total;
-         c += (long long)gridDim.x * DECODE_THREADS) {
-        const int row = (int)(c / per_row), j = (int)(c - (long long)row * per_row);
-        const u32x4 codes = *reinterpret_cast<const u32x4 *>(q + (size_t)row * (K / 2) + 16 * j);
-        const unsigned s = *reinterpret_cast<const uint16_t *>(sf + (size_t)row * (K / 16) + 2 * j);
-        const f16x2 sc = scales2(s);
-        u32x4 *o = reinterpret_cast<u32x4 *>(out + (size_t)row * K + 32 * j);
-        static_for<4>([&](auto dc) {
-            constexpr int d = decltype(dc)::value;
-            const f16x8 v = decode8(codes[d], scale2<d / 2>(sc));
-            o[d] = u32x4{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]), bf16_pair(v[4], v[5]), bf16_pair(v[6], v[7])};
-        });
+    const int K = a.K;
+    const int lane = threadIdx.x & 63;
+    const int upr = (K + 511) / 512;                       // units per row
+    const long long units0 = (long long)a.rows[0] * upr;
+    const long long total = units0 + (long long)a.rows[1] * upr;
+    const long long waves = (long long)gridDim.x * DECODE_WAVES;
+    const long long wave = (long long)blockIdx.x * DECODE_WAVES + (threadIdx.x >> 6);
+    for (long long base = wave; base < total; base += DECODE_UNROLL * waves) {
+        unsigned codes[DECODE_UNROLL], sfb[DECODE_UNROLL];
+        uint16_t *dst[DECODE_UNROLL];
+#pragma unroll
+        for (int j = 0; j < DECODE_UNROLL; ++j) {
+            const long long u = base + j * waves;
+            dst[j] = nullptr;
+            if (u < total) {
+                const int o = u < units0 ? 0 : 1;
+                const long long v = o ? u - units0 : u;
+                const int row = (int)(v / upr);
+                const int e0 = (int)(v - (long long)row * upr) * 512 + 8 * lane;
+                if (e0 < K) {
+                    codes[j] = *reinterpret_cast<const unsigned *>(a.q[o] + (size_t)row * (K / 2) + e0 / 2);
+                    sfb[j] = a.sf[o][(size_t)row * (K / 16) + e0 / 16];
+                    dst[j] = a.out[o] + (size_t)row * K + e0;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < DECODE_UNROLL; ++j) {
+            if (dst[j]) {
+                const f16x2 s = scales2(sfb[j]);
+                const f16x8 v = decode8(codes[j], scale2<0>(s));
+                *reinterpret_cast<u32x4 *>(dst[j]) =
+                    u32x4{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]), bf16_pair(v[4], v[5]), bf16_pair(v[6], v[7])};
+            }
+        }
     }
 }
 

@@ -594,13 +594,24 @@ constexpr size_t kFp4WsAlign = 256;
 size_t fp4_ws_a_bytes(int M, int K) { return (size_t(M) * size_t(K) * 2 + kFp4WsAlign - 1) / kFp4WsAlign * kFp4WsAlign; }
 size_t fp4_ws_bytes(int M, int N, int K) { return fp4_ws_a_bytes(M, K) + size_t(N) * size_t(K) * 2; }
 
-int launch_decode(const void *q, const void *sf, void *out, int rows, int K, void *stream)
+// Both operands decoded into BF16 rows by one launch.
+int launch_decode(const void *Aq, const void *SFA, void *a16, int M, const void *Bq, const void *SFB, void *b16,
+                  int N, int K, void *stream)
 {
     namespace f = gemm355::fp4;
-    f::DecodeArgs d = {static_cast<const uint8_t *>(q), static_cast<const uint8_t *>(sf), static_cast<uint16_t *>(out),
-                       rows, K};
-    const int64_t total = int64_t(rows) * (K / 32);
-    const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(total, f::DECODE_THREADS),
+    f::DecodeArgs d = {};
+    d.q[0] = static_cast<const uint8_t *>(Aq);
+    d.sf[0] = static_cast<const uint8_t *>(SFA);
+    d.out[0] = static_cast<uint16_t *>(a16);
+    d.rows[0] = M;
+    d.q[1] = static_cast<const uint8_t *>(Bq);
+    d.sf[1] = static_cast<const uint8_t *>(SFB);
+    d.out[1] = static_cast<uint16_t *>(b16);
+    d.rows[1] = N;
+    d.K = K;
+    const int64_t units = (int64_t(M) + N) * ceil_div(K, 512);
+    const int64_t per_block = int64_t(f::DECODE_WAVES) * f::DECODE_UNROLL;
+    const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(units, per_block),
                                                                              f::DECODE_MAX_BLOCKS));
     return launch_kernel(f::decode_nvfp4_bf16_kernel, blocks, (unsigned)f::DECODE_THREADS, d,
                          static_cast<hipStream_t>(stream));
@@ -655,9 +666,7 @@ extern "C" int gemm_nvfp4_nt_ws(int M, int N, int K, const void *Aq, const void 
         return GEMM355_ERR_UNSUPPORTED;   // the decoded operands' extents, as for gemm_bf16_nt
     uint8_t *a16 = static_cast<uint8_t *>(workspace);
     uint8_t *b16 = a16 + fp4_ws_a_bytes(M, K);
-    int st = launch_decode(Aq, SFA, a16, M, K, stream);
-    if (st == GEMM355_OK)
-        st = launch_decode(Bq, SFB, b16, N, K, stream);
+    const int st = launch_decode(Aq, SFA, a16, M, Bq, SFB, b16, N, K, stream);
     if (st != GEMM355_OK)
         return st;
     return bf16_product<false, false>(M, N, K, a16, b16, nullptr, GEMM355_ACT_NONE, C, nullptr, 0, stream);

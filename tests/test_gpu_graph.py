@@ -10,7 +10,7 @@ Covered: the 64 x 64, 128 x 128 (one split) and 256 x 256 BF16 instances
 through gemm_bf16_nt, a split product with its reduction through
 gemm_bf16_nt_ws, gemm_bf16_nt_noalloc (its static scratch), the fused
 epilogue, the NVFP4 and microscaled FP4 products, and the decode-first NVFP4
-path (two decode launches and the BF16 product in one graph)."""
+path (the decode launch and the BF16 product in one graph)."""
 import numpy as np
 import pytest
 import torch
