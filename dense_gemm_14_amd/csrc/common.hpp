@@ -207,4 +207,49 @@ __device__ inline void store_tile(f32x16 (&acc)[BI][BJ], const __amdgpu_buffer_r
     }
 }
 
+// Epilogue for 16 x 16 result blocks. The matrix instruction is fed B rows
+// as its first operand and A rows as its second, so lane (l16, grp) of block
+// (i, j) holds C[m][n .. n + 3], m = m0 + 16 i + l16, n = n0 + 16 j + 4 grp.
+// For x = block (i, 2 jp) and y = block (i, 2 jp + 1), v_permlane16_swap
+// exchanges lane groups so that group 0 holds columns 0..7 of x, group 1
+// columns 0..7 of y, group 2 columns 8..15 of x and group 3 columns 8..15 of
+// y: one 16-byte store per lane, 64 contiguous bytes per C row and pair.
+// BI x BJ blocks (BJ even; the wave's tile is 16 BI x 16 BJ).
+template <int EPI, int BI, int BJ>
+__device__ inline void store_tile16(f32x4 (&acc)[BI][BJ], const __amdgpu_buffer_rsrc_t &rc,
+                                    const __amdgpu_buffer_rsrc_t &rbias, int M, int N, int m0, int n0, int lane)
+{
+    static_assert(BJ % 2 == 0, "blocks are stored in pairs of columns");
+    const int l16 = lane & 15, grp = lane >> 4;
+    // fused: bias[n .. n + 3] of this lane's columns in block column j
+    u32x2 bias_w[BJ];
+    if constexpr (EPI != EPI_PLAIN) {
+#pragma unroll
+        for (int j = 0; j < BJ; ++j) {
+            const int n = n0 + 16 * j + 4 * grp;
+            bias_w[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rbias, n < N ? n * 2 : OOB, 0, 0));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+        const int m = m0 + 16 * i + l16;
+#pragma unroll
+        for (int jp = 0; jp < BJ / 2; ++jp) {
+            f32x4 x = acc[i][2 * jp], y = acc[i][2 * jp + 1];
+            if constexpr (EPI != EPI_PLAIN) {
+                x = epilogue4<EPI>(x, bias_w[2 * jp]);
+                y = epilogue4<EPI>(y, bias_w[2 * jp + 1]);
+            }
+            const unsigned x0 = pack_bf16(x[0], x[1]), x1 = pack_bf16(x[2], x[3]);
+            const unsigned y0 = pack_bf16(y[0], y[1]), y1 = pack_bf16(y[2], y[3]);
+            const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
+            const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+            const int n = n0 + 32 * jp + 16 * (grp & 1) + 8 * (grp >> 1);
+            const int off = (m < M && n < N) ? (m * N + n) * 2 : OOB;
+            __builtin_amdgcn_raw_buffer_store_b128(out, rc, off, 0, 0);
+        }
+    }
+}
+
 } // namespace gemm355

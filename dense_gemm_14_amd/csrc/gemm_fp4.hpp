@@ -4,14 +4,18 @@
 // one E4M3 scale per 16 consecutive K elements of a row ("NVFP4 GEMM on
 // Blackwell", section "NVFP4 Datatype"). They are decoded exactly to FP16
 // while being staged into LDS, so the matrix-core loop is the ordinary FP16
-// one (v_mfma_f32_32x32x16_f16, same rate as BF16).
+// one (v_mfma_f32_16x16x32_f16, same rate as BF16).
 //
 // Work decomposition
 //   * Output tile 256 x 256 per workgroup, 8 waves in a 2 x 4 layout, two per
-//     SIMD, each wave owning a 128 x 64 block = 4 x 2 MFMA blocks of 32 x 32
-//     whose FP32 accumulators (128 per lane) live in the accumulation
-//     registers. Two waves per SIMD because the decode is vector ALU work
-//     beside the matrix instructions: measured on gfx950 with a probe (one
+//     SIMD, each wave owning a 128 x 64 block = 8 x 4 MFMA blocks of 16 x 16
+//     (128 FP32 accumulators per lane). 16 x 16 x 32 rather than 32 x 32 x 16
+//     instructions: the same cycles per product, but half the accumulator
+//     reads and writes per product, and the chip runs at a power limit, so
+//     the clock it holds under this loop is higher (measured 5-7 % faster at
+//     4096^3 to 8192^3, bitwise the same C).
+//   * Two waves per SIMD because the decode is vector ALU work beside the
+//     matrix instructions: measured on gfx950 with a probe (one
 //     32 x 32 x 16 FP16 matrix instruction and n conversions or packed
 //     multiplies issued after it, in a loop), one wave per SIMD loses 12, 18
 //     and 25 % of the matrix rate at n = 2, 3 and 4, while two waves per SIMD
@@ -128,10 +132,10 @@ struct DynamicOrder {
 };
 __device__ DynamicOrder g_dynamic_order;
 
-constexpr int CHUNK_EVERY = 3;   // matrix instructions per written chunk
+constexpr int CHUNK_EVERY = 6;   // matrix instructions per written chunk
 constexpr int LOADS = 4;         // staging loads per thread and step
 constexpr int LOAD_AT = 2;       // first of them (then one every LOAD_EVERY instructions)
-constexpr int LOAD_EVERY = 6;
+constexpr int LOAD_EVERY = 12;
 constexpr int SETS = 3;          // register sets: a step's loads are issued three steps before it is computed
 
 // EPI: EPI_PLAIN, or the activation of the fused epilogue (bias, then the
@@ -153,19 +157,19 @@ void gemm_nvfp4_nt_kernel(Problem p)
     const int wave = tid >> 6;
     const int wm = wave & 1;   // wave's 128-row half of the tile (A rows)
     const int wn = wave >> 1;  // wave's 64-column quarter (B rows)
-    const int l32 = lane & 31;
-    const int half = lane >> 5;
+    const int l16 = lane & 15;
+    const int grp = lane >> 4;
     const int K = p.K;
 
-    // Per-lane LDS fragment addresses in stage 0: row l32 of the wave's first
-    // block, logical chunk (2 kk + half) for K sub-step kk of 16 elements;
-    // block i and stage s add 32 i rows and s * TILE_BYTES (immediate offsets)
-    int fa_at[4], fb_at[4];
+    // Per-lane LDS fragment addresses in stage 0: row l16 of the wave's first
+    // block, logical chunk (4 h + grp) for K sub-step h of 32 elements; block
+    // i and stage s add 16 i rows and s * TILE_BYTES (immediate offsets)
+    int fa_at[2], fb_at[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int ko = swizzle(l32, 2 * kk + half) << 4;   // rows differ from l32 by multiples of 32
-        fa_at[kk] = A_TILES + (wm * 128 + l32) * ROW_BYTES + ko;
-        fb_at[kk] = B_TILES + (wn * 64 + l32) * ROW_BYTES + ko;
+    for (int h = 0; h < 2; ++h) {
+        const int ko = swizzle(l16, 4 * h + grp) << 4;   // rows differ from l16 by multiples of 16
+        fa_at[h] = A_TILES + (wm * 128 + l16) * ROW_BYTES + ko;
+        fb_at[h] = B_TILES + (wn * 64 + l16) * ROW_BYTES + ko;
     }
     // Staged row r0 = tid / 2 of each operand, K half kh = tid % 2 of each
     // step, i.e. logical chunks 4 kh .. 4 kh + 3 of the row; wa[d] / wb[d]:
@@ -243,19 +247,20 @@ void gemm_nvfp4_nt_kernel(Problem p)
             *reinterpret_cast<f16x8 *>(lds + (c < 4 ? wa[d] : wb[d]) + st * TILE_BYTES) = decode8(codes, s);
         };
 
-        f32x16 acc[4][2];
-        frag fa[2][4], fb[2][2];
-        // fragment read r (0..5) of sub-step kk from stage `st`: A block r for
-        // r < 4, else B block r - 4
-        auto read_frag = [&](int st, int kk, int set, int r) {
-            if (r < 4)
-                fa[set][r] = *reinterpret_cast<const frag *>(lds + fa_at[kk] + st * TILE_BYTES + r * 32 * ROW_BYTES);
-            else
-                fb[set][r - 4] = *reinterpret_cast<const frag *>(lds + fb_at[kk] + st * TILE_BYTES + (r - 4) * 32 * ROW_BYTES);
+        f32x4 acc[8][4];
+        // A fragments in a ring of four (block i in fa[i % 4], read three
+        // blocks ahead of its use), B fragments in one set per sub-step
+        frag fa[4], fb[2][4];
+        auto read_a = [&](int st, int h, int i) {
+            fa[i & 3] = *reinterpret_cast<const frag *>(lds + fa_at[h] + st * TILE_BYTES + i * 16 * ROW_BYTES);
         };
-        auto mma = [&](int set, int t, bool first) {
-            const int i = (t >> 1) & 3, j = t & 1;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[set][j], fa[set][i], first ? f32x16{} : acc[i][j], 0, 0, 0);
+        auto read_b = [&](int st, int h, int j) {
+            fb[h][j] = *reinterpret_cast<const frag *>(lds + fb_at[h] + st * TILE_BYTES + j * 16 * ROW_BYTES);
+        };
+        // matrix instruction u (0..31) of sub-step h: block (u / 4, u % 4)
+        auto mma = [&](int h, int u, bool first) {
+            const int i = u >> 2, j = u & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[h][j], fa[i & 3], first ? f32x4{} : acc[i][j], 0, 0, 0);
         };
 
         // Prologue: step 0 into stage 0, steps 1 and 2 requested into sets 1, 2.
@@ -279,60 +284,71 @@ void gemm_nvfp4_nt_kernel(Problem p)
         }
         lds_barrier();
 #pragma unroll
-        for (int r = 0; r < 6; ++r)
-            read_frag(0, 0, 0, r);
+        for (int i = 0; i < 3; ++i)
+            read_a(0, 0, i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            read_b(0, 0, j);
         SCHED_FENCE();
 
-        // Step kt computes on LDS stage kt % 2 (par) in four sub-steps of 8
-        // matrix instructions (K = 16 each); each sub-step's fragments are
-        // read during the previous one. During sub-steps 0..2 the register
-        // set holding step kt + 1 is decoded and written into the other
-        // stage, one chunk every three matrix instructions, and step kt + 3 is
-        // requested into the set step kt occupied (kt % 3, already written).
-        // The step's single barrier, before sub-step 3, makes the new stage
-        // visible and releases the current one. Matrix instructions, LDS
-        // accesses and loads keep their hand-fixed order; the decode
-        // arithmetic may move across the scheduling barriers, so the
-        // dependent conversions and multiplies of a chunk spread over several
-        // matrix instructions. Set and stage indices are compile-time values
-        // so that the register sets are named statically (a runtime index
-        // would put them in scratch memory).
+        // Step kt computes on LDS stage kt % 2 (par) in two sub-steps h of 32
+        // matrix instructions (K = 32 each), in groups of four that share an
+        // A block. Group g of a sub-step reads the A block three groups ahead
+        // (into the ring slot group g - 1 has just finished with); during
+        // sub-step 0 the B blocks of sub-step 1 are read into the other B set.
+        // Meanwhile the register set holding step kt + 1 is decoded and
+        // written into the other stage, one chunk every six matrix
+        // instructions, and step kt + 3 is requested into the set step kt
+        // occupied (kt % 3, already written). The step's single barrier, after
+        // group 4 of sub-step 1 (the last read of stage par), makes the new
+        // stage visible and releases the current one; groups 5..7 then read
+        // the next step's first three A blocks and its four B blocks.
+        // Matrix instructions, LDS accesses and loads keep their hand-fixed
+        // order; the decode arithmetic may move across the scheduling
+        // barriers, so the dependent conversions and multiplies of a chunk
+        // spread over several matrix instructions. Set and stage indices are
+        // compile-time values so that the register sets are named statically
+        // (a runtime index would put them in scratch memory).
         auto step = [&](int kt, auto par_c, auto set_c, auto first_c) {
             constexpr int par = decltype(par_c)::value;
             constexpr bool first = decltype(first_c)::value;
             constexpr int set_free = decltype(set_c)::value;   // held step kt, already written
             constexpr int set_next = (set_free + 1) % SETS;    // holds step kt + 1
-            static_for<24>([&](auto tc) {
+            static_for<64>([&](auto tc) {
                 constexpr int t = decltype(tc)::value;
-                constexpr int kk = t >> 3;
-                mma(kk & 1, t & 7, first && kk == 0);
-                if constexpr ((t & 7) < 6)
-                    read_frag(par, kk + 1, (kk + 1) & 1, t & 7);
-                if constexpr (t % CHUNK_EVERY == 1)
+                constexpr int h = t >> 5, u = t & 31, g = u >> 2;
+                if constexpr (h == 1 && u == 20) {
+                    // the next stage is written by every wave, the current one fully read
+                    lds_barrier();
+                    SCHED_FENCE();
+                }
+                mma(h, u, first && h == 0);
+                if constexpr (u % 4 == 0) {
+                    if constexpr (g < 5)
+                        read_a(par, h, g + 3);
+                    else if constexpr (h == 0)
+                        read_a(par, 1, g - 5);
+                    else
+                        read_a(par ^ 1, 0, g - 5);
+                }
+                if constexpr (h == 0 && u % 4 == 2 && g < 4)
+                    read_b(par, 1, g);
+                if constexpr (h == 1 && (u == 21 || u == 23 || u == 25 || u == 27))
+                    read_b(par ^ 1, 0, (u - 21) / 2);
+                if constexpr (t % CHUNK_EVERY == 1 && t / CHUNK_EVERY < 8)
                     write_chunk(par ^ 1, set_next, Int<t / CHUNK_EVERY>{});
                 if constexpr (t >= LOAD_AT && (t - LOAD_AT) % LOAD_EVERY == 0 && (t - LOAD_AT) / LOAD_EVERY < LOADS)
                     load(kt + SETS, set_free, (t - LOAD_AT) / LOAD_EVERY);
-                SCHED_VALU_ONLY();
-            });
-            // the next stage is written by every wave, the current one fully read
-            lds_barrier();
-            SCHED_FENCE();
-            // sub-step 3 on fragment set 1, first fragments of the next stage
-            static_for<8>([&](auto tc) {
-                constexpr int t = decltype(tc)::value;
-                mma(1, t, false);
-                if constexpr (t < 6)
-                    read_frag(par ^ 1, 0, 0, t);
                 SCHED_VALU_ONLY();
             });
         };
 
         if (nk == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = f32x16{};
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = f32x4{};
         } else {
             // step kt uses LDS stage kt % 2 and register set kt % 3: six step
             // bodies cover both cycles
@@ -358,7 +374,7 @@ void gemm_nvfp4_nt_kernel(Problem p)
                 step(kt + 4, Int<1>{}, Int<2>{}, Int<0>{});
         }
 
-        store_tile<EPI>(acc, rc, rbias, p.M, p.N, tm * BM + wm * 128, tn * BN + wn * 64, l32, half);
+        store_tile16<EPI>(acc, rc, rbias, p.M, p.N, tm * BM + wm * 128, tn * BN + wn * 64, lane);
         if (DYN)
             pos = next_pos;   // written before the prologue's barrier, rewritten only after the next one
     }
