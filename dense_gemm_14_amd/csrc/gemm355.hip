@@ -576,10 +576,17 @@ extern "C" int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const
 
 namespace {
 
-// gemm_nvfp4_nt_ws's plan: decode first when the 256 x 256 tiles run at least
-// four rounds of the persistent grid (every A strip is then decoded by all
-// N / 256 tiles of its row and every B strip by all M / 256 of its column),
-// else the staging-decode kernel. Forced by gemm355_force_fp4_path.
+// gemm_nvfp4_nt_ws's plan: decode first, or the staging-decode kernel. Both
+// run 256 x 256 tiles on the same persistent grid; a K step of the BF16
+// kernel on decoded operands is shorter than one of the staging kernel,
+// which decodes every A strip once per tile of its row and every B strip once
+// per tile of its column, so decoding first saves time in proportion to the
+// grid's rounds and the number of K steps, and costs time in proportion to
+// (M + N) K, the elements decoded. Measured on MI355X (nine shapes from
+// 2048 x 16384 x 8192 to 12288^2 x 4096, both paths alternating), the two
+// balance at about kFp4RowsPerRound rows of M + N per round of the grid,
+// whatever K. Forced by gemm355_force_fp4_path.
+constexpr int64_t kFp4RowsPerRound = 5000;
 bool fp4_decode_first(int M, int N, int K, int cus)
 {
     const int forced = g_fp4_path.load(std::memory_order_relaxed);
@@ -587,7 +594,9 @@ bool fp4_decode_first(int M, int N, int K, int cus)
         return false;
     if (forced == 2)
         return true;
-    return ceil_div(M, BM) * ceil_div(N, BN) >= 4 * int64_t(cus);
+    const int64_t tiles = ceil_div(M, BM) * ceil_div(N, BN);
+    const int64_t grid = gemm355::persistent_grid((int)std::min<int64_t>(tiles, 1 << 30), cus);
+    return ceil_div(tiles, grid) * kFp4RowsPerRound > int64_t(M) + N;
 }
 
 constexpr size_t kFp4WsAlign = 256;

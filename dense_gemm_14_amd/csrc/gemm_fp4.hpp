@@ -301,8 +301,8 @@ void gemm_nvfp4_nt_kernel(Problem p)
         // instructions, and step kt + 3 is requested into the set step kt
         // occupied (kt % 3, already written). The step's single barrier, after
         // group 4 of sub-step 1 (the last read of stage par), makes the new
-        // stage visible and releases the current one; groups 5..7 then read
-        // the next step's first three A blocks and its four B blocks.
+        // stage visible and releases the current one; group 5 then reads the
+        // next step's four B blocks, and groups 5..7 its first three A blocks.
         // Matrix instructions, LDS accesses and loads keep their hand-fixed
         // order; the decode arithmetic may move across the scheduling
         // barriers, so the dependent conversions and multiplies of a chunk
@@ -333,8 +333,8 @@ void gemm_nvfp4_nt_kernel(Problem p)
                 }
                 if constexpr (h == 0 && u % 4 == 2 && g < 4)
                     read_b(par, 1, g);
-                if constexpr (h == 1 && (u == 21 || u == 23 || u == 25 || u == 27))
-                    read_b(par ^ 1, 0, (u - 21) / 2);
+                if constexpr (h == 1 && u >= 20 && u < 24)
+                    read_b(par ^ 1, 0, u - 20);
                 if constexpr (t % CHUNK_EVERY == 1 && t / CHUNK_EVERY < 8)
                     write_chunk(par ^ 1, set_next, Int<t / CHUNK_EVERY>{});
                 if constexpr (t >= LOAD_AT && (t - LOAD_AT) % LOAD_EVERY == 0 && (t - LOAD_AT) / LOAD_EVERY < LOADS)
