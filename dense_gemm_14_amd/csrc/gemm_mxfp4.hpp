@@ -1,9 +1,9 @@
 // gemm_mxfp4.hpp -- microscaled FP4 NT GEMM for gfx950 on the matrix cores'
 // own block scaling: E2M1 codes (two per byte, even k in the low nibble) with
 // one E8M0 (power-of-two) scale per 32 consecutive K elements of a row, fed
-// undecoded to v_mfma_scale_f32_32x32x64_f8f6f4, which multiplies 64 K of a
-// 32 x 32 block at four times the BF16 rate and applies each lane's scale to
-// the 32 elements it holds.
+// undecoded to v_mfma_scale_f32_16x16x128_f8f6f4, which multiplies 128 K of
+// a 16 x 16 block at four times the BF16 rate and applies each lane's scale
+// to the 32 elements it holds.
 //
 // The format is not the pages' (their FP4 variant scales every 16 elements by
 // an E4M3 value, "NVFP4 GEMM on Blackwell", section "NVFP4 Datatype", which
@@ -13,9 +13,12 @@
 //
 // Work decomposition
 //   * Output tile 256 x 256 per workgroup, 8 waves in 2 x 4, each wave 128 x
-//     64 = 4 x 2 blocks of 32 x 32 (128 accumulation registers per lane), two
-//     waves per SIMD, so that one wave's matrix instructions run while the
-//     other is held issuing copies or waiting on fragment reads.
+//     64 = 8 x 4 blocks of 16 x 16 (128 accumulators per lane), two waves per
+//     SIMD, so that one wave's matrix instructions run while the other is
+//     held issuing copies or waiting on fragment reads. 16 x 16 blocks rather
+//     than 32 x 32: half the accumulator traffic per product, and a row's
+//     four scale bytes of a step are read by four lanes of one group, so the
+//     scale reads are free of bank conflicts.
 //   * K advances 128 per step: 64 bytes of codes per row (the LDS row) and 4
 //     scale bytes. A stage holds the A and B code tiles (16 KiB each); four
 //     stages (128 KiB) form a ring that runs on across the workgroup's tiles:
@@ -32,17 +35,12 @@
 //     each) and two of B; per block of four steps one 1 KiB scale copy (64
 //     rows of A for waves 0..3, of B for waves 4..7, 16 bytes each). Step k + 3 is
 //     requested during step k, after the barrier that frees step k - 1's
-//     stage, one copy every two matrix instructions over the first half of
+//     stage, one copy every four matrix instructions over the first half of
 //     the step (issued together they stall the wave).
-//   * Per step each wave issues 16 matrix instructions (2 sub-steps of K 64 x
-//     4 x 2 blocks). Fragment reads (16 bytes per lane: row l % 32 of a block,
-//     the 32 K of sub-step kk that belong to lane half l / 32) of sub-step 1
-//     are issued during sub-step 0, those of the next step's sub-step 0 (and
-//     its scales) during sub-step 1.
-//   * A lane's scale for sub-step kk is byte 2 kk + l / 32 of its row's 4;
-//     each row's scale dword is shifted right by 8 (l / 32) once per step, so
-//     that byte 2 kk is the lane's scale in both halves and the instruction's
-//     byte select stays a constant.
+//   * Per step each wave issues 32 matrix instructions, in groups of four
+//     sharing an A block. Fragment reads (16 bytes per lane: row l % 16 of a
+//     block, the 32 K of group l / 16) and the lane's scale byte of each
+//     block are read three groups ahead for A, a step ahead for B.
 #pragma once
 
 #include "common.hpp"
@@ -73,7 +71,7 @@ constexpr int THREADS_MX = 512;                  // 8 waves, two per SIMD
 constexpr int COPIES = 4;                        // code copies per wave and step (2 + 2)
 constexpr int SCALE_COPIES = 1;                  // per wave and scale block (A or B)
 constexpr int EPILOGUE_STORES = 16;              // 16-byte stores per wave per tile (128 x 64 BF16)
-constexpr int EPILOGUE_LOADS = 8;                // fused epilogue: bias loads per wave (2 x 4 column runs)
+constexpr int EPILOGUE_LOADS = 4;                // fused epilogue: bias loads per wave (one per 16-column block)
 
 static_assert(LDS_BYTES <= 163840, "LDS ring exceeds the 160 KiB of a gfx950 workgroup");
 static_assert(TM == 256 && TN == 256 && THREADS_MX == 512, "the copy map assumes 256 x 256 tiles and 8 waves");
@@ -133,8 +131,8 @@ void gemm_mxfp4_nt_kernel(Problem p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0 .. 7; waves w and w + 4 share a SIMD
     const int wm = wave & 1;   // 128-row half of the tile (A rows)
     const int wn = wave >> 1;  // 64-column quarter (B rows)
-    const int l32 = lane & 31;
-    const int half = lane >> 5;
+    const int l16 = lane & 15;
+    const int grp = lane >> 4;
     const int K = p.K;
     const unsigned kb = (unsigned)K / 2;       // code bytes per row
     const unsigned sb = (unsigned)K / 32;      // scale bytes per row
@@ -222,68 +220,54 @@ void gemm_mxfp4_nt_kernel(Problem p)
             copy_one(k, stage, q);
     };
 
-    // Fragments: [buffer][block] 16 bytes (the instruction reads the low four
-    // dwords of an eight-dword FP4 operand); scales [buffer][block] as two
-    // dwords, pre-shifted for the lane's half. A and B rows of a lane have the
-    // same swizzle (they differ by multiples of 32), so one set of chunk
-    // offsets serves both.
-    i32x4 fa[2][4], fb[2][2];
-    unsigned sa[2][4], sbv[2][2];
-    const int a_row0 = 128 * wm + l32, b_row0 = 64 * wn + l32;   // block 0 rows; block i is 32 i rows on
-    int kofs[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-        kofs[kk] = swizzle(l32, 2 * kk + half) << 4;
+    // Fragments: 16 bytes per lane (the instruction reads the low four dwords
+    // of an eight-dword FP4 operand): row l16 of a 16-row block, the 32 K
+    // elements of group grp, i.e. logical chunk grp of the row's 64 bytes.
+    // A blocks in a ring of four (block i in fa[i % 4], read three groups of
+    // matrix instructions ahead of its use), B blocks in one set per step
+    // parity. Scales: byte grp of the row's four for the step, read alone
+    // (byte reads of one dword by the four lanes of a row are served
+    // together), so the instruction's byte select is 0. Rows of a lane's
+    // blocks differ by multiples of 16, so one chunk offset serves all.
+    i32x4 fa[4], fb[2][4];
+    unsigned sa[4], sbv[2][4];
+    const int a_row0 = 128 * wm + l16, b_row0 = 64 * wn + l16;   // block 0 rows; block i is 16 i rows on
+    int kofs = swizzle(l16, grp) << 4;
     int a_frag = A_CODES + a_row0 * ROW_BYTES, b_frag = B_CODES + b_row0 * ROW_BYTES;
-    int a_sc = SCALES_BASE + a_row0 * SCALE_BLOCK_ROW, b_sc = SCALES_BASE + TM * SCALE_BLOCK_ROW + b_row0 * SCALE_BLOCK_ROW;
-    // fragment read r (0..5) of sub-step kk: A block r for r < 4, else B block r - 4
-    auto read_frag = [&](int stage, int kk, int buf, int r) {
-        const uint8_t *st = lds + stage * STAGE_BYTES;
-        if (r < 4)
-            fa[buf][r] = *reinterpret_cast<const i32x4 *>(st + a_frag + r * 32 * ROW_BYTES + kofs[kk]);
-        else
-            fb[buf][r - 4] = *reinterpret_cast<const i32x4 *>(st + b_frag + (r - 4) * 32 * ROW_BYTES + kofs[kk]);
-    };
-    auto read_frags = [&](int stage, int kk, int buf) {
-#pragma unroll
-        for (int r = 0; r < 6; ++r)
-            read_frag(stage, kk, buf, r);
-    };
+    int a_sc = SCALES_BASE + a_row0 * SCALE_BLOCK_ROW + grp, b_sc = SCALES_BASE + TM * SCALE_BLOCK_ROW + b_row0 * SCALE_BLOCK_ROW + grp;
     // scales of K step k: dword k % 4 of the rows' 16 bytes in slot (gb0 + k / 4) % 2
-    const unsigned sh = 8u * (unsigned)half;
-    auto read_scales = [&](int k, int buf) {
-        const uint8_t *st = lds + ((gb0 + (k >> 2)) & 1) * SCALE_BLOCK + (k & 3) * SCALE_ROW;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sa[buf][i] = *reinterpret_cast<const unsigned *>(st + a_sc + 32 * i * SCALE_BLOCK_ROW) >> sh;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            sbv[buf][j] = *reinterpret_cast<const unsigned *>(st + b_sc + 32 * j * SCALE_BLOCK_ROW) >> sh;
+    auto scale_at = [&](int k) { return lds + ((gb0 + (k >> 2)) & 1) * SCALE_BLOCK + (k & 3) * SCALE_ROW; };
+    // A block i of K step k (stage `stage`) and its scales
+    auto read_a = [&](int stage, int k, int i) {
+        fa[i & 3] = *reinterpret_cast<const i32x4 *>(lds + stage * STAGE_BYTES + a_frag + i * 16 * ROW_BYTES + kofs);
+        sa[i & 3] = *reinterpret_cast<const uint8_t *>(scale_at(k) + a_sc + 16 * i * SCALE_BLOCK_ROW);
+    };
+    // B block j of K step k into set `buf`, and its scales
+    auto read_b = [&](int stage, int k, int buf, int j) {
+        fb[buf][j] = *reinterpret_cast<const i32x4 *>(lds + stage * STAGE_BYTES + b_frag + j * 16 * ROW_BYTES + kofs);
+        sbv[buf][j] = *reinterpret_cast<const uint8_t *>(scale_at(k) + b_sc + 16 * j * SCALE_BLOCK_ROW);
     };
 
-    f32x16 acc[4][2];
-    // Matrix instructions of sub-step kk on fragment buffer fbuf and scale
-    // buffer sbuf (format 4 = E2M1 for both operands; byte select 2 kk). B rows are the first operand, so each 32 x 32 result
-    // arrives as in the FP4 kernel: lane (l32, half) of block (i, j) holds
-    // C[m][n + 8 g + 4 half + e] in element 4 g + e, m = row l32 of block i.
-    // matrix instruction t (0..7) of sub-step kk: block (t / 2, t % 2)
-    auto mma1 = [&](int fbuf, int sbuf, int kk, int t) {
-        const int i = t >> 1, j = t & 1;
-        const i32x8 x = __builtin_shufflevector(fb[fbuf][j], fb[fbuf][j], 0, 1, 2, 3, -1, -1, -1, -1);
-        const i32x8 y = __builtin_shufflevector(fa[fbuf][i], fa[fbuf][i], 0, 1, 2, 3, -1, -1, -1, -1);
-        if (kk == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc[i][j], 4, 4, 0, (int)sbv[sbuf][j], 0,
-                                                                    (int)sa[sbuf][i]);
-        else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc[i][j], 4, 4, 2, (int)sbv[sbuf][j], 2,
-                                                                    (int)sa[sbuf][i]);
+    f32x4 acc[8][4];
+    // Matrix instruction t (0..31) of a step on B set `buf`: block (t / 4,
+    // t % 4), format 4 (E2M1) for both operands. B rows are the first
+    // operand, so lane (l16, grp) of block (i, j) holds C[m][n .. n + 3] with
+    // m = row l16 of A block i, n = 4 grp + column 16 j (checked on the
+    // device: D = first . second^T, lane l holding row l % 16 and K group
+    // l / 16, its scale applied to those 32 elements).
+    auto mma1 = [&](int buf, int t) {
+        const int i = t >> 2, j = t & 3;
+        const i32x8 x = __builtin_shufflevector(fb[buf][j], fb[buf][j], 0, 1, 2, 3, -1, -1, -1, -1);
+        const i32x8 y = __builtin_shufflevector(fa[i & 3], fa[i & 3], 0, 1, 2, 3, -1, -1, -1, -1);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, acc[i][j], 4, 4, 0, (int)sbv[buf][j], 0,
+                                                                 (int)sa[i & 3]);
     };
     auto zero_acc = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = f32x16{};
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = f32x4{};
     };
 
     int tm = 0, tn = 0;
@@ -302,28 +286,40 @@ void gemm_mxfp4_nt_kernel(Problem p)
 
         if (nk > 0) {
             if (first) {
-                // fill the ring with steps 0 .. STAGES - 2 and scale block 0
+                // fill the ring with steps 0 .. STAGES - 2 and scale block 0,
+                // and wait for all but step 2's copies, so that step 0's
+                // wait (written for a tile after another) holds here too
                 copy_scales(0);
 #pragma unroll
                 for (int s = 0; s < STAGES - 1; ++s)
                     copy_step(s, s);
-                wait_copies_le<COPIES * (STAGES - 2)>();
+                wait_copies_le<COPIES * (STAGES - 3)>();
                 lds_barrier();
-                read_frags(0, 0, 0);
-                read_scales(0, 0);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+                    read_a(0, 0, i);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    read_b(0, 0, 0, j);
             }
             // (otherwise the previous tile's last steps copied steps 0 .. 2
-            // and read step 0's fragments and scales)
+            // and read step 0's first A blocks, its B blocks and their scales)
 
-            // K step k on stage k % STAGES; scale buffer k % 2
-            auto step = [&](int k, auto sbuf_c) {
-                constexpr int sbuf = decltype(sbuf_c)::value;
+            // K step k on stage k % STAGES, B set k % 2. The step's shape is
+            // fixed at compile time (step 0 of a tile, the first step of a
+            // scale block): a branch inside the loop body would let the
+            // compiler sink a step's matrix instructions past it, away from
+            // the reads and copies they are interleaved with.
+            auto step = [&](int k, auto buf_c, auto block_start_c, auto tile_start_c) {
+                constexpr int buf = decltype(buf_c)::value;
+                constexpr bool block_start = decltype(block_start_c)::value;   // k % 4 == 0
+                constexpr bool tile_start = decltype(tile_start_c)::value;     // k == 0
                 const int stage = k & (STAGES - 1);
                 const int next_stage = (k + 1) & (STAGES - 1);
                 const int copy_stage = (k + STAGES - 1) & (STAGES - 1);
                 // LDS address bases, hidden from the optimiser at every step so
                 // that each stage's addresses are formed where they are used
-                asm volatile("" : "+v"(kofs[0]), "+v"(kofs[1]), "+v"(a_frag), "+v"(b_frag), "+v"(a_sc), "+v"(b_sc));
+                asm volatile("" : "+v"(kofs), "+v"(a_frag), "+v"(b_frag), "+v"(a_sc), "+v"(b_sc));
                 // this wave's reads of step k - 1 and k and its copies of step
                 // k + 1 (and every older scale block) are done: only step
                 // k + 2's code copies may still be in flight, plus a scale
@@ -331,47 +327,54 @@ void gemm_mxfp4_nt_kernel(Problem p)
                 // and at step 0 after a previous tile that tile's epilogue
                 // stores, issued after them
                 wait_reads();
-                if (k == 0 && !first)
+                if constexpr (tile_start)
                     wait_copies_le<COPIES * (STAGES - 3) + EPILOGUE_STORES>();
                 else
                     wait_copies_le<COPIES * (STAGES - 3)>();
                 // after the barrier every wave is done with step k - 1's stage
+                // and step k + 1's stage is complete
                 lds_barrier();
-                // sub-steps 0 and 1, order fixed: fragment read r of sub-step 1
-                // after matrix instruction 2 r of sub-step 0; those of step
-                // k + 1's sub-step 0 likewise during sub-step 1, then its
-                // scales; the copies of step k + STAGES - 1 into step k - 1's
-                // stage one every two matrix instructions, first half only
+                // 32 matrix instructions in groups of four sharing an A block,
+                // order fixed: group g reads A block g + 3 (blocks 0..2 of step
+                // k + 1 in groups 5..7), groups 0..3 step k + 1's B block g;
+                // the copies of step k + STAGES - 1 into step k - 1's stage
+                // one every four matrix instructions over the first half
                 SCHED_FENCE();
-                static_for<16>([&](auto tc) {
+                static_for<32>([&](auto tc) {
                     constexpr int t = decltype(tc)::value;
-                    constexpr int kk = t >> 3, u = t & 7;
-                    mma1(kk, sbuf, kk, u);
-                    if constexpr (u < 6) {
-                        if constexpr (kk == 0)
-                            read_frag(stage, 1, 1, u);
+                    constexpr int g = t >> 2;
+                    mma1(buf, t);
+                    if constexpr (t % 4 == 0) {
+                        if constexpr (g < 5)
+                            read_a(stage, k, g + 3);
                         else
-                            read_frag(next_stage, 0, 0, u);
+                            read_a(next_stage, k + 1, g - 5);
                     }
-                    if constexpr (t % 2 == 1 && t < 2 * COPIES)
-                        copy_one(k + STAGES - 1, copy_stage, t / 2);
-                    if constexpr (t == 15)
-                        read_scales(k + 1, sbuf ^ 1);
+                    if constexpr (t % 4 == 2 && g < 4)
+                        read_b(next_stage, k + 1, buf ^ 1, g);
+                    if constexpr (t % 4 == 1 && t < 4 * COPIES)
+                        copy_one(k + STAGES - 1, copy_stage, t / 4);
                     SCHED_VALU_ONLY();
                 });
                 // the next scale block during the first step of a block: its
                 // slot held block k / 4 - 1, whose steps every wave finished
                 // before this step's barrier
-                if ((k & 3) == 0)
+                if constexpr (block_start)
                     copy_scales((k >> 2) + 1);
             };
-            // nk is a multiple of 4 (K % 512 == 0): steps go in pairs
-            for (int k = 0; k < nk; k += 2) {
-                step(k, Int<0>{});
-                step(k + 1, Int<1>{});
+            // nk is a multiple of 4 (K % 512 == 0): steps go in fours
+            step(0, Int<0>{}, Int<1>{}, Int<1>{});
+            step(1, Int<1>{}, Int<0>{}, Int<0>{});
+            step(2, Int<0>{}, Int<0>{}, Int<0>{});
+            step(3, Int<1>{}, Int<0>{}, Int<0>{});
+            for (int k = 4; k < nk; k += 4) {
+                step(k, Int<0>{}, Int<1>{}, Int<0>{});
+                step(k + 1, Int<1>{}, Int<0>{}, Int<0>{});
+                step(k + 2, Int<0>{}, Int<0>{}, Int<0>{});
+                step(k + 3, Int<1>{}, Int<0>{}, Int<0>{});
             }
         }
-        store_tile<EPI>(acc, rc, rbias, p.M, p.N, tm * TM + 128 * wm, tn * TN + 64 * wn, l32, half);
+        store_tile16<EPI>(acc, rc, rbias, p.M, p.N, tm * TM + 128 * wm, tn * TN + 64 * wn, lane);
         gb0 += nk / SCALE_STEPS;
         tm = ntm;
         tn = ntn;
