@@ -15,12 +15,13 @@
 // 8 l .. 8 l + 7 of a unit -- one code dword, its block's scale byte -- into
 // 16 bytes at byte 16 l of the unit's output, so every load and store
 // instruction of a wave covers one contiguous range (256, 32 and 1024 bytes).
-// Each wave takes four units per round, loads first. One launch decodes both
-// operands (A's units, then B's). The decode is the staging kernel's
-// (decode8, exact to FP16); FP16 -> BF16 is then exact as well (every decoded
-// value has at most 6 significant bits and lies in [2^-10, 2688]), by way of
-// FP32 and its top 16 bits. A row's last unit may be partial (K % 512 != 0):
-// lanes past K neither load nor store.
+// A wave takes whole rows (A's rows, then B's, as one sequence; one launch
+// decodes both operands) and walks each row's units DECODE_UNROLL at a time,
+// loads first, so no index division is needed. The decode is the staging
+// kernel's (decode8, exact to FP16); FP16 -> BF16 is then exact as well
+// (every decoded value has at most 6 significant bits and lies in
+// [2^-10, 2688]), by way of FP32 and its top 16 bits. A row's last unit may
+// be partial (K % 512 != 0): lanes past K neither load nor store.
 #pragma once
 
 #include "gemm_fp4.hpp"
@@ -53,37 +54,33 @@ __global__ __launch_bounds__(DECODE_THREADS) void decode_nvfp4_bf16_kernel(Decod
 {
     const int K = a.K;
     const int lane = threadIdx.x & 63;
-    const int upr = (K + 511) / 512;                       // units per row
-    const long long units0 = (long long)a.rows[0] * upr;
-    const long long total = units0 + (long long)a.rows[1] * upr;
-    const long long waves = (long long)gridDim.x * DECODE_WAVES;
-    const long long wave = (long long)blockIdx.x * DECODE_WAVES + (threadIdx.x >> 6);
-    for (long long base = wave; base < total; base += DECODE_UNROLL * waves) {
-        unsigned codes[DECODE_UNROLL], sfb[DECODE_UNROLL];
-        uint16_t *dst[DECODE_UNROLL];
+    const int rows = a.rows[0] + a.rows[1];
+    const int waves = (int)gridDim.x * DECODE_WAVES;
+    const int first = (int)blockIdx.x * DECODE_WAVES + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    for (int r = first; r < rows; r += waves) {
+        const int o = r < a.rows[0] ? 0 : 1;
+        const int row = o ? r - a.rows[0] : r;
+        const uint8_t *q = a.q[o] + (size_t)row * (K / 2);
+        const uint8_t *sf = a.sf[o] + (size_t)row * (K / 16);
+        uint16_t *out = a.out[o] + (size_t)row * K;
+        for (int e = 8 * lane; e - 8 * lane < K; e += DECODE_UNROLL * 512) {
+            unsigned codes[DECODE_UNROLL], sfb[DECODE_UNROLL];
 #pragma unroll
-        for (int j = 0; j < DECODE_UNROLL; ++j) {
-            const long long u = base + j * waves;
-            dst[j] = nullptr;
-            if (u < total) {
-                const int o = u < units0 ? 0 : 1;
-                const long long v = o ? u - units0 : u;
-                const int row = (int)(v / upr);
-                const int e0 = (int)(v - (long long)row * upr) * 512 + 8 * lane;
+            for (int j = 0; j < DECODE_UNROLL; ++j) {
+                const int e0 = e + 512 * j;
                 if (e0 < K) {
-                    codes[j] = *reinterpret_cast<const unsigned *>(a.q[o] + (size_t)row * (K / 2) + e0 / 2);
-                    sfb[j] = a.sf[o][(size_t)row * (K / 16) + e0 / 16];
-                    dst[j] = a.out[o] + (size_t)row * K + e0;
+                    codes[j] = *reinterpret_cast<const unsigned *>(q + e0 / 2);
+                    sfb[j] = sf[e0 / 16];
                 }
             }
-        }
 #pragma unroll
-        for (int j = 0; j < DECODE_UNROLL; ++j) {
-            if (dst[j]) {
-                const f16x2 s = scales2(sfb[j]);
-                const f16x8 v = decode8(codes[j], scale2<0>(s));
-                *reinterpret_cast<u32x4 *>(dst[j]) =
-                    u32x4{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]), bf16_pair(v[4], v[5]), bf16_pair(v[6], v[7])};
+            for (int j = 0; j < DECODE_UNROLL; ++j) {
+                const int e0 = e + 512 * j;
+                if (e0 < K) {
+                    const f16x8 v = decode8(codes[j], scale2<0>(scales2(sfb[j])));
+                    *reinterpret_cast<u32x4 *>(out + e0) =
+                        u32x4{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]), bf16_pair(v[4], v[5]), bf16_pair(v[6], v[7])};
+                }
             }
         }
     }

@@ -582,11 +582,12 @@ namespace {
 // which decodes every A strip once per tile of its row and every B strip once
 // per tile of its column, so decoding first saves time in proportion to the
 // grid's rounds and the number of K steps, and costs time in proportion to
-// (M + N) K, the elements decoded. Measured on MI355X (nine shapes from
-// 2048 x 16384 x 8192 to 12288^2 x 4096, both paths alternating), the two
-// balance at about kFp4RowsPerRound rows of M + N per round of the grid,
-// whatever K. Forced by gemm355_force_fp4_path.
-constexpr int64_t kFp4RowsPerRound = 5000;
+// (M + N) K, the elements decoded, plus a second launch. Measured on MI355X
+// (14 shapes from 3072^2 x 8192 to 12288^2 x 4096, both paths alternating):
+// with one round the staging kernel was faster at every shape, and from two
+// rounds on the two balance at about kFp4RowsPerRound rows of M + N per
+// round, whatever K. Forced by gemm355_force_fp4_path.
+constexpr int64_t kFp4RowsPerRound = 7000;
 bool fp4_decode_first(int M, int N, int K, int cus)
 {
     const int forced = g_fp4_path.load(std::memory_order_relaxed);
@@ -596,7 +597,8 @@ bool fp4_decode_first(int M, int N, int K, int cus)
         return true;
     const int64_t tiles = ceil_div(M, BM) * ceil_div(N, BN);
     const int64_t grid = gemm355::persistent_grid((int)std::min<int64_t>(tiles, 1 << 30), cus);
-    return ceil_div(tiles, grid) * kFp4RowsPerRound > int64_t(M) + N;
+    const int64_t rounds = ceil_div(tiles, grid);
+    return rounds >= 2 && rounds * kFp4RowsPerRound > int64_t(M) + N;
 }
 
 constexpr size_t kFp4WsAlign = 256;
@@ -618,9 +620,8 @@ int launch_decode(const void *Aq, const void *SFA, void *a16, int M, const void 
     d.out[1] = static_cast<uint16_t *>(b16);
     d.rows[1] = N;
     d.K = K;
-    const int64_t units = (int64_t(M) + N) * ceil_div(K, 512);
-    const int64_t per_block = int64_t(f::DECODE_WAVES) * f::DECODE_UNROLL;
-    const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(units, per_block),
+    // one wave per row until the grid is full; a wave walks its rows' units
+    const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(int64_t(M) + N, f::DECODE_WAVES),
                                                                              f::DECODE_MAX_BLOCKS));
     return launch_kernel(f::decode_nvfp4_bf16_kernel, blocks, (unsigned)f::DECODE_THREADS, d,
                          static_cast<hipStream_t>(stream));

@@ -324,11 +324,11 @@ int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const void *SFA,
  * while staging. The staging-decode kernel decodes every operand strip again
  * for each 256 x 256 tile that uses it (N/256 times for A, M/256 times for
  * B), and that vector work and its LDS writes cost clock under the board
- * power limit. When the saving outweighs the decode -- the persistent
- * grid's rounds of 256 x 256 tiles times 5000 exceed M + N, a balance
- * measured on MI355X (on 256 units: M = N = 6144 or 8192 decode first,
- * M = N = 4096 and M x N = 16384 x 4096 do not, for any K) -- this call
- * decodes A into M x K BF16 rows at the workspace start and
+ * power limit. When the saving outweighs the decode -- the persistent grid
+ * runs at least two rounds of 256 x 256 tiles and the rounds times 7000
+ * exceed M + N, a balance measured on MI355X (on 256 units: M = N = 5120,
+ * 6144 or 8192 decode first, M = N = 4096 and M x N = 2048 x 16384 do not,
+ * for any K) -- this call decodes A into M x K BF16 rows at the workspace start and
  * B into N x K BF16 rows after it (at the next 256-byte boundary) -- the
  * decoding of gemm_nvfp4_nt, exact in BF16 -- then runs the BF16 product
  * (the kernels of gemm_bf16_nt) on them, all on `stream`. Otherwise it runs

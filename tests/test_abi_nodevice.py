@@ -388,17 +388,19 @@ def test_bf16_plan_follows_the_forced_instance_and_checks_arguments():
 
 def test_nvfp4_ws_plan_and_rejections_before_any_device_call():
     lib = g.load()
-    # the shape rule: decode first once the grid's rounds of 256 x 256 tiles
-    # times 5000 exceed M + N (the sides of the measured balance below)
+    # the shape rule: decode first from two rounds of 256 x 256 tiles on, once
+    # the rounds times 7000 exceed M + N (the sides of the measured balance)
     assert g.nvfp4_plan(8192, 8192, 8192, 256) == (True, 4 * 8192 * 8192)   # 4 rounds, 16384
     assert g.nvfp4_plan(8192, 8192, 8192, 304) == (True, 4 * 8192 * 8192)   # ceil(1024 / 304) = 4
-    assert g.nvfp4_plan(8192, 8192, 8192, 512) == (False, 0)                # 2 rounds
-    assert g.nvfp4_plan(4096, 4096, 8192, 256) == (False, 0)                # 1 round, 8192
+    assert g.nvfp4_plan(8192, 8192, 8192, 512) == (False, 0)                # 2 rounds, 14000 < 16384
+    assert g.nvfp4_plan(4096, 4096, 8192, 256) == (False, 0)                # 1 round
+    assert g.nvfp4_plan(3072, 3072, 8192, 256) == (False, 0)                # 1 round, 144 tiles
     assert g.nvfp4_plan(8192, 8192, 0, 256) == (False, 0)                   # K = 0: nothing to decode
     assert g.nvfp4_plan(6144, 6144, 6144, 256)[0]                            # 3 rounds, 12288
     assert g.nvfp4_plan(7168, 7168, 64, 256)[0]                              # 784 tiles: 4 rounds
-    assert not g.nvfp4_plan(5120, 5120, 5120, 256)[0]                        # 2 rounds, 10240
-    assert not g.nvfp4_plan(4096, 16384, 1024, 256)[0]                       # 4 rounds, 20480
+    assert g.nvfp4_plan(5120, 5120, 5120, 256)[0]                            # 2 rounds, 10240
+    assert g.nvfp4_plan(4096, 8192, 8192, 256)[0]                            # 2 rounds, 12288
+    assert g.nvfp4_plan(4096, 16384, 1024, 256)[0]                           # 4 rounds, 20480
     assert not g.nvfp4_plan(2048, 16384, 8192, 256)[0]                       # 2 rounds, 18432
     assert g.nvfp4_plan(12288, 12288, 4096, 256)[0]                          # 9 rounds, 24576
     # workspace: 2 M K rounded up to 256 bytes, then 2 N K
