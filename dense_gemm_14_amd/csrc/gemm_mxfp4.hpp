@@ -16,9 +16,7 @@
 //     64 = 8 x 4 blocks of 16 x 16 (128 accumulators per lane), two waves per
 //     SIMD, so that one wave's matrix instructions run while the other is
 //     held issuing copies or waiting on fragment reads. 16 x 16 blocks rather
-//     than 32 x 32: half the accumulator traffic per product, and a row's
-//     four scale bytes of a step are read by four lanes of one group, so the
-//     scale reads are free of bank conflicts.
+//     than 32 x 32: half the accumulator traffic per product.
 //   * K advances 128 per step: 64 bytes of codes per row (the LDS row) and 4
 //     scale bytes. A stage holds the A and B code tiles (16 KiB each); four
 //     stages (128 KiB) form a ring that runs on across the workgroup's tiles:
@@ -225,10 +223,11 @@ void gemm_mxfp4_nt_kernel(Problem p)
     // elements of group grp, i.e. logical chunk grp of the row's 64 bytes.
     // A blocks in a ring of four (block i in fa[i % 4], read three groups of
     // matrix instructions ahead of its use), B blocks in one set per step
-    // parity. Scales: byte grp of the row's four for the step, read alone
-    // (byte reads of one dword by the four lanes of a row are served
-    // together), so the instruction's byte select is 0. Rows of a lane's
-    // blocks differ by multiples of 16, so one chunk offset serves all.
+    // parity. Scales: byte grp of the row's four for the step, read alone,
+    // so the instruction's byte select is 0 and no shift is needed (the
+    // counters show about six bank-conflict cycles per scale read, as for a
+    // dword read of the row's four; the fragment reads have none). Rows of a
+    // lane's blocks differ by multiples of 16, so one chunk offset serves all.
     i32x4 fa[4], fb[2][4];
     unsigned sa[4], sbv[2][4];
     const int a_row0 = 128 * wm + l16, b_row0 = 64 * wn + l16;   // block 0 rows; block i is 16 i rows on
