@@ -5,10 +5,11 @@
 //
 // Why a second path beside the kernel that decodes while staging: there every
 // 256 x 256 tile decodes its own A and B strips, so at M = N = K = 8192 each
-// operand element is decoded 32 times, and the decode's vector work and LDS
-// writes hold that kernel at the board power limit at a lower clock than the
-// BF16 kernel. Decoding once costs a read of the codes and a write and re-read
-// of 2 (M + N) K bytes of BF16 in HBM instead.
+// operand element is decoded 32 times, and writing the decoded values to LDS
+// (64 KiB per workgroup and K step, beside 192 KiB of fragment reads) costs
+// that kernel matrix-busy cycles the BF16 kernel, whose copies bypass the
+// vector registers, does not lose. Decoding once costs a read of the codes and
+// a write and re-read of 2 (M + N) K bytes of BF16 in HBM instead.
 //
 // Work is split into units of 512 consecutive elements of one row (256 code
 // bytes, 32 scale bytes, 1 KiB of BF16): lane l of a wave decodes elements

@@ -323,8 +323,9 @@ int gemm_nvfp4_nt_bias_act(int M, int N, int K, const void *Aq, const void *SFA,
  * products large enough that decoding each operand once beats decoding it
  * while staging. The staging-decode kernel decodes every operand strip again
  * for each 256 x 256 tile that uses it (N/256 times for A, M/256 times for
- * B), and that vector work and its LDS writes cost clock under the board
- * power limit. When the saving outweighs the decode -- the persistent grid
+ * B), and writing the decoded values into LDS costs it matrix-busy cycles
+ * that the BF16 kernels on decoded rows do not lose. When the saving
+ * outweighs the decode -- the persistent grid
  * runs at least two rounds of 256 x 256 tiles and the rounds times 7000
  * exceed M + N, a balance measured on MI355X (on 256 units: M = N = 5120,
  * 6144 or 8192 decode first, M = N = 4096 and M x N = 2048 x 16384 do not,
