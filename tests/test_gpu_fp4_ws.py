@@ -47,7 +47,10 @@ def _sigma(Q, SF, K):
 
 @pytest.mark.parametrize("path", [g.FP4_PATH_DECODE_FIRST], indirect=True)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (1, 8, 64), (65, 72, 128), (257, 264, 192), (300, 8, 1024),
-                                   (128, 1024, 512), (257, 264, 32), (300, 520, 96), (65, 264, 8160)])
+                                   (128, 1024, 512), (257, 264, 32), (300, 520, 96), (65, 264, 8160),
+                                   # more rows than the decode grid's 8192 waves: waves walk several rows,
+                                   # some across the boundary from A's rows to B's
+                                   (8200, 300, 64), (300, 8200, 96)])
 def test_decode_first_matches_oracle(path, M, N, K):
     Aq, SFA = syn.fp4_operand(M, K, seed=M + 7 * N + K)
     Bq, SFB = syn.fp4_operand(N, K, seed=M + 7 * N + K + 1)
