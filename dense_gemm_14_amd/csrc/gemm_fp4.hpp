@@ -69,12 +69,20 @@ __device__ inline int swizzle(int row, int chunk)
 //
 // Thread t stages row t / 2 of the A tile and of the B tile, K half t % 2 of
 // each step: 16 bytes of packed codes (32 elements) and the two scale bytes
-// of that half (one 16-bit load) per operand, held in one of three register
-// sets (the step being written to LDS and the two after it, already
-// requested from memory). The two threads of a pair read the two halves of
-// the same 32-byte row segment, so each load instruction touches 32 rows
-// instead of 64: the memory pipeline's cost follows the number of distinct
-// lines a load touches.
+// of that half per operand, held in one of three register sets (the step
+// being written to LDS and the two after it, already requested from
+// memory). The two threads of a pair read the two halves of the same 32-byte
+// row segment, so each load instruction touches 32 rows instead of 64: the
+// memory pipeline's cost follows the number of distinct lines a load
+// touches, and each instruction has a cost of its own (timing-only variants
+// at 8192^3: without the code loads 9 % faster, without the scale loads 7 %,
+// though those move an eighth of the bytes). So the scales of a pair of
+// steps come with one instruction: for an even step s the thread with K half
+// h loads the four scale bytes of step s + h (a dword), and each thread takes
+// the two it needs from its own dword or its partner's (adjacent lanes, one
+// lane swap): half the scale instructions, 2 % faster at 8192^3. (With K %
+// 64 == 32 a row's scales are not dword aligned; that instance keeps one
+// 16-bit load per thread and step.)
 // Decoding ("NVFP4 GEMM on Blackwell", section "NVFP4 Datatype"): each code
 // pair converts to two FP16 E2M1 values (v_cvt_scalef32_pk_f16_fp4 with a unit
 // scale), then one packed FP16 multiply applies the E4M3 scale of its 16-element
@@ -211,7 +219,10 @@ void gemm_nvfp4_nt_kernel(Problem p)
         supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, tm, tn);
 
         const int a_code_off = (tm * BM + r0) * (int)kc + 16 * kh, b_code_off = (tn * BN + r0) * (int)kc + 16 * kh;
-        const int a_sf_off = (tm * BM + r0) * (int)ks + 2 * kh, b_sf_off = (tn * BN + r0) * (int)ks + 2 * kh;
+        // scale offsets: KTAIL, the thread's two bytes of each step; else the
+        // dword of step 2 b + kh for a pair of steps 2 b, 2 b + 1 (see load)
+        const int sf_lane = KTAIL ? 2 * kh : 4 * kh;
+        const int a_sf_off = (tm * BM + r0) * (int)ks + sf_lane, b_sf_off = (tn * BN + r0) * (int)ks + sf_lane;
         StageRegs regs[SETS];
         // load q (0..3) of step kt into register set `set`: A codes, A scales,
         // B codes, B scales. The per-lane part of the offset is fixed for the
@@ -231,19 +242,40 @@ void gemm_nvfp4_nt_kernel(Problem p)
             StageRegs &r = regs[set];
             switch (q) {
             case 0: r.a_code = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, at(a_code_off), k0 / 2, 0)); break;
-            case 1: r.a_sf = __builtin_amdgcn_raw_buffer_load_b16(rsa, at(a_sf_off), k0 / 16, 0); break;
+            case 1:
+                if constexpr (KTAIL)
+                    r.a_sf = __builtin_amdgcn_raw_buffer_load_b16(rsa, at(a_sf_off), k0 / 16, 0);
+                else
+                    r.a_sf = __builtin_amdgcn_raw_buffer_load_b32(rsa, a_sf_off, k0 / 16, 0);
+                break;
             case 2: r.b_code = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, at(b_code_off), k0 / 2, 0)); break;
-            default: r.b_sf = __builtin_amdgcn_raw_buffer_load_b16(rsb, at(b_sf_off), k0 / 16, 0); break;
+            default:
+                if constexpr (KTAIL)
+                    r.b_sf = __builtin_amdgcn_raw_buffer_load_b16(rsb, at(b_sf_off), k0 / 16, 0);
+                else
+                    r.b_sf = __builtin_amdgcn_raw_buffer_load_b32(rsb, b_sf_off, k0 / 16, 0);
+                break;
             }
         };
-        // chunk c (0..7) of register set `set` into stage `st`: A for c < 4,
-        // else B; chunk 4 kh + c % 4 of the thread's row
-        auto write_chunk = [&](int st, int set, auto c_c) {
+        // chunk c (0..7) of register set `set` (step s) into stage `st`: A for
+        // c < 4, else B; chunk 4 kh + c % 4 of the thread's row. Its two scale
+        // bytes: KTAIL, in set `set`; else in set `sf_set` (s's own set for an
+        // even s, step s - 1's for an odd one), in the dword lane 2 (r0 % 32)
+        // + (s % 2) loaded, bytes 2 kh and 2 kh + 1.
+        auto write_chunk = [&](int st, int set, auto c_c, int sf_set, auto odd_c) {
             constexpr int c = decltype(c_c)::value;
             constexpr int d = c & 3;
             const StageRegs &r = regs[set];
             const unsigned codes = (c < 4 ? r.a_code : r.b_code)[d];
-            const f16x2 s = scale2<d / 2>(scales2(c < 4 ? r.a_sf : r.b_sf));
+            const int src = KTAIL ? set : sf_set;
+            unsigned sf = c < 4 ? regs[src].a_sf : regs[src].b_sf;
+            if constexpr (!KTAIL) {
+                constexpr int odd = decltype(odd_c)::value;
+                // the pair's lanes are adjacent: swap within each pair
+                const unsigned other = (unsigned)__builtin_amdgcn_mov_dpp((int)sf, 0xB1, 0xF, 0xF, false);
+                sf = (kh == odd ? sf : other) >> (16 * kh);
+            }
+            const f16x2 s = scale2<d / 2>(scales2(sf));
             *reinterpret_cast<f16x8 *>(lds + (c < 4 ? wa[d] : wb[d]) + st * TILE_BYTES) = decode8(codes, s);
         };
 
@@ -269,8 +301,9 @@ void gemm_nvfp4_nt_kernel(Problem p)
         for (int kt = 0; kt < SETS; ++kt)
 #pragma unroll
             for (int q = 0; q < LOADS; ++q)
-                load(kt, kt, q);
-        static_for<8>([&](auto c) { write_chunk(0, 0, c); });
+                if (KTAIL || (kt % 2 == 0) || q % 2 == 0)   // an odd step's scales come with the even one's
+                    load(kt, kt, q);
+        static_for<8>([&](auto c) { write_chunk(0, 0, c, 0, Int<0>{}); });
         // DYN: the ticket has returned by now (it was requested before the
         // loads just written out); thread 0 turns it into the next tile
         if (DYN && tid == 0) {
@@ -335,10 +368,18 @@ void gemm_nvfp4_nt_kernel(Problem p)
                     read_b(par, 1, g);
                 if constexpr (h == 1 && u >= 20 && u < 24)
                     read_b(par ^ 1, 0, u - 20);
+                // step kt + 1 has parity par ^ 1; an odd one's scales sit in
+                // step kt's set
                 if constexpr (t % CHUNK_EVERY == 1 && t / CHUNK_EVERY < 8)
-                    write_chunk(par ^ 1, set_next, Int<t / CHUNK_EVERY>{});
-                if constexpr (t >= LOAD_AT && (t - LOAD_AT) % LOAD_EVERY == 0 && (t - LOAD_AT) / LOAD_EVERY < LOADS)
-                    load(kt + SETS, set_free, (t - LOAD_AT) / LOAD_EVERY);
+                    write_chunk(par ^ 1, set_next, Int<t / CHUNK_EVERY>{}, par == 0 ? set_free : set_next, Int<par ^ 1>{});
+                // step kt + 3 has parity par ^ 1: without KTAIL an odd step
+                // loads no scales, which keeps set_free's scale registers (step
+                // kt's dword pair, whose odd half step kt + 1 uses) intact
+                if constexpr (t >= LOAD_AT && (t - LOAD_AT) % LOAD_EVERY == 0 && (t - LOAD_AT) / LOAD_EVERY < LOADS) {
+                    constexpr int q = (t - LOAD_AT) / LOAD_EVERY;
+                    if constexpr (KTAIL || par == 1 || q % 2 == 0)
+                        load(kt + SETS, set_free, q);
+                }
                 SCHED_VALU_ONLY();
             });
         };
