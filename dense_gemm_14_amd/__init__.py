@@ -14,6 +14,12 @@ The functions mirror the C entry points declared in ``include/gemm355.h``:
     gemm_bf16_nt_noalloc(M, N, K, A, B, C, stream=None)   # *_ws plan, library's fixed scratch
     gemm_nvfp4_nt(M, N, K, Aq, SFA, Bq, SFB, C, stream=None)
     gemm_nvfp4_nt_bias_act(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, stream=None)
+    gemm_nvfp4_nt_ws(M, N, K, Aq, SFA, Bq, SFB, C, workspace, workspace_bytes=None, stream=None)
+    gemm_nvfp4_nt_bias_act_ws(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, workspace,
+                              workspace_bytes=None, stream=None)
+    nvfp4_workspace_size(M, N, K)     # bytes the NVFP4 *_ws calls need on the current device
+    nvfp4_plan(M, N, K, compute_units)  # (decode_first, workspace_bytes) of those calls
+    force_fp4_path(path)              # their path for the process (diagnostic)
     gemm_mxfp4_nt(M, N, K, Aq, SA, Bq, SB, C, stream=None)
     gemm_mxfp4_nt_bias_act(M, N, K, Aq, SA, Bq, SB, bias, activation, C, stream=None)
     force_instance(instance)          # BF16 instance override (diagnostic)
@@ -104,6 +110,8 @@ def load() -> ctypes.CDLL:
     lib.gemm_nvfp4_nt_bias_act.restype = i
     lib.gemm_nvfp4_nt_ws.argtypes = [i, i, i, p, p, p, p, p, p, sz, p]
     lib.gemm_nvfp4_nt_ws.restype = i
+    lib.gemm_nvfp4_nt_bias_act_ws.argtypes = [i, i, i, p, p, p, p, p, i, p, p, sz, p]
+    lib.gemm_nvfp4_nt_bias_act_ws.restype = i
     lib.gemm_nvfp4_nt_workspace_size.argtypes = [i, i, i, ctypes.POINTER(sz)]
     lib.gemm_nvfp4_nt_workspace_size.restype = i
     lib.gemm355_nvfp4_plan.argtypes = [i, i, i, i, p, p]
@@ -341,6 +349,24 @@ def gemm_nvfp4_nt_bias_act(M: int, N: int, K: int, Aq, SFA, Bq, SFB, bias, activ
     c = _addr(C, M * N * 2 if nz else 0, "C")
     _check(lib.gemm_nvfp4_nt_bias_act(M, N, K, aq, sfa, bq, sfb, bb, int(activation), c, _stream(stream)),
            "gemm_nvfp4_nt_bias_act")
+
+
+def gemm_nvfp4_nt_bias_act_ws(M: int, N: int, K: int, Aq, SFA, Bq, SFB, bias, activation: int, C, workspace,
+                              workspace_bytes=None, stream=None) -> None:
+    """gemm_nvfp4_nt_bias_act with a caller-owned workspace, sized and used as
+    for gemm_nvfp4_nt_ws."""
+    lib = load()
+    M, N, K = int(M), int(N), int(K)
+    nz = M > 0 and N > 0
+    aq = _addr(Aq, M * K // 2 if nz else 0, "Aq")
+    sfa = _addr(SFA, M * K // 16 if nz else 0, "SFA")
+    bq = _addr(Bq, N * K // 2 if nz else 0, "Bq")
+    sfb = _addr(SFB, N * K // 16 if nz else 0, "SFB")
+    bb = _addr(bias, N * 2 if nz else 0, "bias")
+    c = _addr(C, M * N * 2 if nz else 0, "C")
+    w, nb = _workspace(workspace, workspace_bytes)
+    _check(lib.gemm_nvfp4_nt_bias_act_ws(M, N, K, aq, sfa, bq, sfb, bb, int(activation), c, w, nb, _stream(stream)),
+           "gemm_nvfp4_nt_bias_act_ws")
 
 
 def gemm_mxfp4_nt(M: int, N: int, K: int, Aq, SA, Bq, SB, C, stream=None) -> None:

@@ -645,11 +645,18 @@ extern "C" int gemm_nvfp4_nt_workspace_size(int M, int N, int K, size_t *bytes)
     return GEMM355_OK;
 }
 
-extern "C" int gemm_nvfp4_nt_ws(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
-                                const void *SFB, void *C, void *workspace, size_t workspace_bytes, void *stream)
+namespace {
+
+// Shared by gemm_nvfp4_nt_ws and gemm_nvfp4_nt_bias_act_ws: validation (all
+// before any HIP call), then the staging kernel or decode-first by the shape
+// rule (fp4_decode_first); FUSED adds the bias and activation in the epilogue
+// of whichever kernel writes C.
+template <bool FUSED>
+int fp4_ws_product(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq, const void *SFB,
+                   const void *bias, int act, void *C, void *workspace, size_t workspace_bytes, void *stream)
 {
     bool empty = false;
-    const int v = fp4_validate<false>(M, N, K, Aq, SFA, Bq, SFB, nullptr, GEMM355_ACT_NONE, C, &empty);
+    const int v = fp4_validate<FUSED>(M, N, K, Aq, SFA, Bq, SFB, bias, act, C, &empty);
     if (v != GEMM355_OK || empty)
         return v;
     if (workspace_bytes > 0 && !workspace)
@@ -661,7 +668,8 @@ extern "C" int gemm_nvfp4_nt_ws(int M, int N, int K, const void *Aq, const void 
             overlaps(workspace, workspace_bytes, Aq, size_t(M) * K / 2) ||
             overlaps(workspace, workspace_bytes, Bq, size_t(N) * K / 2) ||
             overlaps(workspace, workspace_bytes, SFA, size_t(M) * K / 16) ||
-            overlaps(workspace, workspace_bytes, SFB, size_t(N) * K / 16))
+            overlaps(workspace, workspace_bytes, SFB, size_t(N) * K / 16) ||
+            (FUSED && overlaps(workspace, workspace_bytes, bias, size_t(N) * 2)))
             return GEMM355_ERR_INVALID_ARG;
     }
     int cus = 0;
@@ -669,7 +677,7 @@ extern "C" int gemm_nvfp4_nt_ws(int M, int N, int K, const void *Aq, const void 
     if (rc != GEMM355_OK)
         return rc;
     if (!fp4_decode_first(M, N, K, cus))
-        return fp4_product<false>(M, N, K, Aq, SFA, Bq, SFB, nullptr, GEMM355_ACT_NONE, C, stream);
+        return fp4_product<FUSED>(M, N, K, Aq, SFA, Bq, SFB, bias, act, C, stream);
     if (workspace_bytes < fp4_ws_bytes(M, N, K))
         return GEMM355_ERR_UNSUPPORTED;
     if (!extent_ok(M, int64_t(K) * 2) || !extent_ok(N, int64_t(K) * 2))
@@ -679,7 +687,24 @@ extern "C" int gemm_nvfp4_nt_ws(int M, int N, int K, const void *Aq, const void 
     const int st = launch_decode(Aq, SFA, a16, M, Bq, SFB, b16, N, K, stream);
     if (st != GEMM355_OK)
         return st;
-    return bf16_product<false, false>(M, N, K, a16, b16, nullptr, GEMM355_ACT_NONE, C, nullptr, 0, stream);
+    return bf16_product<FUSED, false>(M, N, K, a16, b16, bias, act, C, nullptr, 0, stream);
+}
+
+} // namespace
+
+extern "C" int gemm_nvfp4_nt_ws(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
+                                const void *SFB, void *C, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return fp4_ws_product<false>(M, N, K, Aq, SFA, Bq, SFB, nullptr, GEMM355_ACT_NONE, C, workspace,
+                                 workspace_bytes, stream);
+}
+
+extern "C" int gemm_nvfp4_nt_bias_act_ws(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
+                                         const void *SFB, const void *bias, int activation, void *C,
+                                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    return fp4_ws_product<true>(M, N, K, Aq, SFA, Bq, SFB, bias, activation, C, workspace, workspace_bytes,
+                                stream);
 }
 
 extern "C" int gemm355_nvfp4_plan(int M, int N, int K, int compute_units, int *decode_first, size_t *workspace_bytes)

@@ -349,6 +349,20 @@ int gemm_nvfp4_nt_ws(int M, int N, int K, const void *Aq, const void *SFA, const
                      void *C, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gemm_nvfp4_nt_bias_act_ws -- gemm_nvfp4_nt_bias_act with a workspace the
+ * caller owns: the product of gemm_nvfp4_nt_ws (the same shape rule, the same
+ * workspace size and layout) with the fused epilogue of
+ * gemm_nvfp4_nt_bias_act ("NVFP4 GEMM on Blackwell", "Kernel 1", "Epilogue
+ * Warps": bias per output column added to the FP32 sum, then the activation,
+ * before the BF16 rounding), applied by whichever kernel writes C.
+ * Arguments, requirements and errors as for those two calls; a workspace
+ * overlapping the bias is also GEMM355_ERR_INVALID_ARG.
+ */
+int gemm_nvfp4_nt_bias_act_ws(int M, int N, int K, const void *Aq, const void *SFA, const void *Bq,
+                              const void *SFB, const void *bias, int activation, void *C, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
  * gemm_nvfp4_nt_workspace_size -- *bytes = the workspace gemm_nvfp4_nt_ws
  * uses for this shape on the current device: 2 M K rounded up to a multiple
  * of 256, plus 2 N K, when it decodes first; else 0 (also for M, N or K = 0).

@@ -433,3 +433,15 @@ def test_nvfp4_ws_plan_and_rejections_before_any_device_call():
     assert ws(8, 8, 64, FAKE, 4096) == g.ERR_INVALID_ARG                 # overlaps Aq
     assert ws(8, 8, 64, FAKE + 0x300000, 4096) == g.ERR_INVALID_ARG      # overlaps SFB
     assert ws(8, 8, 64, FAKE + 0x500000, 4096) == g.ERR_NO_DEVICE        # valid: reaches the device query
+
+    # the fused form: the same checks, plus the epilogue's
+    def wsf(M, N, K, w, nb, bias=FAKE + 0x600000, act=g.ACT_GELU_TANH):
+        return lib.gemm_nvfp4_nt_bias_act_ws(M, N, K, FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000,
+                                             bias, act, FAKE + 0x400000, w, nb, None)
+    assert wsf(0, 8, 64, None, 0) == g.OK                               # empty: nothing to do
+    assert wsf(8, 8, 64, FAKE + 0x500000, 4096, act=7) == g.ERR_INVALID_ARG    # unknown activation
+    assert wsf(8, 8, 64, FAKE + 0x500000, 4096, bias=FAKE + 0x600008) == g.ERR_UNSUPPORTED   # bias alignment
+    assert wsf(8, 8, 64, FAKE + 0x500000, 4096, bias=FAKE + 0x400000) == g.ERR_INVALID_ARG   # bias inside C
+    assert wsf(8, 8, 64, FAKE + 0x5FFF00, 4096) == g.ERR_INVALID_ARG    # workspace overlaps the bias
+    assert wsf(8, 8, 64, FAKE + 0x500000, 4096) == g.ERR_NO_DEVICE      # valid: reaches the device query
+    assert wsf(8, 8, 64, FAKE + 0x500000, 4096, bias=None) == g.ERR_NO_DEVICE   # no bias: zeros

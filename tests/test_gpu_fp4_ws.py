@@ -1,5 +1,5 @@
-"""Parity of gemm_nvfp4_nt_ws, the NVFP4 product with a caller-owned
-workspace, through the C ABI. Its decode-first path decodes each operand once
+"""Parity of gemm_nvfp4_nt_ws and gemm_nvfp4_nt_bias_act_ws, the NVFP4
+products with a caller-owned workspace, through the C ABI. Its decode-first path decodes each operand once
 into BF16 rows in the workspace and runs the BF16 kernels on them; it is forced
 (gemm355_force_fp4_path) at ragged and K-tail shapes so that small problems
 exercise it too, and taken by shape at 8192^3. Checks: the oracle within the
@@ -134,3 +134,67 @@ def test_small_workspace_is_rejected_without_launching(path):
     assert e.value.status == g.ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert np.all(C.bits() == CANARY) and bool(torch.all(ws == CANARY))
+
+
+# ---- the fused epilogue through the workspace (gemm_nvfp4_nt_bias_act_ws) -----
+
+ACTS = [g.ACT_NONE, g.ACT_RELU, g.ACT_GELU_TANH]
+
+
+def run_ws_fused(Aq, SFA, Bq, SFB, bias, act, M, N, K):
+    nbytes = g.nvfp4_workspace_size(M, N, K)
+    ws = torch.full((nbytes // 2 + GUARD,), CANARY, dtype=torch.int16, device="cuda") if nbytes else None
+    C = GuardedC(M, N)
+    g.gemm_nvfp4_nt_bias_act_ws(M, N, K, to_dev(Aq), to_dev(SFA), to_dev(Bq), to_dev(SFB),
+                                to_dev(bias) if bias is not None else None, act, C.view, ws, nbytes)
+    torch.cuda.synchronize()
+    assert C.guards_intact(), "write outside C"
+    if ws is not None:
+        assert np.all(ws[nbytes // 2:].cpu().numpy() == CANARY), "write past the workspace"
+    return C.bits()
+
+
+@pytest.mark.parametrize("path", [g.FP4_PATH_DECODE_FIRST], indirect=True)
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("M,N,K", [(300, 264, 512), (65, 72, 96)])
+def test_fused_decode_first_matches_oracle(path, act, M, N, K):
+    Aq, SFA = syn.fp4_operand(M, K, seed=M + K + 3 * act)
+    Bq, SFB = syn.fp4_operand(N, K, seed=N + K + 1)
+    sigma = _sigma(Aq, SFA, K) * _sigma(Bq, SFB, K)
+    # bias on the scale of the sums, so the activations' bend is exercised
+    bias = syn.bf16_uniform(1, N, seed=N + 9, lo=-sigma * K ** 0.5, hi=sigma * K ** 0.5)[0]
+    got = run_ws_fused(Aq, SFA, Bq, SFB, bias, act, M, N, K)
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    ref, z = oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, bias, act, ms, ns, with_z=True)
+    res = tolerance.check_fused(got, ref.reshape(M, N), z.reshape(M, N), K, act, sigma)
+    assert res, res
+
+
+@pytest.mark.parametrize("path", [g.FP4_PATH_DECODE_FIRST], indirect=True)
+@pytest.mark.parametrize("act", [g.ACT_NONE, g.ACT_RELU])
+def test_fused_decode_first_exact_inputs_bitwise(path, act):
+    # unit-exponent scales (1 + m/8) with K = 256: every partial sum is a
+    # multiple of 2^-8 below 2^15, exact in FP32, and so is the bias sum
+    M, N, K = 264, 256, 256
+    Aq, Bq = syn.fp4_codes(M, K, seed=241), syn.fp4_codes(N, K, seed=242)
+    SFA = syn.e4m3_scales(M, K, seed=243, u_lo=0, u_hi=0)
+    SFB = syn.e4m3_scales(N, K, seed=244, u_lo=0, u_hi=0)
+    bias = syn.bf16_sixteenths(1, N, seed=245, jmax=64)[0]
+    got = run_ws_fused(Aq, SFA, Bq, SFB, bias, act, M, N, K)
+    ms, ns = (x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    assert np.array_equal(got, oracle.gemm_nvfp4_nt_bias_act_at(Aq, SFA, Bq, SFB, K, bias, act, ms, ns).reshape(M, N))
+
+
+@pytest.mark.parametrize("path", [g.FP4_PATH_STAGING], indirect=True)
+def test_fused_staging_path_equals_gemm_nvfp4_nt_bias_act(path):
+    M, N, K = 520, 264, 1056
+    Aq, SFA = syn.fp4_operand(M, K, seed=251)
+    Bq, SFB = syn.fp4_operand(N, K, seed=252)
+    bias = syn.bf16_uniform(1, N, seed=253, lo=-50.0, hi=50.0)[0]
+    assert g.nvfp4_workspace_size(M, N, K) == 0
+    C = run_ws_fused(Aq, SFA, Bq, SFB, bias, g.ACT_GELU_TANH, M, N, K)
+    D = GuardedC(M, N)
+    g.gemm_nvfp4_nt_bias_act(M, N, K, to_dev(Aq), to_dev(SFA), to_dev(Bq), to_dev(SFB), to_dev(bias),
+                             g.ACT_GELU_TANH, D.view)
+    torch.cuda.synchronize()
+    assert np.array_equal(C, D.bits())
