@@ -19,8 +19,9 @@
  *    enqueues the work on `stream` and returns. The only scratch memory, the
  *    FP32 partials of a split K or the decoded operands of the decode-first
  *    NVFP4 path, is a workspace the caller passes to the *_ws entry points,
- *    or, for gemm_bf16_nt_noalloc only, a fixed static device array. `stream` is a hipStream_t passed as void*; NULL means
- *    the default (null) stream.
+ *    or, for gemm_bf16_nt_noalloc only, a fixed static device array.
+ *    `stream` is a hipStream_t passed as void*; NULL means the default (null)
+ *    stream.
  *  - Arrays are dense, row-major, with no padding between rows (the leading
  *    dimension of A and B is K, that of C is N). C must not overlap any input.
  *  - Only the M x N elements of C are written.
@@ -36,8 +37,8 @@
  *    per-device cache of the compute-unit count, filled once under a lock,
  *    the overrides set by gemm355_force_instance, gemm355_force_supergroup,
  *    gemm355_force_schedule and gemm355_force_fp4_path (process-wide
- *    diagnostics), and two static
- *    device arrays that only opt-in paths use: the scratch of
+ *    diagnostics), and two static device arrays that only opt-in paths use:
+ *    the scratch of
  *    gemm_bf16_nt_noalloc and the tile counters of the dynamic tile order
  *    (gemm355_force_schedule(1)); calls that use either and overlap on one
  *    GPU race. Calls may be captured into HIP graphs.
