@@ -38,10 +38,9 @@
  *    the overrides set by gemm355_force_instance, gemm355_force_supergroup,
  *    gemm355_force_schedule and gemm355_force_fp4_path (process-wide
  *    diagnostics), and two static device arrays that only opt-in paths use:
- *    the scratch of
- *    gemm_bf16_nt_noalloc and the tile counters of the dynamic tile order
- *    (gemm355_force_schedule(1)); calls that use either and overlap on one
- *    GPU race. Calls may be captured into HIP graphs.
+ *    the scratch of gemm_bf16_nt_noalloc and the tile counters of the
+ *    dynamic tile order (gemm355_force_schedule(1)); calls that use either
+ *    and overlap on one GPU race. Calls may be captured into HIP graphs.
  */
 #ifndef GEMM355_H
 #define GEMM355_H
