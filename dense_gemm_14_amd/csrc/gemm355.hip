@@ -321,7 +321,9 @@ int launch_instance(const Bf16Plan &plan, const Problem &p, void *workspace, voi
         return launch(gemm355::bf16_small::gemm_bf16_nt_small_kernel<EPI>, KERNEL_BF16_SMALL, p, stream,
                       gemm355::bf16_small::TM, gemm355::bf16_small::TN);
     }
-    return launch(gemm355::bf16::gemm_bf16_nt_kernel<EPI>, KERNEL_BF16, p, stream);
+    if (p.K % gemm355::bf16::BK != 0)
+        return launch(gemm355::bf16::gemm_bf16_nt_kernel<EPI, true>, KERNEL_BF16, p, stream);
+    return launch(gemm355::bf16::gemm_bf16_nt_kernel<EPI, false>, KERNEL_BF16, p, stream);
 }
 
 // Shared by the BF16 entry points: validation, plan, launch. FUSED selects

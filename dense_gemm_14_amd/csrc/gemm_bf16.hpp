@@ -8,10 +8,26 @@
 //     whole K loop. The 16 x 16 x 32 instruction moves half the accumulator
 //     data per multiply-add of the 32 x 32 x 16 one, which lowers the energy
 //     per product and so the clock throttling under the board power limit.
-//   * K advances 64 per step. A step is split into two half-steps of K = 32;
-//     a half-step is 64 matrix instructions on one set of fragments (8 A
-//     blocks, 8 B blocks, 16 bytes per lane each) while the other set is
-//     read from LDS.
+//   * K advances 64 per step. A step is 64 block pairs in row order (block
+//     (p / 8, p % 8) for pair p): each pair is the block's two matrix
+//     instructions, K 0..31 and then K 32..63 of the step, back to back on
+//     the same accumulators. An instruction whose accumulator input is the
+//     result of the one just before it takes that result from the matrix
+//     core instead of the register file: on MI355X a loop of such pairs held
+//     a 5 % higher clock under the board power limit than the same
+//     instructions with every accumulator touched once per K = 32 (2.14
+//     against 2.04 GHz with random BF16 data; 696 against 776 W with zeros
+//     at full clock), and power is what bounds this kernel. The summation
+//     order per element is the same either way.
+//   * Fragments (8 A blocks and 8 B blocks of 16 rows, both K halves: 16
+//     bytes per lane and half each) live in one register set; a block's
+//     fragment of the next step is read into its registers once the block's
+//     last pair of this step has issued. B blocks are used by every row, so
+//     B block j of step s + 1 is read after pair 56 + j of step s, seven
+//     pairs before row 0 of step s + 1 needs it (B block 7 in step s + 1
+//     itself, after its pair 0). A block i (1..7) is read in its own step
+//     after pair 4 i - 3, still before the barrier; A block 0 of step s + 1
+//     after pair 34 of step s.
 //   * LDS is a ring of five 32 KiB slots; a slot holds one unit, the A tile
 //     (256 rows x 64 K) or the B tile of one step, as 256 rows of 128 bytes.
 //     Unit 2 s + op (op 0 = A, 1 = B) lives in slot (2 s + op) mod 5. Each 1
@@ -19,9 +35,10 @@
 //     pipeline (lane i fills bytes 16 i .. 16 i + 15 of the block: 8 rows x
 //     128 bytes), so operands pass through no registers and no LDS-write
 //     instructions, and every request is one whole 128-byte row segment.
-//   * One barrier per step, between its two half-steps. Before it each wave
-//     has finished reading step s (so both of its slots are free) and its
-//     copies of step s + 1 have landed. The barrier opens a copy window that
+//   * One barrier per step, after pair 31. Before it each wave has finished
+//     reading step s (its last reads, A block 7, follow pair 25), so both of
+//     its slots are free, and its copies of step s + 1 have landed; step
+//     s + 1 is read from pair 34 on. The barrier opens a copy window that
 //     runs until the next barrier: the B tile of step s + 2 (into the slot of
 //     A_s, needed one step later) and the A tile of step s + 3 (into the slot
 //     of B_s, needed two steps later). Five slots give every copy at least a
@@ -57,20 +74,20 @@ static_assert(BM == 256 && BN == 256 && THREADS == 256, "the copy map assumes 25
 // the 32 epilogue stores and the copies of A2, B2 and A3 of the new tile.
 static_assert(3 * UNIT_COPIES + EPILOGUE_STORES <= 63, "vmcnt counts at most 63 outstanding operations");
 
-// Instruction positions inside a half-step of 64 matrix instructions.
-// Fragment read r (0..15) follows matrix instruction read_at(r): all reads are
-// issued in the first three quarters so they have landed by the half-step's end.
-constexpr int read_at(int r) { return 3 * r + 1; }
-// The copies of a unit go out in four pairs (blocks 2 p and 2 p + 1 of the
-// wave's eight), one pair every sixteen matrix instructions: A pairs in the
-// first half-step, B pairs in the second. In the last step of a tile the B
-// pairs (the next tile's B1) come one every four matrix instructions, so that
-// they have landed by the epilogue, which waits for every copy.
-constexpr int a_pair_at(int p) { return 16 * p + 4; }
-constexpr int b_pair_at(int p, bool last) { return last ? 4 * p + 1 : 16 * p + 1; }
-// Fragment read order: A0, B0..B7, A1..A7, so the first matrix instructions of
-// a half-step (A block 0 against every B block) wait for two reads only.
-constexpr int read_block(int r) { return r == 0 ? 0 : r <= 8 ? 8 + (r - 1) : r - 8; }
+// Positions inside a step, in block pairs (0..63; the barrier follows pair
+// 31). Fragment reads: A block i (1..7) of the step itself after pair
+// a_read_at(i), at least six pairs before row i; B block 7 of the step itself
+// after pair 0; A block 0 and B block j (0..6) of the next step after pairs
+// a_read_at(0) and b_read_at(j), seven pairs before row 0 of the next step
+// (each into registers whose last use is behind it).
+constexpr int a_read_at(int i) { return i == 0 ? 34 : 4 * i - 3; }
+constexpr int b_read_at(int j) { return 57 + j; }
+constexpr int B7_READ = 0;
+// The copies of a unit go out in four pairs (blocks 2 q and 2 q + 1 of the
+// wave's eight), one copy pair every eight block pairs: A before the barrier,
+// B after it.
+constexpr int a_copy_at(int q) { return 8 * q + 2; }
+constexpr int b_copy_at(int q) { return 32 + 8 * q; }
 
 // Buffer resources for the copies start SHIFT bytes before their operand (and
 // span SHIFT bytes more): block j of a pair is addressed with instruction
@@ -80,12 +97,6 @@ constexpr int read_block(int r) { return r == 0 ? 0 : r <= 8 ? 8 + (r - 1) : r -
 // offset and the instruction offset are added (operand extents are < 2^31).
 constexpr int SHIFT = 3072;
 constexpr int OOB_OFF = (int)0x80000000;
-
-// Step kinds of a tile (at least four steps; smaller K goes to the 64 x 64
-// instance): FIRST (step 0, matrix instructions start from zero), MID (1 ..
-// nk - 4), TAIL (nk - 3: copies step nk - 1, the only one with a K tail),
-// NEXT0 and NEXT1 (nk - 2, nk - 1: copy the next tile's steps 0 and 1).
-enum StepKind : int { FIRST, MID, TAIL, NEXT0, NEXT1 };
 
 __device__ inline int swizzle(int r, int c) { return c ^ ((r >> 1) & 7); }
 
@@ -143,9 +154,6 @@ template <int N>
 __device__ inline void wait_copies_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 // Every LDS read this wave issued has returned.
 __device__ inline void wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// The same as an instruction the compiler knows about, so that it drops its
-// own waits for the fragments read before it.
-__device__ inline void wait_reads_known() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
 
 
 // Lane index recomputed where it is used (volatile, so it is not hoisted
@@ -159,7 +167,7 @@ __device__ inline int fresh_lane_id()
 
 // EPI: EPI_PLAIN, or the activation of the fused epilogue (bias, then the
 // activation, before rounding).
-template <int EPI>
+template <int EPI, bool KTAIL>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_kernel(Problem p)
 {
@@ -237,22 +245,26 @@ void gemm_bf16_nt_kernel(Problem p)
 
     // The workgroup's tiles run as one continuous sequence of steps: the ring,
     // the copy windows and the fragment reads carry on across tile
-    // boundaries, so the copies of a tile's first units are issued during the
-    // previous tile's last steps, and the previous tile's accumulators are
-    // converted and stored while the first half-step of the next tile
-    // overwrites them block by block (its matrix instructions start from 0).
+    // boundaries, so the copies of a tile's first units and the fragments of
+    // its first row are fetched during the previous tile's last steps. Every
+    // step runs the same code: what differs (the K step the copies fetch,
+    // the tile whose rows they read, the wait of a tile's first step) is
+    // uniform arithmetic or a uniform branch around it, so the accumulators
+    // are carried by one loop and every step uses the same registers.
 
     // Copies: wave w fills blocks 8 w .. 8 w + 7 (rows 64 w .. 64 w + 63) of
     // every unit; copy j of the wave fills block 8 w + j, lane i position
     // i & 7 of its row i / 8. voff[op][j]: this lane's offset for copy j of
-    // operand op (0 = A, 1 = B) at step 0 of the current tile, in the shifted
-    // buffer and less the instruction offset 1024 (j % 4); a step adds 128
-    // bytes per K step through the step's base. nvoff: the same for the
-    // next tile (equal to voff after the last tile, so the copies a last tile
-    // issues for its successor read valid rows and are never used). Rows past
-    // M or N are clamped to the last row: the copies read valid memory, and
-    // those rows only feed outputs the epilogue does not store.
-    int voff[2][UNIT_COPIES], nvoff[2][UNIT_COPIES];
+    // operand op (0 = A, 1 = B) at K step 0 of the tile the copies read, in
+    // the shifted buffer and less the instruction offset 1024 (j % 4); a step
+    // adds 128 bytes per K step through the step's base. Two steps before a
+    // tile ends they are recomputed for the next tile, whose first two steps
+    // the tile's last two steps copy (for the same tile after the last one,
+    // so the copies a last tile issues for its successor read valid rows and
+    // are never used). Rows past M or N are clamped to the last row: the
+    // copies read valid memory, and those rows only feed outputs the epilogue
+    // does not store.
+    int voff[2][UNIT_COPIES];
     bool tail_ok[2];   // per block parity: this lane's chunk of step nk - 1 lies below K
     auto offsets = [&](int t_m, int t_n, int (&o)[2][UNIT_COPIES]) {
         const int ln = fresh_lane_id();
@@ -276,7 +288,6 @@ void gemm_bf16_nt_kernel(Problem p)
         has_next = pos < p.tiles;
         if (has_next)
             supergroup_tile(pos, p.tiles_m, p.tiles_n, p.supergroup, ntm, ntn);
-        offsets(has_next ? ntm : tm, has_next ? ntn : tn, nvoff);
     };
     find_next();
 
@@ -303,122 +314,160 @@ void gemm_bf16_nt_kernel(Problem p)
         ring[3] = r0;
         ring[4] = r1;
     };
-    // Pair p of operand op's unit at K step ks_off / 128 into slot `slot`;
-    // NEXT: the next tile's rows; TAIL: chunks at or past K read as zeros
-    // (through the buffer form, whose range check turns OOB_OFF into zeros).
-    auto copies = [&](int op, auto p_c, int slot, int ks_off, bool next, bool tail) {
-        constexpr int p = decltype(p_c)::value;
-        constexpr int j0 = 2 * p, j1 = 2 * p + 1;
-        int v0 = next ? nvoff[op][j0] : voff[op][j0];
-        int v1 = next ? nvoff[op][j1] : voff[op][j1];
-        if (tail) {
-            v0 = tail_ok[0] ? v0 : OOB_OFF;
-            v1 = tail_ok[1] ? v1 : OOB_OFF;
-            copy_pair_buffer<1024 * (j0 & 3), 1024 * (j1 & 3)>(op ? rb : ra, copy_base[p >> 1] + (unsigned)slot, v0,
+    // Pair q of operand op's unit at K step ks_off / 128 into slot `slot`.
+    // With a K tail (KTAIL), every copy goes through the buffer form, and in
+    // the step that copies K step nk - 1 (tail) the chunks at or past K read
+    // as zeros (the buffer's range check turns OOB_OFF into zeros).
+    auto copies = [&](int op, auto q_c, int slot, int ks_off, bool tail) {
+        constexpr int q = decltype(q_c)::value;
+        constexpr int j0 = 2 * q, j1 = 2 * q + 1;
+        int v0 = voff[op][j0];
+        int v1 = voff[op][j1];
+        if constexpr (KTAIL) {
+            v0 = tail && !tail_ok[0] ? OOB_OFF : v0;
+            v1 = tail && !tail_ok[1] ? OOB_OFF : v1;
+            copy_pair_buffer<1024 * (j0 & 3), 1024 * (j1 & 3)>(op ? rb : ra, copy_base[q >> 1] + (unsigned)slot, v0,
                                                                 v1, ks_off);
         } else {
             copy_pair<1024 * (j0 & 3), 1024 * (j1 & 3)>((op ? gb : ga) + (unsigned)ks_off,
-                                                         copy_base[p >> 1] + (unsigned)slot, v0, v1);
+                                                         copy_base[q >> 1] + (unsigned)slot, v0, v1);
         }
     };
 
     bf16x8 fa[2][8], fb[2][8];
-    // Read r of half-step h of the step whose units sit in slots sa, sb.
-    auto read = [&](int sa, int sb, int h, int r) {
-        const int q = read_block(r);
-        if (q < 8)
-            fa[h][q] = *reinterpret_cast<const bf16x8 *>(lds + (a_ofs[h] + sa) + q * 16 * ROW_BYTES);
-        else
-            fb[h][q - 8] = *reinterpret_cast<const bf16x8 *>(lds + (b_ofs[h] + sb) + (q - 8) * 16 * ROW_BYTES);
+    // Both K halves of A block i / B block j of the step whose unit sits in
+    // slot `slot`.
+    auto read_a = [&](int slot, int i) {
+        fa[0][i] = *reinterpret_cast<const bf16x8 *>(lds + (a_ofs[0] + slot) + i * 16 * ROW_BYTES);
+        SCHED_FENCE();
+        fa[1][i] = *reinterpret_cast<const bf16x8 *>(lds + (a_ofs[1] + slot) + i * 16 * ROW_BYTES);
     };
-    // Matrix instruction t of a half-step: block (t / 8, t % 8). B rows are
-    // the first operand and A rows the second, so each 16 x 16 result arrives
-    // transposed (one C row per lane, four adjacent columns).
-    auto mma = [&](int h, int t, bool first) {
-        const int i = t >> 3, j = t & 7;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], first ? f32x4{} : acc[i][j], 0, 0, 0);
+    auto read_b = [&](int slot, int j) {
+        fb[0][j] = *reinterpret_cast<const bf16x8 *>(lds + (b_ofs[0] + slot) + j * 16 * ROW_BYTES);
+        SCHED_FENCE();
+        fb[1][j] = *reinterpret_cast<const bf16x8 *>(lds + (b_ofs[1] + slot) + j * 16 * ROW_BYTES);
+    };
+    // Block pair p: block (p / 8, p % 8), K 0..31 then K 32..63 of the step,
+    // nothing scheduled between the two. B rows are the first operand and A
+    // rows the second, so each 16 x 16 result arrives transposed (one C row
+    // per lane, four adjacent columns). The empty statement takes the second
+    // half's fragments as inputs, so the compiler's wait for them (the later
+    // of each pair of reads) comes before the pair and none between its two
+    // instructions.
+    auto mma2 = [&](int p) {
+        const int i = p >> 3, j = p & 7;
+        asm volatile("" ::"v"(fb[1][j]), "v"(fa[1][i]));
+        SCHED_FENCE();
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
+        SCHED_FENCE();
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
+        SCHED_FENCE();
     };
 
     // Prologue of the workgroup's first tile: units A0, B0, A1, B1 (A2 comes
-    // with the first step's copies, as for every later tile). All four have
-    // landed before the first barrier, as the epilogue of every later tile
-    // waits for the next tile's first two steps.
+    // with the first step's copies, as for every later tile), all landed
+    // before the first barrier, then the fragments of step 0's row 0 that the
+    // previous tile's last step reads for every later tile: A block 0 and B
+    // blocks 0..6.
 #pragma unroll
     for (int u = 0; u < SLOTS - 1; ++u)
-        static_for<UNIT_COPIES / 2>([&](auto pr) { copies(u & 1, pr, u * UNIT_BYTES, (u >> 1) * ROW_BYTES, false, false); });
+        static_for<UNIT_COPIES / 2>([&](auto q) { copies(u & 1, q, u * UNIT_BYTES, (u >> 1) * ROW_BYTES, false); });
     wait_all_copies();
     lds_barrier();
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-        read(ring[0], ring[1], 0, r);
+    // (in the order a step issues them, which the compiler's waits for them
+    // at the top of the loop assume)
+    read_a(ring[0], 0);
     SCHED_FENCE();
-
-    // Step s of the current tile. Its copies fetch step s + 2: the A tile
-    // during the first half-step into the slot of B_{s-1} (freed by the
-    // previous barrier), the B tile during the second into the slot of A_s.
-    // The barrier between the half-steps follows this wave's last read of
-    // step s and the landing of its copies of step s + 1; FIRST needs no
-    // wait there, since the copies of steps 0 and 1 had all landed before the
-    // previous tile's epilogue stores (or before the prologue's barrier).
-    // Only the copies' order among themselves is relied on, never their order
-    // relative to stores. The order of matrix instructions, LDS reads, copies
-    // and scalar instructions inside each half-step is fixed by hand (a
-    // scheduling barrier after every matrix instruction and what follows
-    // it); only plain vector ALU work may move across those barriers, so its
-    // dependency chains spread over several matrix instructions instead of
-    // stalling the issue of the next one.
-    auto step = [&](int s, auto kind_c) {
-        constexpr int kind = decltype(kind_c)::value;
-        constexpr bool first = kind == FIRST, next = kind == NEXT0 || kind == NEXT1, tail = kind == TAIL;
-        asm volatile("" : "+v"(a_ofs[0]), "+v"(a_ofs[1]), "+v"(b_ofs[0]), "+v"(b_ofs[1]), "+s"(copy_base[0]), "+s"(copy_base[1]));
-        // byte offset of the K step the copies fetch (step 0 or 1 of the next tile for NEXT0 / NEXT1)
-        const int ks_off = kind == NEXT0 ? 0 : kind == NEXT1 ? ROW_BYTES : (kind == TAIL ? nk - 1 : s + 2) * ROW_BYTES;
-        // first half-step: fragments 0; read the second half of step s
-        static_for<64>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            mma(0, t, first);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (t == read_at(r))
-                    read(ring[0], ring[1], 1, r);
-            if constexpr (t >= a_pair_at(0) && (t - a_pair_at(0)) % 16 == 0 && t <= a_pair_at(UNIT_COPIES / 2 - 1))
-                copies(0, Int<(t - a_pair_at(0)) / 16>{}, ring[4], ks_off, next, tail);
+    for (int j = 0; j < 7; ++j) {
+        read_b(ring[1], j);
+        SCHED_FENCE();
+    }
+
+    // Step s of the current tile. Its copies fetch K step s + 2 (steps 0 and
+    // 1 of the next tile in the last two steps): the A tile before the
+    // barrier into the slot of B_{s-1} (freed by the previous barrier), the B
+    // tile after it into the slot of A_s. The barrier follows this wave's
+    // last read of step s and the landing of its copies of step s + 1 (in a
+    // tile's first step the previous tile's epilogue stores, issued after
+    // those copies, may stay in flight). Only the copies' order among
+    // themselves is relied on, never their order relative to stores. The
+    // order of matrix instructions, LDS reads, copies and scalar
+    // instructions inside a step is fixed by hand (a scheduling barrier after
+    // every block pair and what follows it); only plain vector ALU work may
+    // move across those barriers, so its dependency chains spread over
+    // several matrix instructions instead of stalling the issue of the next
+    // one. Fragment reads are waited for by the compiler's own counter waits,
+    // just before the pair that uses them, so the B reads issued at the end
+    // of a step overlap the next step's first row.
+    auto step = [&](int s) {
+        asm volatile("" : "+v"(a_ofs[0]), "+v"(a_ofs[1]), "+v"(b_ofs[0]), "+v"(b_ofs[1]), "+s"(copy_base[0]), "+s"(copy_base[1]));
+        const int ks = s + 2 < nk ? s + 2 : s + 2 - nk;   // K step the copies fetch
+        const int ks_off = ks * ROW_BYTES;
+        const bool tail = KTAIL && ks == nk - 1;
+        // pairs 0..31: the last fragments of step s; the A copies
+        static_for<32>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            mma2(p);
+            if constexpr (p == B7_READ)
+                read_b(ring[1], 7);
+#pragma unroll
+            for (int i = 1; i < 8; ++i)
+                if (p == a_read_at(i))
+                    read_a(ring[0], i);
+            if constexpr (p >= a_copy_at(0) && (p - a_copy_at(0)) % 8 == 0 && p <= a_copy_at(UNIT_COPIES / 2 - 1))
+                copies(0, Int<(p - a_copy_at(0)) / 8>{}, ring[4], ks_off, tail);
             SCHED_VALU_ONLY();
         });
         wait_reads();
-        if constexpr (!first)
+        if (s == 0)
+            wait_copies_le<UNIT_COPIES + EPILOGUE_STORES>();
+        else
             wait_copies_le<UNIT_COPIES>();
         lds_barrier();
         SCHED_FENCE();
-        // second half-step: fragments 1; read the first half of step s + 1
-        // (the next tile's first step after a tile's last)
-        static_for<64>([&](auto tc) {
-            constexpr int t = decltype(tc)::value;
-            mma(1, t, false);
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (t == read_at(r))
-                    read(ring[2], ring[3], 0, r);
-            constexpr int b_step = b_pair_at(1, kind == NEXT1) - b_pair_at(0, kind == NEXT1);
-            constexpr int b0 = b_pair_at(0, kind == NEXT1);
-            if constexpr (t >= b0 && (t - b0) % b_step == 0 && (t - b0) / b_step < UNIT_COPIES / 2)
-                copies(1, Int<(t - b0) / b_step>{}, ring[0], ks_off, next, tail);
+        // pairs 32..63: step s + 1's A block 0 and B blocks 0..6 (the next
+        // tile's first step after a tile's last); the B copies
+        static_for<32>([&](auto pc) {
+            constexpr int p = 32 + decltype(pc)::value;
+            mma2(p);
+            if constexpr (p == a_read_at(0))
+                read_a(ring[2], 0);
+            if constexpr (p >= b_read_at(0))
+                read_b(ring[3], p - b_read_at(0));
+            if constexpr (p >= b_copy_at(0) && (p - b_copy_at(0)) % 8 == 0 && p <= b_copy_at(UNIT_COPIES / 2 - 1))
+                copies(1, Int<(p - b_copy_at(0)) / 8>{}, ring[0], ks_off, tail);
             SCHED_VALU_ONLY();
         });
-        wait_reads_known();
         SCHED_FENCE();
         rotate();
     };
 
     for (;;) {
-        step(0, Int<FIRST>{});
-        for (int s = 1; s < nk - 3; ++s)
-            step(s, Int<MID>{});
-        step(nk - 3, Int<TAIL>{});
-        step(nk - 2, Int<NEXT0>{});
-        step(nk - 1, Int<NEXT1>{});
-        // epilogue; the next tile's first two steps are in LDS or landing
-        wait_all_copies();
+        // Accumulators start from zero, written into them (one zero per
+        // block that the compiler cannot see through, so that no instruction
+        // of the first step takes an immediate or shared zero instead): every
+        // pair runs in place on its block's registers.
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float zero;
+                asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+                acc[i][j] = f32x4{zero, zero, zero, zero};
+            }
+        // two loops over the same step: between them the copy offsets move
+        // to the next tile's rows (a branch for it inside the loop makes the
+        // compiler treat the slot offsets as divergent)
+        for (int s = 0; s < nk - 2; ++s)
+            step(s);
+        offsets(has_next ? ntm : tm, has_next ? ntn : tn, voff);
+#pragma clang loop unroll(disable)
+        for (int s = nk - 2; s < nk; ++s)
+            step(s);
+        // epilogue: the next tile's first two steps are in LDS or landing,
+        // its row 0 fragments read; the stores are issued behind the copies
+        // of its step 1, which its first step waits for
         const int ln = fresh_lane_id();
         if constexpr (FUSED) {
             // by block-column pairs, the bias of the next pair requested
@@ -439,19 +488,14 @@ void gemm_bf16_nt_kernel(Problem p)
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int jp = 0; jp < 4; ++jp)
 #pragma unroll
-                for (int jp = 0; jp < 4; ++jp)
+                for (int i = 0; i < 8; ++i)
                     store_pair(tm, tn, i, jp, ln, u32x2{}, u32x2{});
         }
         if (!has_next)
             break;
         // switch to the next tile
-#pragma unroll
-        for (int j = 0; j < UNIT_COPIES; ++j) {
-            voff[0][j] = nvoff[0][j];
-            voff[1][j] = nvoff[1][j];
-        }
         tm = ntm;
         tn = ntn;
         ++round;
