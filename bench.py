@@ -80,7 +80,8 @@ WORKLOADS = {
 CONFIG_INDEX = {"bf16_256": 0, "bf16_4096": 1, "bf16_8192": 2, "bf16_8000": 3, "bf16_skinny": 3,
                 "fp4_8192": 4, "bf16_gelu_8192": 2, "mx_8192": 4, "fp4_ws_8192": 4}
 # BF16 kernels are templates over the epilogue: -1 plain, 2 bias + tanh-form GELU
-KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel<%d>", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel",
+# (the 256 x 256 kernel also over whether K has a tail past a multiple of 64)
+KERNEL_NAME = {"bf16": "gemm355::bf16::gemm_bf16_nt_kernel<%d, %s>", "fp4": "gemm355::fp4::gemm_nvfp4_nt_kernel",
                "mx": "gemm355::mx::gemm_mxfp4_nt_kernel<-1>",
                "bf16_small": "gemm355::bf16_small::gemm_bf16_nt_small_kernel<%d>",
                "bf16_small_long": "gemm355::bf16_small_long::gemm_bf16_nt_small_long_kernel<%d, 4>",
@@ -108,7 +109,7 @@ def kernels_for(kind: str, M: int, N: int, K: int, compute_units: int = 256) -> 
     if instance == 2:   # the 64 x 64 instance's long-K staging (same rule as the library's)
         long_k = K >= 4096 and 2 * -(-M // 64) * -(-N // 64) >= compute_units
         return [KERNEL_NAME["bf16_small_long" if long_k else "bf16_small"] % epi]
-    return [KERNEL_NAME["bf16"] % epi]
+    return [KERNEL_NAME["bf16"] % (epi, "true" if K % 64 else "false")]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
