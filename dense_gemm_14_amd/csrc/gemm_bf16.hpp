@@ -97,8 +97,11 @@ constexpr int B7_READ = 2;
 // 8192^3 and 1.5 % at 8000^3 than both copies after the pair, same box,
 // alternating; one copy per block pair, every two, three or four pairs,
 // measured in between).
+// In a tile's last two steps, which copy the next tile's first two, the B
+// copies come every two pairs, so that they have landed when the epilogue
+// waits for every copy.
 constexpr int a_copy_at(int q) { return 8 * q + 2; }
-constexpr int b_copy_at(int q) { return 32 + 8 * q; }
+constexpr int b_copy_at(int q, bool last = false) { return 32 + (last ? 2 : 8) * q; }
 
 // Buffer resources for the copies start SHIFT bytes before their operand (and
 // span SHIFT bytes more): block j of a pair is addressed with instruction
@@ -452,10 +455,10 @@ void gemm_bf16_nt_kernel(Problem p)
     // 1 of the next tile in the last two steps): the A tile before the
     // barrier into the slot of B_{s-1} (freed by the previous barrier), the B
     // tile after it into the slot of A_s. The barrier follows this wave's
-    // last read of step s and the landing of its copies of step s + 1 (in a
-    // tile's first step the previous tile's epilogue stores, issued after
-    // those copies, may stay in flight). Only the copies' order among
-    // themselves is relied on, never their order relative to stores. The
+    // last read of step s and the landing of its copies of step s + 1 (a
+    // tile's first step waits for none: the epilogue before it waited for
+    // all). Only the copies' order among themselves is relied on, never their
+    // order relative to stores. The
     // order of matrix instructions, LDS reads, copies and scalar
     // instructions inside a step is fixed by hand (a scheduling barrier after
     // every block pair and what follows it); only plain vector ALU work may
@@ -464,8 +467,9 @@ void gemm_bf16_nt_kernel(Problem p)
     // one. Fragment reads are waited for by the compiler's own counter waits,
     // just before the pair that uses them, so the B reads issued at the end
     // of a step overlap the next step's first row.
-    auto step = [&](int s, auto first_c) {
+    auto step = [&](int s, auto first_c, auto last_c) {
         constexpr bool first = decltype(first_c)::value;
+        constexpr bool last = decltype(last_c)::value;
         asm volatile("" : "+v"(a_ofs[0]), "+v"(a_ofs[1]), "+v"(b_ofs[0]), "+v"(b_ofs[1]), "+s"(copy_base[0]), "+s"(copy_base[1]));
         const int ks = s + 2 < nk ? s + 2 : s + 2 - nk;   // K step the copies fetch
         const int ks_off = ks * ROW_BYTES;
@@ -487,9 +491,7 @@ void gemm_bf16_nt_kernel(Problem p)
             SCHED_VALU_ONLY();
         });
         wait_reads();
-        if constexpr (first)
-            wait_copies_le<UNIT_COPIES + EPILOGUE_STORES>();
-        else
+        if constexpr (!first)
             wait_copies_le<UNIT_COPIES>();
         lds_barrier();
         SCHED_FENCE();
@@ -497,9 +499,9 @@ void gemm_bf16_nt_kernel(Problem p)
         // next tile's first step after a tile's last); the B copies
         static_for<32>([&](auto pc) {
             constexpr int p = 32 + decltype(pc)::value;
-            constexpr int b_step = b_copy_at(1) - b_copy_at(0);
-            if constexpr (p >= b_copy_at(0) && (p - b_copy_at(0)) % b_step == 0 && p <= b_copy_at(UNIT_COPIES / 2 - 1))
-                mma2_copies(p, 1, Int<(p - b_copy_at(0)) / b_step>{}, ring[0], ks_off, tail);
+            constexpr int b0 = b_copy_at(0, last), b_step = b_copy_at(1, last) - b0;
+            if constexpr (p >= b0 && (p - b0) % b_step == 0 && p <= b_copy_at(UNIT_COPIES / 2 - 1, last))
+                mma2_copies(p, 1, Int<(p - b0) / b_step>{}, ring[0], ks_off, tail);
             else
                 mma2(p);
 #pragma unroll
@@ -529,20 +531,23 @@ void gemm_bf16_nt_kernel(Problem p)
                 asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
                 acc[i][j] = f32x4{zero, zero, zero, zero};
             }
-        // the first step (its wait lets the previous tile's stores drain),
-        // then two loops over the same step: between them the copy offsets
+        // the first step (it waits for no copies), then two loops over the
+        // same step (in the second the B copies come early): between them the
+        // copy offsets
         // move to the next tile's rows (a branch for it inside the loop makes
         // the compiler treat the slot offsets as divergent)
-        step(0, Int<1>{});
+        step(0, Int<1>{}, Int<0>{});
         for (int s = 1; s < nk - 2; ++s)
-            step(s, Int<0>{});
+            step(s, Int<0>{}, Int<0>{});
         offsets(has_next ? ntm : tm, has_next ? ntn : tn, voff);
 #pragma clang loop unroll(disable)
         for (int s = nk - 2; s < nk; ++s)
-            step(s, Int<0>{});
-        // epilogue: the next tile's first two steps are in LDS or landing,
-        // its row 0 fragments read; the stores are issued behind the copies
-        // of its step 1, which its first step waits for
+            step(s, Int<0>{}, Int<1>{});
+        // epilogue: the next tile's first two steps have landed (waited for
+        // here, before the first store, so that no later wait has to count
+        // stores and copies together: the counter may see them complete out
+        // of order), its first fragments are read
+        wait_all_copies();
         const int ln = fresh_lane_id();
         if constexpr (FUSED) {
             // by block-column pairs, the bias of the next pair requested
