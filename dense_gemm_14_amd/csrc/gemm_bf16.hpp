@@ -8,10 +8,10 @@
 //     whole K loop. The 16 x 16 x 32 instruction moves half the accumulator
 //     data per multiply-add of the 32 x 32 x 16 one, which lowers the energy
 //     per product and so the clock throttling under the board power limit.
-//   * K advances 64 per step. A step is 64 block pairs in row order (block
-//     (p / 8, p % 8) for pair p): each pair is the block's two matrix
-//     instructions, K 0..31 and then K 32..63 of the step, back to back on
-//     the same accumulators. An instruction whose accumulator input is the
+//   * K advances 64 per step. A step is 64 block pairs (the first 32 walk
+//     rows 0..3 column by column, the last 32 rows 4..7): each pair is the
+//     block's two matrix instructions, K 0..31 and then K 32..63 of the step,
+//     back to back on the same accumulators. An instruction whose accumulator input is the
 //     result of the one just before it takes that result from the matrix
 //     core instead of the register file: on MI355X a loop of such pairs held
 //     a 5 % higher clock under the board power limit than the same
@@ -22,12 +22,12 @@
 //   * Fragments (8 A blocks and 8 B blocks of 16 rows, both K halves: 16
 //     bytes per lane and half each) live in one register set; a block's
 //     fragment of the next step is read into its registers once the block's
-//     last pair of this step has issued. B blocks are used by every row, so
-//     B block j of step s + 1 is read after pair 56 + j of step s, seven
-//     pairs before row 0 of step s + 1 needs it (B block 7 in step s + 1
-//     itself, after its pair 0). A block i (1..7) is read in its own step
-//     after pair 4 i - 3, still before the barrier; A block 0 of step s + 1
-//     after pair 34 of step s.
+//     last pair of this step has issued, at least eight pairs before its
+//     first use there. B block j (0..6) of step s + 1 is read after pair
+//     36 + 4 j of step s (its last use in step s is pair 35 + 4 j), A blocks
+//     0..3 after pairs 34..46; A blocks 4..7 and B block 7 of a step are read
+//     in the step itself, before its barrier. The 32 reads spread evenly over
+//     the step.
 //   * LDS is a ring of five 32 KiB slots; a slot holds one unit, the A tile
 //     (256 rows x 64 K) or the B tile of one step, as 256 rows of 128 bytes.
 //     Unit 2 s + op (op 0 = A, 1 = B) lives in slot (2 s + op) mod 5. Each 1
@@ -36,7 +36,7 @@
 //     128 bytes), so operands pass through no registers and no LDS-write
 //     instructions, and every request is one whole 128-byte row segment.
 //   * One barrier per step, after pair 31. Before it each wave has finished
-//     reading step s (its last reads, A block 7, follow pair 25), so both of
+//     reading step s (its last reads, A block 7, follow pair 26), so both of
 //     its slots are free, and its copies of step s + 1 have landed; step
 //     s + 1 is read from pair 34 on. The barrier opens a copy window that
 //     runs until the next barrier: the B tile of step s + 2 (into the slot of
@@ -197,7 +197,9 @@ __device__ inline int fresh_lane_id()
 }
 
 // EPI: EPI_PLAIN, or the activation of the fused epilogue (bias, then the
-// activation, before rounding).
+// activation, before rounding). KTAIL: K is not a multiple of 64; every copy
+// then goes through the buffer form, whose range check zero-fills the chunks
+// of the last K step that lie at or past K.
 template <int EPI, bool KTAIL>
 __global__ __attribute__((amdgpu_flat_work_group_size(THREADS, THREADS), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_nt_kernel(Problem p)
@@ -215,7 +217,7 @@ void gemm_bf16_nt_kernel(Problem p)
     const int K = p.K;
 
     // Fragment of a 16-row block: lane (l16, grp) reads row l16 of the block,
-    // logical chunk grp (first half-step) or 4 + grp (second half-step).
+    // logical chunk grp (K 0..31 of the step) or 4 + grp (K 32..63).
     // Blocks start at multiples of 16 rows, which leaves the swizzle unchanged.
     const int kofs0 = swizzle(l16, grp) << 4;
     const int kofs1 = swizzle(l16, 4 + grp) << 4;
