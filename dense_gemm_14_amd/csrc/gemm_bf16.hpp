@@ -546,9 +546,10 @@ void gemm_bf16_nt_kernel(Problem p)
         for (int s = nk - 2; s < nk; ++s)
             step(s, Int<0>{}, Int<1>{});
         // epilogue: the next tile's first two steps have landed (waited for
-        // here, before the first store, so that no later wait has to count
-        // stores and copies together: the counter may see them complete out
-        // of order), its first fragments are read
+        // here, before the first store, so that the next tile's first step
+        // needs no wait: the counter may see copies and stores complete out of
+        // order, and later waits rely only on copies completing in order among
+        // themselves), its first fragments are read
         wait_all_copies();
         const int ln = fresh_lane_id();
         if constexpr (FUSED) {
