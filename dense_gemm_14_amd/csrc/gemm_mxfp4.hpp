@@ -305,14 +305,13 @@ void gemm_mxfp4_nt_kernel(Problem p)
             // and read step 0's first A blocks, its B blocks and their scales)
 
             // K step k on stage k % STAGES, B set k % 2. The step's shape is
-            // fixed at compile time (step 0 of a tile, the first step of a
-            // scale block): a branch inside the loop body would let the
-            // compiler sink a step's matrix instructions past it, away from
-            // the reads and copies they are interleaved with.
-            auto step = [&](int k, auto buf_c, auto block_start_c, auto tile_start_c) {
+            // fixed at compile time (the first step of a scale block): a
+            // branch inside the loop body would let the compiler sink a
+            // step's matrix instructions past it, away from the reads and
+            // copies they are interleaved with.
+            auto step = [&](int k, auto buf_c, auto block_start_c) {
                 constexpr int buf = decltype(buf_c)::value;
                 constexpr bool block_start = decltype(block_start_c)::value;   // k % 4 == 0
-                constexpr bool tile_start = decltype(tile_start_c)::value;     // k == 0
                 const int stage = k & (STAGES - 1);
                 const int next_stage = (k + 1) & (STAGES - 1);
                 const int copy_stage = (k + STAGES - 1) & (STAGES - 1);
@@ -320,16 +319,16 @@ void gemm_mxfp4_nt_kernel(Problem p)
                 // that each stage's addresses are formed where they are used
                 asm volatile("" : "+v"(kofs), "+v"(a_frag), "+v"(b_frag), "+v"(a_sc), "+v"(b_sc));
                 // this wave's reads of step k - 1 and k and its copies of step
-                // k + 1 (and every older scale block) are done: only step
-                // k + 2's code copies may still be in flight, plus a scale
-                // block issued after them (which makes this wait stricter),
-                // and at step 0 after a previous tile that tile's epilogue
-                // stores, issued after them
+                // k + 1 (and every older scale block) are done. Copies complete
+                // in issue order among themselves, so while one of step k + 1's
+                // is pending all COPIES of step k + 2 are too: at most COPIES
+                // outstanding operations means step k + 1 has landed, whatever
+                // else is counted (a scale block copied after step k + 2's
+                // codes; at step 0 after a previous tile, that tile's epilogue
+                // loads and stores, whose completion order against the copies
+                // is not relied on)
                 wait_reads();
-                if constexpr (tile_start)
-                    wait_copies_le<COPIES * (STAGES - 3) + EPILOGUE_STORES>();
-                else
-                    wait_copies_le<COPIES * (STAGES - 3)>();
+                wait_copies_le<COPIES * (STAGES - 3)>();
                 // after the barrier every wave is done with step k - 1's stage
                 // and step k + 1's stage is complete
                 lds_barrier();
@@ -362,15 +361,11 @@ void gemm_mxfp4_nt_kernel(Problem p)
                     copy_scales((k >> 2) + 1);
             };
             // nk is a multiple of 4 (K % 512 == 0): steps go in fours
-            step(0, Int<0>{}, Int<1>{}, Int<1>{});
-            step(1, Int<1>{}, Int<0>{}, Int<0>{});
-            step(2, Int<0>{}, Int<0>{}, Int<0>{});
-            step(3, Int<1>{}, Int<0>{}, Int<0>{});
-            for (int k = 4; k < nk; k += 4) {
-                step(k, Int<0>{}, Int<1>{}, Int<0>{});
-                step(k + 1, Int<1>{}, Int<0>{}, Int<0>{});
-                step(k + 2, Int<0>{}, Int<0>{}, Int<0>{});
-                step(k + 3, Int<1>{}, Int<0>{}, Int<0>{});
+            for (int k = 0; k < nk; k += 4) {
+                step(k, Int<0>{}, Int<1>{});
+                step(k + 1, Int<1>{}, Int<0>{});
+                step(k + 2, Int<0>{}, Int<0>{});
+                step(k + 3, Int<1>{}, Int<0>{});
             }
         }
         store_tile16<EPI>(acc, rc, rbias, p.M, p.N, tm * TM + 128 * wm, tn * TN + 64 * wn, lane);

@@ -392,7 +392,7 @@ int gemm355_force_fp4_path(int path);
 /*
  * gemm_mxfp4_nt -- C = A * B^T for microscaled FP4 operands (E2M1 codes with
  * one E8M0 power-of-two scale per 32 elements), on the gfx950 matrix cores'
- * own block scaling (v_mfma_scale_f32_32x32x64_f8f6f4, four times the BF16
+ * own block scaling (v_mfma_scale_f32_16x16x128_f8f6f4, four times the BF16
  * rate). Not a format of the pages: their FP4 variant scales every 16
  * elements by an E4M3 value ("NVFP4 GEMM on Blackwell", "NVFP4 Datatype"),
  * whose mantissa the hardware scaling cannot apply; this is the block-scaled
