@@ -1,7 +1,9 @@
-"""A host-side model of the copy, wait, barrier and read order of the two
-kernels that carry their LDS ring from one output tile into the next (the BF16
-256 x 256 kernel and the microscaled FP4 kernel), checked for every step count
-up to 40 and three tiles per workgroup.
+"""A host-side model of the copy, wait, barrier and read order of the kernels
+whose waits leave copies in flight: the two that carry their LDS ring from one
+output tile into the next (the BF16 256 x 256 kernel and the microscaled FP4
+kernel, three tiles per workgroup) and the 64 x 64 long-K kernel, whose B
+units arrive in parts over four steps; every step count up to 40 (60 for the
+long-K kernel).
 
 The only ordering assumed of the hardware is the one the kernels rely on: a
 wave's LDS-DMA copies complete in the order it issued them, while its stores
@@ -43,6 +45,7 @@ class Wave:
         self.proven = 0           # copies proven complete: a prefix of self.copies
         self.visible = set()      # units every wave's copies of which are complete and behind a barrier
         self.content = [None] * slots
+        self.parts = {}           # unit -> copies it takes in all (issued over one or several steps)
         self.last_read = {}       # unit -> sequence number of its last read
         self.seq = 0
         self.barrier_seq = -1
@@ -52,7 +55,8 @@ class Wave:
         self.seq += 1
         return self.seq
 
-    def copy(self, unit, slot, parts):
+    def copy(self, unit, slot, parts, total=None):
+        self.parts[unit] = parts if total is None else total
         held = self.content[slot]
         if held is not None and held != unit:
             r = self.last_read.get(held, -1)
@@ -75,7 +79,7 @@ class Wave:
         done = self.copies[:self.proven]
         pending = set(self.copies[self.proven:])
         for s, u in enumerate(self.content):
-            if u is not None and u in done and u not in pending:
+            if u is not None and u not in pending and done.count(u) == self.parts[u]:
                 self.visible.add(u)
         self.barrier_seq = self.tick()
 
@@ -247,7 +251,7 @@ def mx_run(nk, tiles):
                     w.read(nxt_s, nxt_slot)
                 if tt % 4 == 1 and tt < 4 * MX_COPIES:
                     ut, uk = unit_of(t, k + MX_STAGES - 1)
-                    w.copy(C(ut, uk), (k + MX_STAGES - 1) % MX_STAGES, 1)
+                    w.copy(C(ut, uk), (k + MX_STAGES - 1) % MX_STAGES, 1, total=MX_COPIES)
             if k % MX_SCALE_STEPS == 0:
                 bt, bb = sunit(t, k // MX_SCALE_STEPS + 1)
                 w.copy(S(bt, bb), sslot(bt, bb), 1)
@@ -276,3 +280,84 @@ def test_mx_wait_counting_stores_would_not_prove_the_next_step():
     assert w.proven == 0
     w.wait(MX_COPIES)
     assert w.copies[:w.proven] == [("codes", 1, 0)] * MX_COPIES + [("codes", 1, 1)] * MX_COPIES
+
+
+# ---- BF16 64 x 64 long-K kernel ---------------------------------------------------
+
+SL_A_SLOTS = 8       # A ring: one step per unit
+SL_B_SLOTS = 3       # B ring: SUPER steps per unit (512-byte rows)
+SL_SUPER = 4
+SL_A_COPIES = 2      # per wave and step
+SL_B_COPIES = 2      # per wave and step (one part of a B unit)
+
+
+def sl_wait_left(phase):
+    return 22 if phase == 0 else 18 if phase == 3 else 24
+
+
+def test_small_long_constants_match_the_kernel():
+    s = _src("gemm_bf16_small_long.hpp")
+    assert "constexpr int A_SLOTS = %d;" % SL_A_SLOTS in s
+    assert "static constexpr int SLOTS = %d;" % SL_B_SLOTS in s
+    assert "constexpr int A_COPIES = %d;" % SL_A_COPIES in s
+    assert "constexpr int B_COPIES = %d;" % SL_B_COPIES in s
+    assert "static_assert(SUPER == %d," % SL_SUPER in s
+    assert "static constexpr int wait_left(int phase) { return phase == 0 ? 22 : phase == 3 ? 18 : 24; }" in s
+    assert re.search(r"copy_b\(s / SUPER \+ B_SLOTS - 1, Int<phase>\{\}\);\s*copy_a\(s \+ A_SLOTS - 1\);\s*"
+                     r"wait_reads\(\);\s*wait_copies_left<BS::wait_left\(phase\)>\(\);\s*lds_barrier\(\);", s)
+    assert "wait_copies_left<BS::wait_left(SUPER - 1)>();" in s
+
+
+def small_long_run(nk):
+    """One tile (each tile starts from drained rings): the prologue issues what
+    steps -8 .. -1 would have, then step s copies part s % 4 of B unit s / 4 + 2
+    and the A tile of step s + 7 (past K as zeros, still issued), waits, and
+    after the barrier reads step s + 1."""
+    w = Wave(SL_A_SLOTS + SL_B_SLOTS)
+    A = lambda s: ("A", s)
+    B = lambda j: ("B", j)
+    aslot = lambda s: s % SL_A_SLOTS
+    bslot = lambda j: SL_A_SLOTS + j % SL_B_SLOTS
+
+    def copy_b(j):
+        w.copy(B(j), bslot(j), SL_B_COPIES, total=SL_SUPER * SL_B_COPIES)
+
+    def copy_a(s):
+        w.copy(A(s), aslot(s), SL_A_COPIES)
+
+    def read_step(s):
+        for _ in range(4):
+            w.read(A(s), aslot(s))
+            w.read(B(s // SL_SUPER), bslot(s // SL_SUPER))
+
+    w.wait_reads()
+    w.wait(0)
+    w.barrier()
+    for t in range(-SL_SUPER * (SL_B_SLOTS - 1), 0):
+        unit = (t - t % SL_SUPER) // SL_SUPER + SL_B_SLOTS - 1
+        if unit >= 0:
+            copy_b(unit)
+        if t + SL_A_SLOTS - 1 >= 0:
+            copy_a(t + SL_A_SLOTS - 1)
+    w.wait(sl_wait_left(SL_SUPER - 1))
+    w.barrier()
+    read_step(0)
+    for s in range(nk):
+        copy_b(s // SL_SUPER + SL_B_SLOTS - 1)
+        copy_a(s + SL_A_SLOTS - 1)
+        w.wait_reads()
+        w.wait(sl_wait_left(s % SL_SUPER))
+        w.barrier()
+        read_step(s + 1)
+    w.wait_reads()
+    w.wait(0)
+    return w
+
+
+@pytest.mark.parametrize("nk", range(1, 61))
+def test_small_long_order(nk):
+    small_long_run(nk)
+
+
+def test_small_long_model_catches_a_looser_wait():
+    _fails_with_looser_waits(lambda nk, tiles: small_long_run(nk), 12)
