@@ -1,9 +1,10 @@
-"""A host-side model of the copy, wait, barrier and read order of the kernels
-whose waits leave copies in flight: the two that carry their LDS ring from one
-output tile into the next (the BF16 256 x 256 kernel and the microscaled FP4
-kernel, three tiles per workgroup) and the 64 x 64 long-K kernel, whose B
-units arrive in parts over four steps; every step count up to 40 (60 for the
-long-K kernel).
+"""A host-side model of the copy, wait, barrier and read order of every kernel
+whose waits leave LDS-DMA copies in flight: the two that carry their LDS ring
+from one output tile into the next (the BF16 256 x 256 kernel and the
+microscaled FP4 kernel, three tiles per workgroup), the 64 x 64 long-K kernel,
+whose B units arrive in parts over four steps, and the whole-step rings of
+the 64 x 64 kernel and of the split-K kernel's A and B copying waves; every
+step count up to 40 (60 for the long-K kernel).
 
 The only ordering assumed of the hardware is the one the kernels rely on: a
 wave's LDS-DMA copies complete in the order it issued them, while its stores
@@ -361,3 +362,56 @@ def test_small_long_order(nk):
 
 def test_small_long_model_catches_a_looser_wait():
     _fails_with_looser_waits(lambda nk, tiles: small_long_run(nk), 12)
+
+
+# ---- rings of whole-step units: the 64 x 64 kernel and the split-K kernel ----------
+
+def ring_run(nk, stages, copies, wait_bound, tiles):
+    """A wave that copies one unit of `copies` parts per step, `stages` - 1
+    steps ahead, into a ring of `stages` slots; every tile starts from a
+    drained ring. Step s copies step s + stages - 1 (past K as zeros, still
+    issued) into the slot of step s - 1, waits, and after the barrier reads
+    step s + 1."""
+    w = Wave(stages)
+    ahead = stages - 1
+    for t in range(tiles):
+        U = lambda s: ("step", t, s)
+        w.wait_reads()
+        w.wait(0)
+        w.barrier()
+        for s in range(ahead):
+            w.copy(U(s), s % stages, copies)
+        w.wait(wait_bound)
+        w.barrier()
+        w.read(U(0), 0)
+        for s in range(nk):
+            w.copy(U(s + ahead), (s + ahead) % stages, copies)
+            w.wait_reads()
+            w.wait(wait_bound)
+            w.barrier()
+            w.read(U(s + 1), (s + 1) % stages)
+        w.tick()   # epilogue stores
+    return w
+
+
+def test_small_and_splitk_constants_match_the_kernels():
+    s = _src("gemm_bf16_small.hpp")
+    assert "constexpr int STAGES = 10;" in s and "constexpr int COPIES = 4;" in s
+    assert s.count("wait_copies_le<COPIES * (STAGES - 2)>();") == 2
+    assert "copy(s + STAGES - 1, Int<3>{});\n            wait_reads();" in s
+    k = _src("gemm_bf16_splitk.hpp")
+    assert "constexpr int A_STAGES = 3;" in k and "constexpr int B_STAGES = 7;" in k
+    assert "constexpr int COPIES = 4;" in k
+    assert re.search(r"if \(copies_b\)\s*wait_copies_le<COPIES \* \(B_STAGES - 2\)>\(\);\s*else\s*"
+                     r"wait_copies_le<COPIES \* \(A_STAGES - 2\)>\(\);", k)
+    assert "copy_step(ls + stages - 1);\n        // this wave's reads of step ls and its copies of step ls + 1 are done\n        wait_reads();\n        wait_next();" in k
+
+
+@pytest.mark.parametrize("nk", range(1, 41))
+@pytest.mark.parametrize("stages", [10, 3, 7])   # the 64 x 64 ring; split-K's A and B rings
+def test_ring_order(nk, stages):
+    ring_run(nk, stages, 4, 4 * (stages - 2), tiles=2)
+
+
+def test_ring_model_catches_a_looser_wait():
+    _fails_with_looser_waits(lambda nk, tiles: ring_run(nk, 7, 4, 20, tiles), 12)
